@@ -1,0 +1,68 @@
+"""Plant plausible mistakes into a copy of the oracle (on the CPU) and check
+that the pins in test_oracle_pins.py reject every one of them.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "spa_oracle.py")
+
+# (name, original text, mistaken text)
+MUTATIONS = [
+    ("relu_dropped", "s = (np.maximum(dots, 0) * w[b]", "s = (dots * w[b]"),
+    ("head_weight_dropped", "s = (np.maximum(dots, 0) * w[b].astype(np.int64)[None, :]).sum(axis=1)",
+     "s = (np.maximum(dots, 0)).sum(axis=1)"),
+    ("prefill_relu_dropped", "(np.maximum(dots, 0) * w[b, i]", "(dots * w[b, i]"),
+    ("pool_no_half", "np.floor_divide(2 * s + n, 2 * n)", "np.floor_divide(s, n)"),
+    ("pool_trunc", "np.floor_divide(2 * s + n, 2 * n)", "np.trunc((2 * s + n) / (2 * n))"),
+    ("rank_ascending", "key=lambda j: (-int(s[j]), j)", "key=lambda j: (int(s[j]), j)"),
+    ("ties_highest_index", "key=lambda j: (-int(s[j]), j)", "key=lambda j: (-int(s[j]), -j)"),
+    ("topp_strict", "hit = np.nonzero(M >= p)[0]", "hit = np.nonzero(M > p)[0]"),
+    ("topp_off_by_one", "kp = int(hit[0]) + 1 if len(hit)", "kp = int(hit[0]) if len(hit)"),
+    ("kmin_ignored", "k = min(len(order), max(k_min, min(kp, k_max)))", "k = min(len(order), min(kp, k_max))"),
+    ("kmax_ignored", "k = min(len(order), max(k_min, min(kp, k_max)))", "k = min(len(order), max(k_min, kp))"),
+    ("beta_ignored", "lg = beta * np.array(", "lg = np.array("),
+    ("scale_dropped", "x = (K @ qv) * scale", "x = (K @ qv)"),
+    ("no_normalise", "return (e @ V) / z, float(m + np.log(z))", "return (e @ V), float(m + np.log(z))"),
+    ("lse_no_max", "return (e @ V) / z, float(m + np.log(z))", "return (e @ V) / z, float(np.log(z))"),
+    ("gqa_modulo", "            g = h // G\n            toks", "            g = h % Hkv\n            toks"),
+    ("prefill_gqa_modulo", "                g = h // G\n                K = to_f64(k[b, g, kslots]",
+     "                g = h % Hkv\n                K = to_f64(k[b, g, kslots]"),
+    ("causal_strict", "keep = k_pos[kslots] <= pos_u", "keep = k_pos[kslots] < pos_u"),
+    ("window_off_by_one", "set(range(max(0, L - window_tok), L))", "set(range(max(0, L - window_tok), L - 1))"),
+    ("sink_tokens_dropped", "toks = sorted(set(range(min(sink_tok, L))) | ", "toks = sorted("),
+    ("block_tail_unmasked", "for t in range(j * blk, min((j + 1) * blk, L))]", "for t in range(j * blk, (j + 1) * blk)]"),
+    ("local_blocks_dropped", " | set(range(max(0, nbv - n_local), nbv))\n    cand", "\n    cand"),
+    ("prefill_sink_dropped", "reserved = set(range(min(n_sink, i + 1))) | ", "reserved = "),
+    ("prefill_diag_dropped", "set(range(max(0, i - n_local), i)) | {i}", "set(range(max(0, i - n_local), i))"),
+    ("score_mask_inclusive", "J = min(ia, nKb)", "J = min(ia + 1, nKb)"),
+    ("inverse_is_forward", "    out = np.empty_like(x)\n    idx = [slice(None)] * x.ndim",
+     "    return np.take(x, perm, axis=axis)\n    idx = [slice(None)] * x.ndim"),
+    ("bf16_shift", "u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
+     "u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)"),
+    ("segment_check_loose", "return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))", "return True"),
+]
+
+
+def test_mutation_list_applies():
+    src = open(SRC).read()
+    for name, old, new in MUTATIONS:
+        assert src.count(old) == 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_reject_planted_mistake(tmp_path, name, old, new):
+    src = open(SRC).read()
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), pkg / "__init__.py")
+    (pkg / "spa_oracle.py").write_text(src.replace(old, new))
+    env = dict(os.environ, SPA_ORACLE_UNDER_TEST=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
