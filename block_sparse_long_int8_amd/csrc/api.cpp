@@ -1,0 +1,308 @@
+// C ABI of the block-sparse attention library: argument validation, workspace
+// sizing and kernel launches.  Every check runs on the host before anything is
+// enqueued; a failed check launches nothing.  See include/spa.h for the
+// contract of each entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/spa.h"
+#include "spa_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+spa_status fail(spa_status code, const char* fn, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+spa_status fail(spa_status code, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(fn) + ": " + buf;
+  return code;
+}
+
+spa_status ok() {
+  g_last_error.clear();
+  return SPA_OK;
+}
+
+spa_status from_hip(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return ok();
+  return fail(SPA_ERR_HIP, fn, "HIP launch error %d (%s)", (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+#define REQUIRE(cond, code, ...)                    \
+  do {                                              \
+    if (!(cond)) return fail(code, fn, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* spa_status_string(spa_status s) {
+  switch (s) {
+    case SPA_OK: return "SPA_OK";
+    case SPA_ERR_INVALID_ARG: return "SPA_ERR_INVALID_ARG";
+    case SPA_ERR_UNSUPPORTED: return "SPA_ERR_UNSUPPORTED";
+    case SPA_ERR_WORKSPACE: return "SPA_ERR_WORKSPACE";
+    case SPA_ERR_HIP: return "SPA_ERR_HIP";
+    default: return "SPA_ERR_UNKNOWN";
+  }
+}
+
+const char* spa_last_error(void) { return g_last_error.c_str(); }
+
+int spa_version(void) { return 100; }
+
+// ------------------------------------------------------------------ scores --
+
+size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, int mode) {
+  if (mode != SPA_SCORE_PREFILL_TOKENS || B <= 0 || H_idx <= 0 || r <= 0) return 0;
+  const size_t hr = (size_t)H_idx * r;
+  return align256((size_t)B * (size_t)(Mq > 0 ? Mq : 0) * hr) + align256((size_t)B * (size_t)(nKb > 0 ? nKb : 0) * hr);
+}
+
+spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
+                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len, int blk,
+                           int mode, int32_t* scores, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "spa_index_score";
+  REQUIRE(mode == SPA_SCORE_DECODE || mode == SPA_SCORE_PREFILL_POOLED || mode == SPA_SCORE_PREFILL_TOKENS,
+          SPA_ERR_INVALID_ARG, "unknown mode %d", mode);
+  REQUIRE(B >= 0 && Mq >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG,
+          "negative size (B=%d Mq=%d nKb=%d q_blk0=%d)", B, Mq, nKb, q_blk0);
+  REQUIRE(H_idx >= 1 && r >= 4 && r % 4 == 0, SPA_ERR_INVALID_ARG, "need H_idx >= 1 and r a positive multiple of 4 (H_idx=%d r=%d)", H_idx, r);
+  REQUIRE((long)H_idx * r <= 1024, SPA_ERR_INVALID_ARG, "H_idx*r = %ld exceeds 1024 (int32 scores could overflow)", (long)H_idx * r);
+  REQUIRE(blk >= 1, SPA_ERR_INVALID_ARG, "blk must be >= 1 (got %d)", blk);
+  if (mode == SPA_SCORE_DECODE) REQUIRE(Mq == 1, SPA_ERR_INVALID_ARG, "decode mode needs Mq == 1 (got %d)", Mq);
+  if (B == 0 || Mq == 0 || nKb == 0) return ok();
+  REQUIRE(qI && kI && w && scores, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(qI) && aligned16(kI) && aligned16(scores), SPA_ERR_INVALID_ARG, "qI, kI and scores must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == SPA_SCORE_DECODE) {
+    REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode mode needs seq_len");
+    return from_hip(spa::launch_score_decode(qI, kI, w, B, H_idx, r, nKb, seq_len, blk, scores, s), fn);
+  }
+  REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
+  const int8_t* qb = qI;
+  const int8_t* kb = kI;
+  if (mode == SPA_SCORE_PREFILL_TOKENS) {
+    const size_t need = spa_index_score_workspace_size(B, H_idx, r, Mq, nKb, mode);
+    REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+    int8_t* pq = (int8_t*)ws;
+    int8_t* pk = pq + align256((size_t)B * Mq * H_idx * r);
+    hipError_t e = spa::launch_pool_blocks(qI, B, Mq * blk, Mq, q_blk0 * blk, H_idx, r, blk, seq_len, pq, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    e = spa::launch_pool_blocks(kI, B, nKb * blk, nKb, 0, H_idx, r, blk, seq_len, pk, s);
+    if (e != hipSuccess) return from_hip(e, fn);
+    qb = pq;
+    kb = pk;
+  }
+  return from_hip(spa::launch_score_prefill(qb, kb, w, B, H_idx, Mq, nKb, q_blk0, seq_len, blk, scores, s), fn);
+}
+
+// --------------------------------------------------------------- selection --
+
+static spa_status select_common(const char* fn, const int32_t* scores, int B, int M, int nKb,
+                                int q_blk0, const int32_t* seq_len, int blk, int n_sink, int n_local,
+                                int prefill, int mode, int k, float beta, float p, int k_min,
+                                int k_max, int32_t* idx, int32_t* count, int cap, void* stream) {
+  REQUIRE(prefill == 0 || prefill == 1, SPA_ERR_INVALID_ARG, "prefill must be 0 or 1 (got %d)", prefill);
+  REQUIRE(B >= 0 && M >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG, "negative size");
+  REQUIRE(blk >= 1 && n_sink >= 0 && n_local >= 0, SPA_ERR_INVALID_ARG, "need blk >= 1, n_sink >= 0, n_local >= 0");
+  if (!prefill) REQUIRE(M == 1, SPA_ERR_INVALID_ARG, "decode selection needs M == 1 (got %d)", M);
+  const int budget = mode == 0 ? k : k_max;
+  if (mode == 0) {
+    REQUIRE(k >= 0, SPA_ERR_INVALID_ARG, "k must be >= 0 (got %d)", k);
+  } else {
+    REQUIRE(std::isfinite(p) && p > 0.f && p <= 1.f, SPA_ERR_INVALID_ARG, "need 0 < p <= 1 (got %g)", (double)p);
+    REQUIRE(std::isfinite(beta) && beta >= 0.f, SPA_ERR_INVALID_ARG, "need finite beta >= 0 (got %g)", (double)beta);
+    REQUIRE(k_min >= 0 && k_min <= k_max, SPA_ERR_INVALID_ARG, "need 0 <= k_min <= k_max (got %d, %d)", k_min, k_max);
+  }
+  const long need_cap = (long)n_sink + n_local + budget + (prefill ? 1 : 0);
+  REQUIRE(cap >= 1 && (long)cap >= need_cap, SPA_ERR_INVALID_ARG, "cap %d < reserved + budget = %ld", cap, need_cap);
+  REQUIRE(nKb <= spa::select_max_blocks(), SPA_ERR_UNSUPPORTED, "nKb %d exceeds %d", nKb, spa::select_max_blocks());
+  if (B == 0 || M == 0) return ok();
+  REQUIRE(scores && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  if (!prefill) REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode selection needs seq_len");
+  REQUIRE(aligned16(scores) && aligned16(idx) && aligned16(count), SPA_ERR_INVALID_ARG, "scores, idx and count must be 16-byte aligned");
+  spa::SelectArgs a;
+  a.scores = scores;
+  a.B = B;
+  a.M = M;
+  a.nKb = nKb;
+  a.q_blk0 = q_blk0;
+  a.seq_len = seq_len;
+  a.blk = blk;
+  a.n_sink = n_sink;
+  a.n_local = n_local;
+  a.prefill = prefill;
+  a.mode = mode;
+  a.k = k;
+  a.beta = beta;
+  a.p = p;
+  a.k_min = k_min;
+  a.k_max = k_max;
+  a.idx = idx;
+  a.count = count;
+  a.cap = cap;
+  return from_hip(spa::launch_select(a, (hipStream_t)stream), fn);
+}
+
+spa_status spa_select_topk(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                           const int32_t* seq_len, int blk, int n_sink, int n_local, int prefill,
+                           int k, int32_t* idx, int32_t* count, int cap, void* ws, size_t ws_bytes,
+                           void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return select_common("spa_select_topk", scores, B, M, nKb, q_blk0, seq_len, blk, n_sink, n_local,
+                       prefill, 0, k, 0.f, 1.f, 0, 0, idx, count, cap, stream);
+}
+
+spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                           const int32_t* seq_len, int blk, int n_sink, int n_local, int prefill,
+                           float beta, float p, int k_min, int k_max, int32_t* idx, int32_t* count,
+                           int cap, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return select_common("spa_select_topp", scores, B, M, nKb, q_blk0, seq_len, blk, n_sink, n_local,
+                       prefill, 1, 0, beta, p, k_min, k_max, idx, count, cap, stream);
+}
+
+// ---------------------------------------------------------- decode attention --
+
+size_t spa_sparse_decode_attn_workspace_size(int B, int Hq, int Hkv, int d) {
+  if (B <= 0 || Hkv <= 0 || Hq <= 0 || d <= 0 || Hq % Hkv) return 0;
+  return spa::decode_ws_bytes(B, Hq, Hkv, d, spa::decode_workers());
+}
+
+spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                                  int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                  const int32_t* count, int cap, int blk, const uint8_t* head_mode,
+                                  int local_sink_tok, int local_window_tok, int B, int Hq, int Hkv,
+                                  int d, int Tcap, float scale, void* out, int out_dtype,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "spa_sparse_decode_attn";
+  REQUIRE(io_dtype == SPA_F32 || io_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown io_dtype %d", io_dtype);
+  REQUIRE(out_dtype == SPA_F32 || out_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && Tcap >= 1, SPA_ERR_INVALID_ARG, "bad sizes (B=%d Hq=%d Hkv=%d d=%d Tcap=%d)", B, Hq, Hkv, d, Tcap);
+  REQUIRE(Hq % Hkv == 0, SPA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  REQUIRE(cap >= 1 && local_sink_tok >= 0 && local_window_tok >= 0, SPA_ERR_INVALID_ARG, "need cap >= 1 and non-negative local sizes");
+  REQUIRE(std::isfinite(scale), SPA_ERR_INVALID_ARG, "scale must be finite");
+  REQUIRE(blk == 16 || blk == 32 || blk == 64 || blk == 128, SPA_ERR_UNSUPPORTED, "blk %d not in {16,32,64,128}", blk);
+  REQUIRE(Hq / Hkv <= 16, SPA_ERR_UNSUPPORTED, "more than 16 query heads per KV head (%d)", Hq / Hkv);
+  if (io_dtype == SPA_BF16)
+    REQUIRE(d == 128, SPA_ERR_UNSUPPORTED, "bf16 decode supports d == 128 only (got %d)", d);
+  else
+    REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "fp32 decode supports d in {64,128} (got %d)", d);
+  REQUIRE((long)B * Hkv <= 4096, SPA_ERR_UNSUPPORTED, "B*Hkv = %ld exceeds 4096", (long)B * Hkv);
+  if (B == 0) return ok();
+  REQUIRE(q && k_cache && v_cache && out && seq_len && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned16(out) && aligned16(idx),
+          SPA_ERR_INVALID_ARG, "tensor pointers must be 16-byte aligned");
+  const size_t need = spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d);
+  REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  spa::DecodeArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.io_bf16 = io_dtype == SPA_BF16;
+  a.seq_len = seq_len;
+  a.idx = idx;
+  a.count = count;
+  a.cap = cap;
+  a.blk = blk;
+  a.head_mode = head_mode;
+  a.sink_tok = local_sink_tok;
+  a.window_tok = local_window_tok;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.Tcap = Tcap;
+  a.scale = scale;
+  a.out = out;
+  a.out_bf16 = out_dtype == SPA_BF16;
+  a.lse = lse;
+  a.ws = ws;
+  return from_hip(spa::launch_decode(a, (hipStream_t)stream), fn);
+}
+
+// ----------------------------------------------------------------- prefill --
+
+spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const void* k,
+                                    const void* v, const int32_t* q_pos, const int32_t* k_pos,
+                                    const int32_t* idx, const int32_t* count, int cap, int blk,
+                                    int B, int Hq, int Hkv, int d, int T, float scale, void* out,
+                                    int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  const char* fn = "spa_block_sparse_prefill";
+  (void)ws;
+  (void)ws_bytes;
+  REQUIRE(out_dtype == SPA_F32 || out_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
+  REQUIRE(B >= 0 && Tq >= 0 && q_blk0 >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && T >= 1 && cap >= 1,
+          SPA_ERR_INVALID_ARG, "bad sizes");
+  REQUIRE(Hq % Hkv == 0, SPA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  REQUIRE(std::isfinite(scale), SPA_ERR_INVALID_ARG, "scale must be finite");
+  REQUIRE(blk == 64, SPA_ERR_UNSUPPORTED, "prefill supports blk == 64 only (got %d)", blk);
+  REQUIRE(d == 128, SPA_ERR_UNSUPPORTED, "prefill supports d == 128 only (got %d)", d);
+  REQUIRE((long)q_blk0 * blk + Tq <= T, SPA_ERR_INVALID_ARG, "query slots [%ld, %ld) exceed T = %d",
+          (long)q_blk0 * blk, (long)q_blk0 * blk + Tq, T);
+  if (B == 0 || Tq == 0) return ok();
+  REQUIRE(q && k && v && idx && count && out, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), SPA_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  spa::PrefillArgs a;
+  a.q = q;
+  a.q_blk0 = q_blk0;
+  a.Tq = Tq;
+  a.k = k;
+  a.v = v;
+  a.q_pos = q_pos;
+  a.k_pos = k_pos;
+  a.idx = idx;
+  a.count = count;
+  a.cap = cap;
+  a.blk = blk;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.T = T;
+  a.scale = scale;
+  a.out = out;
+  a.out_bf16 = out_dtype == SPA_BF16;
+  a.lse = lse;
+  return from_hip(spa::launch_prefill(a, (hipStream_t)stream), fn);
+}
+
+// ------------------------------------------------------------- permutation --
+
+spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
+                               const int32_t* perm, int seg, int inverse, void* stream) {
+  const char* fn = "spa_segment_permute";
+  REQUIRE(outer >= 0 && T >= 0 && row_bytes >= 1 && seg >= 1, SPA_ERR_INVALID_ARG, "bad sizes");
+  REQUIRE(inverse == 0 || inverse == 1, SPA_ERR_INVALID_ARG, "inverse must be 0 or 1");
+  REQUIRE(outer <= 65535, SPA_ERR_UNSUPPORTED, "outer %ld exceeds 65535", (long)outer);
+  if (outer == 0 || T == 0) return ok();
+  REQUIRE(src && dst && perm, SPA_ERR_INVALID_ARG, "null pointer");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  const uintptr_t n = (uintptr_t)outer * (uintptr_t)T * row_bytes;
+  REQUIRE(s0 + n <= d0 || d0 + n <= s0, SPA_ERR_INVALID_ARG, "src and dst overlap");
+  return from_hip(spa::launch_permute(src, dst, outer, T, row_bytes, perm, inverse, (hipStream_t)stream), fn);
+}
+
+}  // extern "C"

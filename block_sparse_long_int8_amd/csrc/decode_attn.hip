@@ -1,0 +1,579 @@
+// Sparse flash-decode over the selected tokens, split over waves, merged by
+// log-sum-exp.
+//
+// HGA page, "Atención Exacta de Token": the output is a standard softmax over
+// exactly the selected tokens.  RTPurbo page §1: retrieval heads attend the
+// selected blocks, local heads attend attention-sink tokens plus a sliding
+// window; §5 of the same page motivates a bandwidth-first decode kernel.
+//
+// Work decomposition (MI355X: 256 CUs, HBM-bound gather):
+//   * an "item" is one (sequence b, KV head g); its tokens are cut into 32-token
+//     tiles (a selected 64-token block is two tiles);
+//   * all items' tiles are laid end to end and split evenly over a persistent
+//     grid of waves, so load balance does not depend on how budgets vary per
+//     sequence (dual top-p gives 21..185 blocks per sequence);
+//   * a wave that crosses an item boundary writes one partial (unnormalised o,
+//     running max m, running sum l) per item it touched, into slot item + wave;
+//     the merge kernel finds the partials of item i at slots i + w for
+//     w = first_tile(i)/share .. last_tile(i)/share.
+//
+// bf16 tile (d = 128, up to 16 query heads per KV head, GQA sharing: K/V are
+// read once per KV head for all its query heads):
+//   S^T[32 tok, 16 heads] = K[32, 128] . Q^T     (2 x 4 MFMA 16x16x32 bf16)
+//   O^T[128, 16 heads]   += V^T[128, 32] . P^T   (8 MFMA 16x16x32 bf16)
+//   - K feeds the A operand straight from HBM: lane (row m, group g4) loads 16
+//     bytes of token m; the d-order of the contraction is permuted identically
+//     in Q, so no transposition is needed.
+//   - V is loaded so that the 16 lanes of a group read one token's whole
+//     256-byte row; each lane then holds 8 tokens x 8 dims and an in-register
+//     8x8 transpose (byte permutes) forms the V^T operands whose rows are
+//     d = 8m + jj.  No LDS round trip.
+//   - P^T needs no data movement: the C layout of S^T already puts each
+//     lane's 8 token probabilities where the B operand wants them.
+//   - the next tile's 16 x 16-byte loads are issued before the current tile's
+//     math (two register buffers).
+// fp32 tile (d in {64, 128}): plain VALU version of the same online softmax.
+#include "spa_internal.h"
+
+namespace spa {
+
+namespace {
+
+constexpr int kWPB = 4;
+constexpr int kThreads = kWPB * kWave;
+constexpr int kMaxItems = 4096;
+constexpr int kTile = 32;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr size_t kHeader = 256;
+
+struct WsLayout {
+  int* hdr;         // [0] total tiles, [1] share, [2] workers
+  int* item_start;  // [n_items + 1]
+  float* part_ml;   // [slots][G][2]
+  float* part_o;    // [slots][G][d]
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(void* ws, int n_items, int workers, int G, int d) {
+  char* p = (char*)ws;
+  WsLayout L;
+  L.hdr = (int*)p;
+  L.item_start = (int*)(p + kHeader);
+  size_t off = kHeader + align256((size_t)(n_items + 1) * sizeof(int));
+  const size_t slots = (size_t)n_items + workers;
+  L.part_ml = (float*)(p + off);
+  off += align256(slots * G * 2 * sizeof(float));
+  L.part_o = (float*)(p + off);
+  return L;
+}
+
+__host__ __device__ inline size_t ws_total(int n_items, int workers, int G, int d) {
+  const size_t slots = (size_t)n_items + workers;
+  return kHeader + align256((size_t)(n_items + 1) * sizeof(int)) +
+         align256(slots * G * 2 * sizeof(float)) + align256(slots * G * d * sizeof(float));
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of 32-token tiles of item (b, g).
+__device__ __forceinline__ int item_tiles(const DecodeArgs& a, int b, int g, int tpb) {
+  const int L = a.seq_len[b];
+  if (a.head_mode && a.head_mode[g]) {
+    const int ns = min(a.sink_tok, L);
+    const int wstart = max(ns, L - a.window_tok);
+    return (ns + kTile - 1) / kTile + (L - wstart + kTile - 1) / kTile;
+  }
+  return a.count[b] * tpb;
+}
+
+// First token and number of valid tokens of tile u of item (b, g).
+__device__ __forceinline__ void tile_info(const DecodeArgs& a, int b, int g, int u, int tpb,
+                                          int& tok0, int& nvalid) {
+  const int L = a.seq_len[b];
+  if (a.head_mode && a.head_mode[g]) {
+    const int ns = min(a.sink_tok, L);
+    const int wstart = max(ns, L - a.window_tok);
+    const int nst = (ns + kTile - 1) / kTile;
+    if (u < nst) {
+      tok0 = u * kTile;
+      nvalid = min(kTile, ns - tok0);
+    } else {
+      tok0 = wstart + (u - nst) * kTile;
+      nvalid = min(kTile, L - tok0);
+    }
+  } else {
+    const int j = a.idx[(size_t)b * a.cap + u / tpb];
+    const int sub = u % tpb;
+    tok0 = j * a.blk + sub * kTile;
+    nvalid = min(min(kTile, a.blk - sub * kTile), L - tok0);
+  }
+}
+
+// Block-wide: item_start[] = exclusive prefix of item tile counts (in LDS),
+// returns the total.  Every thread of the block must call it.
+__device__ int build_plan(const DecodeArgs& a, int n_items, int* item_start, int* scratch) {
+  const int tpb = (a.blk + kTile - 1) / kTile;
+  const int tid = threadIdx.x;
+  const int per = (n_items + kThreads - 1) / kThreads;
+  const int i0 = tid * per;
+  const int i1 = min(n_items, i0 + per);
+  int local = 0;
+  for (int it = i0; it < i1; ++it) {
+    const int len = item_tiles(a, it / a.Hkv, it % a.Hkv, tpb);
+    item_start[it] = local;  // provisional: offset inside this thread's run
+    local += len;
+  }
+  // exclusive scan of per-thread totals
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  int x = local;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) scratch[wid] = x;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWPB; ++w) {
+    off += (w < wid) ? scratch[w] : 0;
+    tot += scratch[w];
+  }
+  off += x - local;
+  for (int it = i0; it < i1; ++it) item_start[it] += off;
+  if (tid == 0) item_start[n_items] = tot;
+  __syncthreads();
+  return tot;
+}
+
+// largest it in [0, n_items) with item_start[it] <= t
+__device__ __forceinline__ int find_item(const int* item_start, int n_items, int t) {
+  int lo = 0, hi = n_items - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (item_start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------ bf16 path ----
+constexpr int D = 128;
+
+struct TileRegs {
+  uint4 k[8];  // [mt*4 + j]
+  uint4 v[8];  // [i]
+};
+
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                          int tok0, int nvalid, int lane, TileRegs& t) {
+  const int m = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int tau = min(16 * mt + m, nvalid - 1);
+    const uint16_t* row = kb + (size_t)(tok0 + tau) * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = *reinterpret_cast<const uint4*>(row + 8 * (4 * j + g4));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nvalid - 1);
+    t.v[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(tok0 + tau) * D + 8 * m);
+  }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+struct HeadState {
+  float m;       // running max of scaled logits (log2 domain), per column
+  float l;       // lane-partial running sum
+  f32x4 o[8];    // O^T accumulators, [jj] -> rows d = 32*g4 + 8*r + jj
+};
+
+__device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg, int nvalid,
+                                          float scale_log2, int lane, HeadState& st) {
+  const int g4 = lane >> 4;
+  f32x4 s[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[mt * 4 + j]), qreg[j], s[mt], 0, 0, 0);
+  }
+  float x[8];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tau = 16 * mt + 4 * g4 + r;
+      const float v = tau < nvalid ? s[mt][r] * scale_log2 : -INFINITY;
+      x[mt * 4 + r] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
+  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+  const float m_new = fmaxf(st.m, tmax);
+  // m_new is -inf only if every token seen so far is masked: nothing to add
+  const float base = m_new == -INFINITY ? 0.f : m_new;
+  const float corr = exp2f(st.m - base);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    p[e] = exp2f(x[e] - base);
+    psum += p[e];
+  }
+  st.l = st.l * corr + psum;
+  st.m = m_new;
+  // P^T operand: k index 8*g4 + e <-> token 16*(e/4) + 4*g4 + (e%4)
+  const uint4 pu = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                    pack_bf16x2(p[6], p[7])};
+  const bf16x8 pb = as_bf16x8(pu);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    // V^T operand of output rows d = 8m + jj: element jj of each of the 8 token rows
+    const int wsel = jj >> 1;
+    uint32_t a4[4];
+#pragma unroll
+    for (int aa = 0; aa < 4; ++aa) {
+      const uint32_t lo = word_of(t.v[2 * aa], wsel);
+      const uint32_t hi = word_of(t.v[2 * aa + 1], wsel);
+      a4[aa] = (jj & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+    }
+    const uint4 au = {a4[0], a4[1], a4[2], a4[3]};
+    f32x4 acc = st.o[jj] * corr;
+    st.o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(au), pb, acc, 0, 0, 0);
+  }
+}
+
+__global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, int n_items,
+                                                               int workers) {
+  __shared__ int item_start[kMaxItems + 1];
+  __shared__ int scratch[kWPB];
+  const int total = build_plan(a, n_items, item_start, scratch);
+  const int share = (total + workers - 1) / workers;
+  const int G = a.Hq / a.Hkv;
+  WsLayout ws = ws_layout(a.ws, n_items, workers, G, D);
+  if (blockIdx.x == 0) {
+    for (int t = threadIdx.x; t <= n_items; t += kThreads) ws.item_start[t] = item_start[t];
+    if (threadIdx.x == 0) {
+      ws.hdr[0] = total;
+      ws.hdr[1] = share;
+      ws.hdr[2] = workers;
+    }
+  }
+  if (share == 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = blockIdx.x * kWPB + threadIdx.x / kWave;
+  int t = w * share;
+  const int t_end = min(total, t + share);
+  if (t >= t_end) return;
+
+  const int tpb = (a.blk + kTile - 1) / kTile;
+  const int m = lane & 15, g4 = lane >> 4;
+  const float scale_log2 = a.scale * kLog2e;
+  const uint16_t* q = (const uint16_t*)a.q;
+  const uint16_t* kc = (const uint16_t*)a.k;
+  const uint16_t* vc = (const uint16_t*)a.v;
+
+  int item = find_item(item_start, n_items, t);
+  while (t < t_end) {
+    while (item_start[item + 1] <= t) ++item;
+    const int seg_end = min(t_end, item_start[item + 1]);
+    const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
+    const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * D;
+    const uint16_t* kb = kc + kv_off;
+    const uint16_t* vb = vc + kv_off;
+
+    bf16x8 qreg[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 qv = {0u, 0u, 0u, 0u};
+      if (m < G) qv = *reinterpret_cast<const uint4*>(q + ((size_t)b * a.Hq + g * G + m) * D + 8 * (4 * j + g4));
+      qreg[j] = as_bf16x8(qv);
+    }
+    HeadState st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) st.o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int u = t - item_start[item];
+    const int u_end = seg_end - item_start[item];
+    TileRegs A, Bt;
+    int tokA, nvA, tokB = 0, nvB = 0;
+    tile_info(a, b, g, u, tpb, tokA, nvA);
+    if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
+    while (u < u_end) {
+      if (u + 1 < u_end) {
+        tile_info(a, b, g, u + 1, tpb, tokB, nvB);
+        if (nvB > 0) load_tile(kb, vb, tokB, nvB, lane, Bt);
+      }
+      if (nvA > 0) tile_math(A, qreg, nvA, scale_log2, lane, st);
+      if (++u >= u_end) break;
+      if (u + 1 < u_end) {
+        tile_info(a, b, g, u + 1, tpb, tokA, nvA);
+        if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
+      }
+      if (nvB > 0) tile_math(Bt, qreg, nvB, scale_log2, lane, st);
+      ++u;
+    }
+
+    // partial for (item, wave)
+    const size_t slot = (size_t)item + w;
+    float lt = st.l;
+    lt += shfl_xor_f(lt, 16);
+    lt += shfl_xor_f(lt, 32);
+    if (m < G) {
+      float* po = ws.part_o + (slot * G + m) * D + 32 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float4 lo4 = {st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]};
+        float4 hi4 = {st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]};
+        *reinterpret_cast<float4*>(po + 8 * r) = lo4;
+        *reinterpret_cast<float4*>(po + 8 * r + 4) = hi4;
+      }
+      if (g4 == 0) {
+        ws.part_ml[(slot * G + m) * 2 + 0] = st.m;
+        ws.part_ml[(slot * G + m) * 2 + 1] = lt;
+      }
+    }
+    t = seg_end;
+  }
+}
+
+// ------------------------------------------------------------ fp32 path ----
+// One wave per worker.  Scores: lane (tau, half) computes q_h . k_tau for the
+// heads h = 2*hh + half.  The running max of every head is kept replicated in
+// all lanes; probabilities and new maxima go through per-wave LDS, then every
+// lane accumulates P.V for its d values.
+template <int DD>
+__global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int n_items,
+                                                              int workers) {
+  __shared__ int item_start[kMaxItems + 1];
+  __shared__ int scratch[kWPB];
+  __shared__ float q_s[kWPB][16 * DD];
+  __shared__ float p_s[kWPB][16][kTile];
+  __shared__ float mnew_s[kWPB][16];
+  const int total = build_plan(a, n_items, item_start, scratch);
+  const int share = (total + workers - 1) / workers;
+  const int G = a.Hq / a.Hkv;
+  WsLayout ws = ws_layout(a.ws, n_items, workers, G, DD);
+  if (blockIdx.x == 0) {
+    for (int t = threadIdx.x; t <= n_items; t += kThreads) ws.item_start[t] = item_start[t];
+    if (threadIdx.x == 0) {
+      ws.hdr[0] = total;
+      ws.hdr[1] = share;
+      ws.hdr[2] = workers;
+    }
+  }
+  if (share == 0) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int w = blockIdx.x * kWPB + wv;
+  int t = w * share;
+  const int t_end = min(total, t + share);
+  if (t >= t_end) return;
+  const int tpb = (a.blk + kTile - 1) / kTile;
+  const float scale_log2 = a.scale * kLog2e;
+  const float* q = (const float*)a.q;
+  const float* kc = (const float*)a.k;
+  const float* vc = (const float*)a.v;
+  constexpr int NDL = DD / kWave;  // d values per lane in P.V
+  const int tau = lane & 31, half = lane >> 5;
+
+  int item = find_item(item_start, n_items, t);
+  while (t < t_end) {
+    while (item_start[item + 1] <= t) ++item;
+    const int seg_end = min(t_end, item_start[item + 1]);
+    const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
+    const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * DD;
+    wave_sync();
+    for (int e = lane; e < G * DD; e += kWave) q_s[wv][e] = q[((size_t)b * a.Hq + g * G) * DD + e];
+    wave_sync();
+    float mrun[16], lrun[16], acc[16][NDL];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      mrun[h] = -INFINITY;
+      lrun[h] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NDL; ++c) acc[h][c] = 0.f;
+    }
+    for (int u = t - item_start[item]; u < seg_end - item_start[item]; ++u) {
+      int tok0, nvalid;
+      tile_info(a, b, g, u, tpb, tok0, nvalid);
+      if (nvalid <= 0) continue;
+      const float* krow = kc + kv_off + (size_t)(tok0 + min(tau, nvalid - 1)) * DD;
+      float sc[8];
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) sc[hh] = 0.f;
+      for (int c = 0; c < DD; c += 4) {
+        const float4 kv = *reinterpret_cast<const float4*>(krow + c);
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+          const int h = 2 * hh + half;
+          if (h < G) {
+            const float* qh = &q_s[wv][h * DD + c];
+            sc[hh] += qh[0] * kv.x + qh[1] * kv.y + qh[2] * kv.z + qh[3] * kv.w;
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        const int h = 2 * hh + half;
+        const float x = tau < nvalid ? sc[hh] * scale_log2 : -INFINITY;
+        float mx = x;
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+        if (h < G) {
+          const float m_new = fmaxf(mrun[h], mx);
+          const float base = m_new == -INFINITY ? 0.f : m_new;
+          p_s[wv][h][tau] = exp2f(x - base);
+          if (tau == 0) mnew_s[wv][h] = m_new;
+        }
+      }
+      wave_sync();
+#pragma unroll
+      for (int h = 0; h < 16; ++h) {
+        if (h < G) {
+          const float m_new = mnew_s[wv][h];
+          const float base = m_new == -INFINITY ? 0.f : m_new;
+          const float corr = exp2f(mrun[h] - base);
+          mrun[h] = m_new;
+          float ps = 0.f;
+          for (int tt = 0; tt < nvalid; ++tt) ps += p_s[wv][h][tt];
+          lrun[h] = lrun[h] * corr + ps;
+#pragma unroll
+          for (int c = 0; c < NDL; ++c) acc[h][c] *= corr;
+        }
+      }
+      for (int tt = 0; tt < nvalid; ++tt) {
+        const float* vrow = vc + kv_off + (size_t)(tok0 + tt) * DD;
+        float vv[NDL];
+#pragma unroll
+        for (int c = 0; c < NDL; ++c) vv[c] = vrow[lane + kWave * c];
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+          if (h < G) {
+            const float pv = p_s[wv][h][tt];
+#pragma unroll
+            for (int c = 0; c < NDL; ++c) acc[h][c] += pv * vv[c];
+          }
+      }
+      wave_sync();
+    }
+    const size_t slot = (size_t)item + w;
+#pragma unroll
+    for (int h = 0; h < 16; ++h)
+      if (h < G) {
+#pragma unroll
+        for (int c = 0; c < NDL; ++c) ws.part_o[(slot * G + h) * DD + lane + kWave * c] = acc[h][c];
+        if (lane == 0) {
+          ws.part_ml[(slot * G + h) * 2 + 0] = mrun[h];
+          ws.part_ml[(slot * G + h) * 2 + 1] = lrun[h];
+        }
+      }
+    t = seg_end;
+  }
+}
+
+// ----------------------------------------------------------------- merge ----
+// grid: n_items; block: G * d / 4 threads (one float4 of one head each).
+__global__ void decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
+  const int G = a.Hq / a.Hkv;
+  const int d = a.d;
+  WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
+  const int item = blockIdx.x;
+  const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
+  const int h = threadIdx.x / (d / 4);
+  const int c4 = threadIdx.x - h * (d / 4);
+  if (h >= G) return;
+  const int share = ws.hdr[1];
+  const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = -INFINITY;
+  if (s1 > s0 && share > 0) {
+    const int w0 = s0 / share, w1 = (s1 - 1) / share;
+    float M = -INFINITY;
+    for (int w = w0; w <= w1; ++w) M = fmaxf(M, ws.part_ml[(((size_t)item + w) * G + h) * 2]);
+    if (M != -INFINITY) {
+      float L = 0.f;
+      float4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int w = w0; w <= w1; ++w) {
+        const size_t slot = (size_t)item + w;
+        const float mw = ws.part_ml[(slot * G + h) * 2];
+        const float lw = ws.part_ml[(slot * G + h) * 2 + 1];
+        const float f = exp2f(mw - M);
+        L += f * lw;
+        const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
+        acc.x += f * ow.x;
+        acc.y += f * ow.y;
+        acc.z += f * ow.z;
+        acc.w += f * ow.w;
+      }
+      const float inv = 1.f / L;
+      o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+      lse_v = (M + log2f(L)) * kLn2;
+    }
+  }
+  const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
+  if (a.out_bf16) {
+    uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
+  } else {
+    *reinterpret_cast<float4*>((float*)a.out + orow) = o;
+  }
+  if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
+}
+
+int g_workers = 0;
+
+}  // namespace
+
+int decode_workers() {
+  if (g_workers == 0) {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    // two 4-wave workgroups per CU: eight 32-token tiles in flight per CU
+    g_workers = cus * 2 * kWPB;
+  }
+  return g_workers;
+}
+
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers) {
+  return ws_total(B * Hkv, workers, Hq / Hkv, d);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const int n_items = a.B * a.Hkv;
+  const int workers = decode_workers();
+  const int blocks = workers / kWPB;
+  if (a.io_bf16) {
+    decode_bf16_kernel<<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+  } else if (a.d == 64) {
+    decode_f32_kernel<64><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+  } else {
+    decode_f32_kernel<128><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = a.Hq / a.Hkv;
+  decode_merge_kernel<<<n_items, G * a.d / 4, 0, s>>>(a, n_items, workers);
+  return hipGetLastError();
+}
+
+}  // namespace spa

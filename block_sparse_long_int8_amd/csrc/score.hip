@@ -1,0 +1,199 @@
+// Indexer scoring kernels.
+//
+// Score of a query row against key block t (SpotAttention page, §1
+// "Arquitectura del Selector"): sum over indexer heads h of
+// w_h * ReLU(qI_h . kI_{h,t}); the vectors are int8 of rank r (RTPurbo page,
+// §2) and every product is accumulated exactly in int32.
+//
+//  * decode: one thread per key block; int8 dot products with v_dot4 (4 MACs
+//    per instruction) over 16-byte loads of the block's [H, r] row.
+//  * prefill: int8 MFMA 32x32x16 -- one MFMA per indexer head covers 32 query
+//    blocks x 32 key blocks with K = r = 16, so no MAC is padding; ReLU and the
+//    head weights are applied per head in the epilogue (the ReLU sits inside
+//    the head sum, so heads cannot be folded into the K dimension).
+//  * pooling: per-token vectors averaged per block and rounded to
+//    floor(mean + 1/2) (PBS-Attn page, §4: block importance by mean pooling).
+#include "spa_internal.h"
+
+namespace spa {
+
+namespace {
+
+constexpr int INT32_MIN_V = (int)0x80000000;
+
+__device__ __forceinline__ int floor_div_pos(int a, int b) {  // b > 0
+  int q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// ---------------------------------------------------------------- decode ----
+// grid: (ceil(nKb / 256), B); block 256.
+__global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restrict__ qI,
+                                                           const int8_t* __restrict__ kI,
+                                                           const int8_t* __restrict__ w, int H,
+                                                           int r, int nKb,
+                                                           const int32_t* __restrict__ seq_len,
+                                                           int blk, int32_t* __restrict__ scores) {
+  __shared__ int q_words[256];  // H*r/4 <= 256
+  __shared__ int w_s[256];
+  const int b = blockIdx.y;
+  const int HR = H * r;
+  const int nw = HR >> 2;
+  const int* q_src = reinterpret_cast<const int*>(qI + (size_t)b * HR);
+  for (int t = threadIdx.x; t < nw; t += blockDim.x) q_words[t] = q_src[t];
+  for (int t = threadIdx.x; t < H; t += blockDim.x) w_s[t] = w[(size_t)b * H + t];
+  __syncthreads();
+
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= nKb) return;
+  const int L = seq_len[b];
+  const int nbv = min(nKb, (L + blk - 1) / blk);
+  int32_t* dst = scores + (size_t)b * nKb + j;
+  if (j >= nbv) {
+    *dst = INT32_MIN_V;
+    return;
+  }
+  const int wpr = r >> 2;  // words per head
+  const int8_t* row = kI + ((size_t)b * nKb + j) * HR;
+  int total = 0;
+  if ((HR & 15) == 0) {
+    const int4* row4 = reinterpret_cast<const int4*>(row);
+    int h = 0, in_head = 0, dot = 0;
+    for (int c = 0; c < (HR >> 4); ++c) {
+      const int4 kv = row4[c];
+      const int kw[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = __builtin_amdgcn_sdot4(q_words[c * 4 + e], kw[e], dot, false);
+        if (++in_head == wpr) {
+          total += w_s[h] * max(dot, 0);
+          ++h;
+          in_head = 0;
+          dot = 0;
+        }
+      }
+    }
+  } else {
+    const int* roww = reinterpret_cast<const int*>(row);
+    for (int h = 0; h < H; ++h) {
+      int dot = 0;
+      for (int e = 0; e < wpr; ++e) dot = __builtin_amdgcn_sdot4(q_words[h * wpr + e], roww[h * wpr + e], dot, false);
+      total += w_s[h] * max(dot, 0);
+    }
+  }
+  *dst = total;
+}
+
+// --------------------------------------------------------------- pooling ----
+// x_tok [B, n_tok, H*r] int8 whose token 0 is absolute token tok0; block jb of
+// the output covers absolute tokens [tok0 + jb*blk, +blk) below seq_len.
+// grid: (nblocks, B); block = H*r/4 threads (one 4-byte word each).
+__global__ void pool_blocks_kernel(const int8_t* __restrict__ x_tok, int n_tok, int nblocks,
+                                   int tok0, int HR, int blk, const int32_t* __restrict__ seq_len,
+                                   int8_t* __restrict__ out) {
+  const int jb = blockIdx.x;
+  const int b = blockIdx.y;
+  const int word = threadIdx.x;
+  if (word * 4 >= HR) return;
+  const int L = seq_len ? seq_len[b] : tok0 + n_tok;
+  const int a0 = tok0 + jb * blk;
+  const int n = max(0, min(min(a0 + blk, L), tok0 + n_tok) - a0);
+  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+  const int8_t* base = x_tok + ((size_t)b * n_tok + (a0 - tok0)) * HR + word * 4;
+  for (int t = 0; t < n; ++t) {
+    const int v = *reinterpret_cast<const int*>(base + (size_t)t * HR);
+    s0 += (int)(int8_t)(v & 0xFF);
+    s1 += (int)(int8_t)((v >> 8) & 0xFF);
+    s2 += (int)(int8_t)((v >> 16) & 0xFF);
+    s3 += v >> 24;  // arithmetic shift keeps the sign of the top byte
+  }
+  int res = 0;
+  if (n > 0) {
+    const int dn = 2 * n;
+    const int m0 = floor_div_pos(2 * s0 + n, dn), m1 = floor_div_pos(2 * s1 + n, dn);
+    const int m2 = floor_div_pos(2 * s2 + n, dn), m3 = floor_div_pos(2 * s3 + n, dn);
+    res = (m0 & 0xFF) | ((m1 & 0xFF) << 8) | ((m2 & 0xFF) << 16) | ((m3 & 0xFF) << 24);
+  }
+  *reinterpret_cast<int*>(out + ((size_t)b * nblocks + jb) * HR + word * 4) = res;
+}
+
+// ------------------------------------------------------- prefill (MFMA) ----
+// One wave computes a 32 (query blocks) x 32 (key blocks) tile for all heads.
+// v_mfma_i32_32x32x16_i8 operands: lane l supplies row/col (l % 32) and the 8
+// K-elements 8*(l/32)..+7; the result gives lane l column (l % 32) and rows
+// 8*(v/4) + 4*(l/32) + (v%4), v = 0..15.
+// grid: (ceil(nKb/32), ceil(Mq/32), B); block 64.
+__global__ void __launch_bounds__(64) score_prefill_kernel(const int8_t* __restrict__ qIb,
+                                                          const int8_t* __restrict__ kIb,
+                                                          const int8_t* __restrict__ w, int H,
+                                                          int Mq, int nKb, int q_blk0,
+                                                          const int32_t* __restrict__ seq_len,
+                                                          int blk, int32_t* __restrict__ scores) {
+  const int lane = threadIdx.x;
+  const int j0 = blockIdx.x * 32;
+  const int i0 = blockIdx.y * 32;
+  const int b = blockIdx.z;
+  const int col = j0 + (lane & 31);
+  const int half = lane >> 5;
+  const int nbv = seq_len ? min(nKb, (seq_len[b] + blk - 1) / blk) : nKb;
+
+  int acc[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0;
+
+  // the whole tile lies on or above the diagonal: nothing to compute
+  const bool any = j0 < q_blk0 + min(i0 + 32, Mq) - 1 && j0 < nbv;
+  if (any) {
+    const int arow = i0 + (lane & 31);
+    for (int h = 0; h < H; ++h) {
+      long a = 0, bb = 0;
+      if (arow < Mq) a = *reinterpret_cast<const long*>(qIb + (((size_t)b * Mq + arow) * H + h) * 16 + half * 8);
+      if (col < nKb) bb = *reinterpret_cast<const long*>(kIb + (((size_t)b * nKb + col) * H + h) * 16 + half * 8);
+      i32x16 d = {0};
+      d = __builtin_amdgcn_mfma_i32_32x32x16_i8(a, bb, d, 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = i0 + 8 * (v >> 2) + 4 * half + (v & 3);
+        const int wv = row < Mq ? (int)w[((size_t)b * Mq + row) * H + h] : 0;
+        acc[v] += wv * max(d[v], 0);
+      }
+    }
+  }
+  if (col >= nKb) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = i0 + 8 * (v >> 2) + 4 * half + (v & 3);
+    if (row >= Mq) continue;
+    const bool valid = col < q_blk0 + row && col < nbv;
+    scores[((size_t)b * Mq + row) * nKb + col] = valid ? acc[v] : INT32_MIN_V;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
+                               int r, int nKb, const int32_t* seq_len, int blk, int32_t* scores,
+                               hipStream_t s) {
+  dim3 grid((nKb + 255) / 256, B);
+  score_decode_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, r, nKb, seq_len, blk, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok, int nblocks, int tok0, int H,
+                              int r, int blk, const int32_t* seq_len, int8_t* out, hipStream_t s) {
+  const int HR = H * r;
+  dim3 grid(nblocks, B);
+  pool_blocks_kernel<<<grid, (HR / 4 + 63) / 64 * 64, 0, s>>>(x_tok, n_tok, nblocks, tok0, HR,
+                                                                blk, seq_len, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_prefill(const int8_t* qIb, const int8_t* kIb, const int8_t* w, int B,
+                                int H, int Mq, int nKb, int q_blk0, const int32_t* seq_len,
+                                int blk, int32_t* scores, hipStream_t s) {
+  dim3 grid((nKb + 31) / 32, (Mq + 31) / 32, B);
+  score_prefill_kernel<<<grid, 64, 0, s>>>(qIb, kIb, w, H, Mq, nKb, q_blk0, seq_len, blk, scores);
+  return hipGetLastError();
+}
+
+}  // namespace spa

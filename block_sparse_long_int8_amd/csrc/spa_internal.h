@@ -1,0 +1,109 @@
+// Internal declarations shared by the HIP kernels and the C-ABI layer.
+// gfx950 only: 64-wide waves, MFMA builtins of CDNA4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace spa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 bit helpers (bf16 is carried as uint16 bit patterns) ----------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---- cross-lane helpers ---------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+__device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
+
+// ---- launch plumbing --------------------------------------------------------
+struct LaunchStatus {
+  int code;  // 0 ok, else hipError_t value
+};
+
+// Score kernels (score.hip)
+hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
+                               int r, int nKb, const int32_t* seq_len, int blk, int32_t* scores,
+                               hipStream_t s);
+hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok_per_seq, int nblocks,
+                              int tok0, int H, int r, int blk, const int32_t* seq_len,
+                              int8_t* out, hipStream_t s);
+hipError_t launch_score_prefill(const int8_t* qIb, const int8_t* kIb, const int8_t* w, int B,
+                                int H, int Mq, int nKb, int q_blk0, const int32_t* seq_len,
+                                int blk, int32_t* scores, hipStream_t s);
+
+// Selection kernels (select.hip)
+struct SelectArgs {
+  const int32_t* scores;
+  int B, M, nKb, q_blk0;
+  const int32_t* seq_len;
+  int blk, n_sink, n_local, prefill;
+  int mode;  // 0 top-k, 1 top-p
+  int k;
+  float beta, p;
+  int k_min, k_max;
+  int32_t* idx;
+  int32_t* count;
+  int cap;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+int select_max_blocks();
+
+// Decode attention (decode_attn.hip)
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int io_bf16;
+  const int32_t* seq_len;
+  const int32_t* idx;
+  const int32_t* count;
+  int cap, blk;
+  const uint8_t* head_mode;
+  int sink_tok, window_tok;
+  int B, Hq, Hkv, d, Tcap;
+  float scale;
+  void* out;
+  int out_bf16;
+  float* lse;
+  void* ws;
+};
+size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers);
+int decode_workers();  // persistent workers (waves) for the current device
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Block-sparse prefill (prefill_attn.hip)
+struct PrefillArgs {
+  const void* q;
+  int q_blk0, Tq;
+  const void* k;
+  const void* v;
+  const int32_t* q_pos;
+  const int32_t* k_pos;
+  const int32_t* idx;
+  const int32_t* count;
+  int cap, blk, B, Hq, Hkv, d, T;
+  float scale;
+  void* out;
+  int out_bf16;
+  float* lse;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
+// Segment permutation (permute.hip)
+hipError_t launch_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
+                          const int32_t* perm, int inverse, hipStream_t s);
+
+}  // namespace spa

@@ -1,0 +1,161 @@
+"""The two hot paths as sequences of library calls, with buffers preallocated.
+
+DecodeStep:  spa_index_score -> spa_select_topk | spa_select_topp -> spa_sparse_decode_attn
+PrefillStep: spa_segment_permute (Q, K, V, per-token indexer vectors)
+             -> spa_index_score (per-token, pooled) -> spa_select_topk (prefill rows)
+             -> spa_block_sparse_prefill -> spa_segment_permute (inverse, on O)
+
+Only marshalling lives here; every step runs in the HIP library.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class DecodeSpec:
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    Tcap: int
+    blk: int
+    H_idx: int
+    r: int
+    n_sink: int
+    n_local: int
+    select: str = "topk"          # "topk" | "topp"
+    k: int = 0
+    beta: float = 1.0
+    p: float = 0.9
+    k_min: int = 0
+    k_max: int = 0
+    local_sink_tok: int = 0
+    local_window_tok: int = 0
+    out_dtype: torch.dtype = torch.float32
+
+    @property
+    def nb(self) -> int:
+        return -(-self.Tcap // self.blk)
+
+    @property
+    def cap(self) -> int:
+        budget = self.k if self.select == "topk" else self.k_max
+        return max(1, min(self.nb, self.n_sink + self.n_local + budget))
+
+
+class DecodeStep:
+    """One decode step of one attention layer; owns its scratch and output buffers."""
+
+    def __init__(self, spec: DecodeSpec, device="cuda"):
+        self.spec = s = spec
+        dev = torch.device(device)
+        self.scores = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((s.B, s.cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((s.B,), dtype=torch.int32, device=dev)
+        self.out = torch.empty((s.B, s.Hq, s.d), dtype=s.out_dtype, device=dev)
+        self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=dev)
+        n = L.spa_sparse_decode_attn_workspace_size(s.B, s.Hq, s.Hkv, s.d)
+        self.ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
+
+    def score(self, qI, kI, w, seq_len):
+        s = self.spec
+        return L.spa_index_score(qI, kI, w, s.blk, seq_len=seq_len, mode=L.SPA_SCORE_DECODE, scores=self.scores)
+
+    def select(self, seq_len):
+        s = self.spec
+        if s.select == "topk":
+            return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, seq_len=seq_len,
+                                     idx=self.idx, count=self.count)
+        return L.spa_select_topp(self.scores, s.blk, s.n_sink, s.n_local, s.beta, s.p, s.k_min, s.k_max, s.cap,
+                                 seq_len=seq_len, idx=self.idx, count=self.count)
+
+    def attend(self, q, k_cache, v_cache, seq_len, head_mode=None):
+        s = self.spec
+        return L.spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, self.idx, self.count, s.blk,
+                                        head_mode=head_mode, local_sink_tok=s.local_sink_tok,
+                                        local_window_tok=s.local_window_tok, out=self.out, lse=self.lse,
+                                        ws=self.ws)
+
+    def __call__(self, q, k_cache, v_cache, qI, kI, w, seq_len, head_mode=None):
+        self.score(qI, kI, w, seq_len)
+        self.select(seq_len)
+        return self.attend(q, k_cache, v_cache, seq_len, head_mode)
+
+
+@dataclass
+class PrefillSpec:
+    B: int
+    T: int
+    Hq: int
+    Hkv: int
+    d: int
+    blk: int
+    H_idx: int
+    r: int
+    k: int
+    n_sink: int
+    n_local: int
+    seg: int
+    out_dtype: torch.dtype = torch.float32
+
+    @property
+    def nb(self) -> int:
+        return -(-self.T // self.blk)
+
+    @property
+    def cap(self) -> int:
+        return max(1, min(self.nb, self.n_sink + self.n_local + 1 + self.k))
+
+
+class PrefillStep:
+    """Permuted block-sparse prefill of one attention layer (one chunk covering T)."""
+
+    def __init__(self, spec: PrefillSpec, device="cuda"):
+        self.spec = s = spec
+        dev = torch.device(device)
+        bf = torch.bfloat16
+        self.qp = torch.empty((s.B, s.Hq, s.T, s.d), dtype=bf, device=dev)
+        self.kp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
+        self.vp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
+        self.qIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
+        self.kIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
+        self.scores = torch.empty((s.B, s.nb, s.nb), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((s.B, s.nb, s.cap), dtype=torch.int32, device=dev)
+        self.count = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
+        n = L.spa_index_score_workspace_size(s.B, s.H_idx, s.r, s.nb, s.nb, L.SPA_SCORE_PREFILL_TOKENS)
+        self.score_ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
+        self.out_slot = torch.empty((s.B, s.Hq, s.T, s.d), dtype=s.out_dtype, device=dev)
+        self.lse_slot = torch.empty((s.B, s.Hq, s.T), dtype=torch.float32, device=dev)
+        self.out = torch.empty_like(self.out_slot)
+        self.pos = None
+
+    def front(self, qI_tok, kI_tok, w, perm):
+        """Permute the indexer inputs, pool, score and select."""
+        s = self.spec
+        L.spa_segment_permute(qI_tok, perm, s.seg, dim=1, dst=self.qIp)
+        L.spa_segment_permute(kI_tok, perm, s.seg, dim=1, dst=self.kIp)
+        L.spa_index_score(self.qIp, self.kIp, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
+                          ws=self.score_ws)
+        L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
+                          count=self.count)
+        return self.idx, self.count
+
+    def __call__(self, q, k, v, qI_tok, kI_tok, w, perm):
+        s = self.spec
+        if self.pos is None or self.pos.data_ptr() == 0 or not torch.equal(self.pos[0], perm):
+            self.pos = perm.reshape(1, -1).expand(s.B, -1).contiguous()
+        L.spa_segment_permute(q, perm, s.seg, dim=2, dst=self.qp)
+        L.spa_segment_permute(k, perm, s.seg, dim=2, dst=self.kp)
+        L.spa_segment_permute(v, perm, s.seg, dim=2, dst=self.vp)
+        self.front(qI_tok, kI_tok, w, perm)
+        L.spa_block_sparse_prefill(self.qp, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
+                                   k_pos=self.pos, out=self.out_slot, lse=self.lse_slot)
+        L.spa_segment_permute(self.out_slot, perm, s.seg, dim=2, inverse=True, dst=self.out)
+        return self.out

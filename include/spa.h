@@ -1,0 +1,211 @@
+/*
+ * spa.h -- C ABI of the block-sparse long-context attention library (gfx950).
+ *
+ * One decode step of query-dependent block-sparse attention is
+ *     spa_index_score -> spa_select_topk | spa_select_topp -> spa_sparse_decode_attn
+ * and one permuted block-sparse prefill is
+ *     spa_segment_permute -> spa_index_score (prefill) -> spa_select_topk (prefill)
+ *     -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer to a dense row-major array with
+ *     the layout stated at the call; the caller owns all buffers.  The library
+ *     never allocates device memory: temporaries live in a caller-provided
+ *     workspace sized by the matching *_workspace_size function.
+ *   - Calls are asynchronous on the caller's stream (a hipStream_t passed as
+ *     void*; NULL is the default stream).  Nothing synchronises.
+ *   - Arguments are validated on the host before anything is enqueued; on any
+ *     error the function returns a negative status and launches nothing.
+ *     Values inside device arrays (idx, count, perm, positions, seq_len) are
+ *     trusted: they must satisfy the stated ranges.
+ *   - Pointers to bf16/fp32/int tensors must be 16-byte aligned.
+ *   - No global mutable state: calls on different streams may run concurrently
+ *     as long as their workspaces do not overlap.
+ *   - bf16 is passed as its 16-bit pattern (uint16 storage).
+ */
+#ifndef SPA_H_
+#define SPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int spa_status;
+#define SPA_OK 0
+#define SPA_ERR_INVALID_ARG (-1) /* bad shape, null pointer, misalignment, cap too small */
+#define SPA_ERR_UNSUPPORTED (-2) /* valid request outside what the kernels implement     */
+#define SPA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than required            */
+#define SPA_ERR_HIP (-4)         /* the HIP runtime reported an error at launch           */
+
+/* element types of attention inputs/outputs */
+#define SPA_F32 0
+#define SPA_BF16 1
+
+/* spa_index_score modes */
+#define SPA_SCORE_DECODE 0         /* one query row per sequence against its key blocks  */
+#define SPA_SCORE_PREFILL_POOLED 1 /* query blocks x key blocks, block vectors given     */
+#define SPA_SCORE_PREFILL_TOKENS 2 /* as POOLED, per-token vectors pooled by the library */
+
+/* Human-readable name of a status code (static storage). */
+const char* spa_status_string(spa_status s);
+
+/* Detail of the last error returned on the calling host thread ("" if none). */
+const char* spa_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int spa_version(void);
+
+/*
+ * spa_index_score -- int8 indexer block scores, exact in int32.
+ *
+ * Defined by the SpotAttention page, §1 "Arquitectura del Selector": a query
+ * row's score for key block t is sum_h w_h * ReLU(qI_h . kI_{h,t}) over H_idx
+ * indexer heads, with per-head projections of rank r (r = 16 on the RTPurbo
+ * page, §2) given here as int8 vectors.  Products are accumulated exactly in
+ * int32; the host rejects H_idx*r > 1024 so no score can overflow.
+ *
+ * mode SPA_SCORE_DECODE (Mq must be 1):
+ *   qI [B, H_idx, r], kI [B, nKb, H_idx, r], w [B, H_idx]  ->  scores [B, nKb].
+ *   Blocks j >= ceil(seq_len[b]/blk) get INT32_MIN.  seq_len [B] is required.
+ * mode SPA_SCORE_PREFILL_POOLED:
+ *   qI [B, Mq, H_idx, r] are the pooled vectors of query blocks q_blk0..q_blk0+Mq-1,
+ *   kI [B, nKb, H_idx, r] the pooled key-block vectors, w [B, Mq, H_idx]
+ *   -> scores [B, Mq, nKb], defined for key blocks j < q_blk0 + i (strictly
+ *   before the query block, and j < ceil(seq_len[b]/blk) when seq_len is given);
+ *   INT32_MIN elsewhere.  seq_len may be NULL.
+ * mode SPA_SCORE_PREFILL_TOKENS:
+ *   qI [B, Mq*blk, H_idx, r] per-token query vectors of the chunk (its first
+ *   token is block q_blk0's first token), kI [B, nKb*blk, H_idx, r] per-token
+ *   key vectors; each block is mean-pooled to floor(mean + 1/2) over its tokens
+ *   below seq_len (block importance by mean pooling, PBS-Attn page §4), then
+ *   scored as in POOLED mode.  Needs spa_index_score_workspace_size bytes.
+ * Supported: r % 4 == 0, 1 <= H_idx, H_idx*r <= 1024; PREFILL modes need r == 16.
+ */
+spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
+                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len, int blk,
+                           int mode, int32_t* scores, void* ws, size_t ws_bytes, void* stream);
+size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, int mode);
+
+/*
+ * spa_select_topk -- static top-k block selection with reserved blocks.
+ *
+ * RTPurbo page §3 (fixed top-k budget) with the reserved blocks of the
+ * SpotAttention page §3 (sink prefix and recency suffix always kept) and the
+ * always-visible current chunk of the HGA page ("Mecanismo Central").
+ * Per row, candidates are ranked by (score descending, block index ascending)
+ * and the first min(k, #candidates) are kept.
+ *
+ * scores [B, M, nKb] int32 (as written by spa_index_score).
+ * prefill == 0 (decode, M must be 1): with e = ceil(seq_len[b]/blk) valid blocks,
+ *   reserved = {0..n_sink-1} and {e-n_local..e-1}; candidates = the other valid blocks.
+ * prefill == 1: row i is query block a = q_blk0 + i; reserved = {0..n_sink-1} (those <= a),
+ *   {a-n_local..a-1} and the diagonal {a}; candidates = the other blocks j < a.
+ *   seq_len may be NULL (then every block below nKb is valid).
+ * Output: idx [B, M, cap] int32, ascending block indices of reserved + chosen,
+ *   padded with -1; count [B, M] int32 = number of valid entries.
+ * Errors: SPA_ERR_INVALID_ARG if cap < n_sink + n_local + k (+1 in prefill).
+ * Supported: nKb <= 4096.  No workspace needed (ws may be NULL).
+ */
+spa_status spa_select_topk(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                           const int32_t* seq_len, int blk, int n_sink, int n_local, int prefill,
+                           int k, int32_t* idx, int32_t* count, int cap, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/*
+ * spa_select_topp -- dual top-p block selection.
+ *
+ * RTPurbo page §3 and SpotAttention page §3: the reserved sink / recency
+ * blocks are always kept; over the remaining candidates (the residual
+ * distribution) the masses softmax(beta * score) are accumulated in rank order
+ * (score descending, index ascending) until the cumulative mass reaches p; the
+ * prefix length is clamped to [k_min, k_max] (k_min is the floor of the
+ * SpotAttention page, k_max a cap on the workspace of the attention step) and
+ * to the number of candidates.  Masses are computed in fp32 on the device.
+ * Arguments and outputs as spa_select_topk; cap >= n_sink + n_local + k_max
+ * (+1 in prefill).  0 < p <= 1, beta >= 0, 0 <= k_min <= k_max.
+ */
+spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                           const int32_t* seq_len, int blk, int n_sink, int n_local, int prefill,
+                           float beta, float p, int k_min, int k_max, int32_t* idx, int32_t* count,
+                           int cap, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * spa_sparse_decode_attn -- exact softmax attention over the selected tokens.
+ *
+ * HGA page, "Atención Exacta de Token": a standard softmax over exactly the
+ * selected token set.  RTPurbo page §1: retrieval heads read the selected
+ * blocks, local heads read attention-sink tokens plus a sliding window.
+ * Split over the selected tokens (each split keeps a running max and sum),
+ * then a log-sum-exp merge.
+ *
+ * q [B, Hq, d]; k_cache, v_cache [B, Hkv, Tcap, d] (io_dtype SPA_BF16 or
+ * SPA_F32); query head h reads KV head h / (Hq/Hkv).  The query is the token at
+ * position seq_len[b]-1, already in the cache.
+ * head_mode [Hkv] uint8 (NULL = all 0): 0 = retrieval head, attends the tokens
+ *   of blocks idx[b, 0..count[b]-1] (idx [B, cap], count [B]) below seq_len;
+ *   1 = local head, attends tokens [0, local_sink_tok) and
+ *   [seq_len-local_window_tok, seq_len).
+ * scale multiplies q.k (normally 1/sqrt(d)).
+ * out [B, Hq, d] (out_dtype SPA_F32 or SPA_BF16); lse [B, Hq] fp32 natural-log
+ * log-sum-exp of the scaled logits (may be NULL).  A head with no token gets
+ * out = 0 and lse = -inf.
+ * Supported: bf16 needs d == 128, f32 needs d in {64, 128}; Hq % Hkv == 0,
+ * Hq/Hkv <= 16; blk in {16, 32, 64, 128}; B*Hkv <= 4096.
+ * Workspace: spa_sparse_decode_attn_workspace_size bytes (depends on the
+ * current device's compute-unit count).
+ */
+spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                                  int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                  const int32_t* count, int cap, int blk, const uint8_t* head_mode,
+                                  int local_sink_tok, int local_window_tok, int B, int Hq, int Hkv,
+                                  int d, int Tcap, float scale, void* out, int out_dtype,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream);
+size_t spa_sparse_decode_attn_workspace_size(int B, int Hq, int Hkv, int d);
+
+/*
+ * spa_block_sparse_prefill -- causal attention of a query chunk over selected key blocks.
+ *
+ * PBS-Attn page: block-sparse attention that skips key blocks outside a
+ * precomputed block list ("Declaración del Problema"), on token orders
+ * permuted inside segments with causality kept on the original positions
+ * (§2); HGA page: exact softmax over the selected tokens.
+ *
+ * q [B, Hq, Tq, d] holds query slots q_blk0*blk .. q_blk0*blk+Tq-1 (slot order);
+ * k, v [B, Hkv, T, d].  q_pos, k_pos [B, T] int32 give each slot's original
+ * position (NULL = identity).  Query slot u in block a = q_blk0 + i attends the
+ * key slots t of blocks idx[b, i, 0..count[b,i]-1] (idx [B, Mq, cap], Mq =
+ * ceil(Tq/blk), count [B, Mq]) with t < T and k_pos[t] <= q_pos[u].
+ * out [B, Hq, Tq, d] (SPA_F32 or SPA_BF16); lse [B, Hq, Tq] fp32 (may be NULL).
+ * A query with no visible key gets out = 0 and lse = -inf.
+ * Supported: bf16 inputs, d == 128, blk == 64, Hq % Hkv == 0.  No workspace.
+ */
+spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const void* k,
+                                    const void* v, const int32_t* q_pos, const int32_t* k_pos,
+                                    const int32_t* idx, const int32_t* count, int cap, int blk,
+                                    int B, int Hq, int Hkv, int d, int T, float scale, void* out,
+                                    int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/*
+ * spa_segment_permute -- gather or scatter rows through a segment-wise permutation.
+ *
+ * PBS-Attn page §1 (keys/values permuted in pairs leave the output unchanged,
+ * permuted queries permute the output, the inverse restores the order) and §2
+ * (permutations stay inside contiguous segments of seg tokens).
+ * src and dst are viewed as [outer, T, row_bytes].  inverse == 0:
+ * dst[o, t] = src[o, perm[t]]; inverse == 1: dst[o, perm[t]] = src[o, t].
+ * perm [T] int32 must map every segment [s*seg, (s+1)*seg) onto itself (not
+ * checked).  src and dst must not overlap.  Pointers need 16-byte alignment
+ * only when row_bytes % 16 == 0 (the fast path); otherwise any alignment.
+ */
+spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
+                               const int32_t* perm, int seg, int inverse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H_ */

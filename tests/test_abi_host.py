@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects invalid arguments before touching the GPU.  No GPU needed.
+"""
+import ctypes
+
+import pytest
+
+import block_sparse_long_int8_amd as S
+
+L = S.lib()
+N = None
+
+
+def test_exports_every_declared_symbol():
+    names = S.declared_symbols()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version():
+    assert L.spa_status_string(0) == b"SPA_OK"
+    assert L.spa_status_string(-1) == b"SPA_ERR_INVALID_ARG"
+    assert L.spa_status_string(-4) == b"SPA_ERR_HIP"
+    assert L.spa_version() >= 100
+
+
+def _fake(n=1):
+    # aligned non-null host addresses: validation must fail before any dereference
+    return ctypes.c_void_p(0x1000 * n)
+
+
+def test_index_score_rejections():
+    f = L.spa_index_score
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 7, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert b"unknown mode" in L.spa_last_error()
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 15, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 128, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 2, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(N, _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    # misaligned kI
+    assert f(_fake(), ctypes.c_void_p(0x2004), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    # prefill needs r == 16
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 8, 4, 10, 0, N, 64, 1, _fake(5), N, 0, N) == S.SPA_ERR_UNSUPPORTED
+    # per-token prefill without workspace
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_WORKSPACE
+    # empty batch is a valid no-op
+    assert f(N, N, N, 0, 8, 16, 1, 10, 0, N, 64, 0, N, N, 0, N) == S.SPA_OK
+    assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 2) == 2 * 1024 * 128
+    assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 0) == 0
+
+
+def test_select_rejections():
+    tk = L.spa_select_topk
+    # cap smaller than reserved + k
+    assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 68, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert b"cap" in L.spa_last_error()
+    # decode rows need M == 1 and seq_len
+    assert tk(_fake(), 1, 2, 100, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tk(_fake(), 1, 1, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tk(_fake(), 1, 1, 5000, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_UNSUPPORTED
+    assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, -1, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    tp = L.spa_select_topp
+    assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 1.5, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 32, 16, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, float("nan"), 0.9, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 16, 512, _fake(3), _fake(4), 516, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tp(N, 0, 1, 100, 0, N, 64, 1, 4, 0, 0.125, 0.9, 16, 512, N, N, 517, N, 0, N) == S.SPA_OK
+
+
+def test_decode_attn_rejections():
+    f = L.spa_sparse_decode_attn
+    args = dict(q=_fake(), k=_fake(2), v=_fake(3), io=S.SPA_BF16, sl=_fake(4), idx=_fake(5), cnt=_fake(6), cap=69,
+                blk=64, hm=N, ns=0, nw=0, B=1, Hq=32, Hkv=8, d=128, T=32768, scale=0.088, out=_fake(7),
+                od=S.SPA_F32, lse=N, ws=_fake(8), wsb=1 << 30, st=N)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(*a.values())
+
+    assert call(d=64) == S.SPA_ERR_UNSUPPORTED                 # bf16 needs d = 128
+    assert call(Hq=30) == S.SPA_ERR_INVALID_ARG                # not a multiple of Hkv
+    assert call(Hq=8 * 17) == S.SPA_ERR_UNSUPPORTED             # G > 16
+    assert call(blk=48) == S.SPA_ERR_UNSUPPORTED
+    assert call(io=5) == S.SPA_ERR_INVALID_ARG
+    assert call(od=9) == S.SPA_ERR_INVALID_ARG
+    assert call(scale=float("inf")) == S.SPA_ERR_INVALID_ARG
+    assert call(idx=N) == S.SPA_ERR_INVALID_ARG
+    assert call(ws=N) == S.SPA_ERR_WORKSPACE
+    assert call(wsb=16) == S.SPA_ERR_WORKSPACE
+    assert call(q=ctypes.c_void_p(0x1008)) == S.SPA_ERR_INVALID_ARG
+    assert call(B=0) == S.SPA_OK
+    assert call(io=S.SPA_F32, d=96) == S.SPA_ERR_UNSUPPORTED
+
+
+def test_prefill_and_permute_rejections():
+    f = L.spa_block_sparse_prefill
+    base = [_fake(), 0, 4096, _fake(2), _fake(3), N, N, _fake(4), _fake(5), 34, 64, 1, 32, 8, 128, 4096, 0.088,
+            _fake(6), S.SPA_F32, N, N, 0, N]
+    b = list(base); b[10] = 32
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # blk must be 64
+    b = list(base); b[14] = 64
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # d must be 128
+    b = list(base); b[1] = 10
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # query slots past T
+    b = list(base); b[0] = N
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[2] = 0
+    assert f(*b) == S.SPA_OK                                   # empty chunk
+    p = L.spa_segment_permute
+    assert p(_fake(), _fake(2), 4, 100, 256, _fake(3), 64, 2, N) == S.SPA_ERR_INVALID_ARG
+    assert p(_fake(), _fake(), 4, 100, 256, _fake(3), 64, 0, N) == S.SPA_ERR_INVALID_ARG   # overlap
+    assert p(_fake(), _fake(2), 4, 100, 256, N, 64, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert p(N, N, 0, 100, 256, N, 64, 0, N) == S.SPA_OK

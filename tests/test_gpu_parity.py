@@ -1,0 +1,302 @@
+"""GPU parity against the CPU oracle on small workloads (several tiles, ragged
+tails) through the C ABI: scores and top-k bit-exact, top-p by the set rule,
+attention within max|diff| <= 1e-2 and relative L2 <= 2e-3.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+from gpu_util import attn_close, check_topp_row, dev, sel_lists
+
+pytestmark = pytest.mark.gpu
+
+S = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global S
+    import block_sparse_long_int8_amd as mod
+    mod.lib()
+    S = mod
+    yield
+
+
+DECODE_CFGS = [gen.TINY_DECODE, gen.SMALL_TINY_RAGGED, gen.SMALL_DECODE_TOPK, gen.SMALL_DECODE_TOPP,
+               gen.SMALL_DECODE_HEADSPLIT]
+
+
+def _decode_inputs(cfg):
+    inp = gen.make(cfg)
+    t = dict(
+        q=dev(inp["q"], cfg.dtype), k=dev(inp["k"], cfg.dtype), v=dev(inp["v"], cfg.dtype),
+        qI=dev(inp["qI"]), kI=dev(inp["kI"]), w=dev(inp["w"]), seq_len=dev(inp["seq_len"]),
+        head_mode=dev(inp["head_mode"]))
+    return inp, t
+
+
+def _spec(cfg):
+    return S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta, p=cfg.p,
+                        k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
+                        local_window_tok=cfg.local_window_tok)
+
+
+@pytest.mark.parametrize("cfg", DECODE_CFGS, ids=[c.name for c in DECODE_CFGS])
+def test_decode_step_parity(cfg):
+    print(f"[decode parity] {cfg.name}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    # scores: bit-exact over every block (past-the-end blocks carry INT32_MIN)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    idx_h = step.idx.cpu().numpy()
+    for b in range(cfg.B):
+        assert (idx_h[b, len(gsel[b]):] == -1).all(), "padding after count must be -1"
+    if cfg.select == "topk":
+        assert gsel == ref["sel"]
+    else:
+        for b in range(cfg.B):
+            check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    # attention on the GPU's own selection, against fp64
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok)
+    attn_close(step.out.cpu().numpy(), o_ref)
+    assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
+
+
+@pytest.mark.parametrize("cfg", [gen.SMALL_DECODE_TOPK, gen.SMALL_DECODE_TOPP], ids=["topk", "topp"])
+def test_decode_deterministic(cfg):
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    outs = []
+    for _ in range(3):
+        step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+        torch.cuda.synchronize()
+        outs.append((step.idx.clone(), step.out.clone(), step.lse.clone()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a, b)
+
+
+def test_decode_bf16_output_and_no_lse():
+    cfg = gen.SMALL_DECODE_TOPK
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"])
+    o32 = step.out.clone()
+    ob, lse = S.spa_sparse_decode_attn(t["q"], t["k"], t["v"], t["seq_len"], step.idx, step.count, cfg.blk,
+                                       out_dtype=torch.bfloat16, want_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    # bf16 output is the fp32 output rounded to nearest even
+    assert torch.equal(ob, o32.to(torch.bfloat16))
+
+
+def test_decode_local_window_covers_all_equals_dense():
+    # local heads with a window wider than the sequence see every token
+    cfg = gen.SMALL_TINY_RAGGED
+    inp, t = _decode_inputs(cfg)
+    hm = torch.ones(cfg.Hkv, dtype=torch.uint8, device="cuda")
+    idx = torch.zeros((cfg.B, 1), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((cfg.B,), dtype=torch.int32, device="cuda")
+    out, lse = S.spa_sparse_decode_attn(t["q"], t["k"], t["v"], t["seq_len"], idx, cnt, cfg.blk, head_mode=hm,
+                                        local_sink_tok=0, local_window_tok=10 ** 6)
+    torch.cuda.synchronize()
+    full = [list(range(-(-int(L) // cfg.blk))) for L in inp["seq_len"]]
+    o_ref, _ = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], full, cfg.blk)
+    attn_close(out.cpu().numpy(), o_ref)
+
+
+def test_decode_empty_selection_gives_zero_and_neg_inf():
+    cfg = gen.SMALL_DECODE_TOPK
+    inp, t = _decode_inputs(cfg)
+    idx = torch.full((cfg.B, 4), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((cfg.B,), dtype=torch.int32, device="cuda")
+    out, lse = S.spa_sparse_decode_attn(t["q"], t["k"], t["v"], t["seq_len"], idx, cnt, cfg.blk)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out) == 0
+    assert torch.isneginf(lse).all()
+
+
+def test_decode_batch_zero_is_noop():
+    q = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.empty((0, 1, 64, 128), dtype=torch.bfloat16, device="cuda")
+    z = torch.empty((0,), dtype=torch.int32, device="cuda")
+    zi = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    out, lse = S.spa_sparse_decode_attn(q, k, k, z, zi, z, 64)
+    assert out.shape == (0, 4, 128)
+
+
+def test_topk_edge_cases():
+    # k = 0 keeps only reserved blocks; short sequences keep everything; ties go to the lowest index
+    B, nb, blk = 3, 40, 16
+    s = np.zeros((B, nb), dtype=np.int32)
+    s[0, [5, 9, 13]] = 7
+    s[1, :] = 3
+    L = np.array([nb * blk, 3 * blk - 5, 1], dtype=np.int32)
+    sc = dev(s)
+    # blocks past the sequence end are never read, whatever they hold
+    for k in (0, 2, 5, 100):
+        idx, cnt = S.spa_select_topk(sc, blk, 1, 2, k, 1 + 2 + k, seq_len=dev(L))
+        gsel = sel_lists(idx, cnt)
+        ref, _ = O.select_decode(s.astype(np.int64), L, blk, 1, 2, "topk", k=k)
+        assert gsel == ref, (k, gsel, ref)
+
+
+def test_select_prefill_rows_match_oracle():
+    rng = np.random.default_rng(3)
+    M, nKb = 70, 70
+    s = rng.integers(0, 50, size=(2, M, nKb)).astype(np.int32)   # heavy ties
+    for n_sink, n_local, k in ((1, 0, 6), (2, 3, 4), (0, 0, 0)):
+        cap = n_sink + n_local + 1 + k
+        idx, cnt = S.spa_select_topk(dev(s), 64, n_sink, n_local, k, cap, prefill=True)
+        gsel = sel_lists(idx, cnt)
+        ref = O.select_prefill_topk(s.astype(np.int64), n_sink, n_local, k)
+        assert gsel == ref
+        # a later chunk of rows with q_blk0 > 0
+        idx2, cnt2 = S.spa_select_topk(dev(np.ascontiguousarray(s[:, 30:])), 64, n_sink, n_local, k, cap,
+                                       prefill=True, q_blk0=30)
+        ref2 = O.select_prefill_topk(s[:, 30:].astype(np.int64), n_sink, n_local, k, q_blk0=30)
+        assert sel_lists(idx2, cnt2) == ref2
+
+
+def test_topp_edge_cases():
+    # one-hot -> K_min; p = 1 -> everything up to K_max; equal scores -> lowest indices
+    B, nb, blk = 3, 64, 64
+    s = np.zeros((B, nb), dtype=np.int32)
+    s[0, 17] = 20000
+    s[1] = np.arange(nb)
+    L = np.full(B, nb * blk, dtype=np.int32)
+    for p, kmin, kmax in ((0.9, 4, 20), (1.0, 0, 64), (0.5, 0, 64)):
+        cap = 1 + 4 + kmax
+        idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, 0.125, p, kmin, kmax, cap, seq_len=dev(L))
+        gsel = sel_lists(idx, cnt)
+        ref, info = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topp", beta=0.125, p=p, k_min=kmin, k_max=kmax)
+        for b in range(B):
+            info[b]["reserved"] = O.decode_sets(int(L[b]), blk, 1, 4)[0]
+            check_topp_row(gsel[b], info[b], kmin, kmax, p)
+
+
+def test_scores_prefill_pooled_and_tokens():
+    cfg = gen.SMALL_PREFILL
+    inp = gen.make(cfg)
+    qIb = O.pool_blocks(inp["qI_tok"], cfg.blk)
+    kIb = O.pool_blocks(inp["kI_tok"], cfg.blk)
+    ref = O.score_prefill(qIb, kIb, inp["w"])
+    s1 = S.spa_index_score(dev(qIb), dev(kIb), dev(inp["w"]), cfg.blk, mode=S.SPA_SCORE_PREFILL_POOLED)
+    s2 = S.spa_index_score(dev(inp["qI_tok"]), dev(inp["kI_tok"]), dev(inp["w"]), cfg.blk,
+                           mode=S.SPA_SCORE_PREFILL_TOKENS)
+    torch.cuda.synchronize()
+    assert np.array_equal(s1.cpu().numpy().astype(np.int64), ref)
+    assert np.array_equal(s2.cpu().numpy().astype(np.int64), ref)
+    # a chunk of query blocks 7..19 scored on its own gives the same rows
+    s3 = S.spa_index_score(dev(np.ascontiguousarray(qIb[:, 7:20])), dev(kIb),
+                           dev(np.ascontiguousarray(inp["w"][:, 7:20])), cfg.blk, mode=S.SPA_SCORE_PREFILL_POOLED,
+                           q_blk0=7)
+    torch.cuda.synchronize()
+    assert np.array_equal(s3.cpu().numpy().astype(np.int64), ref[:, 7:20])
+
+
+def test_pool_ragged_tokens():
+    rng = np.random.default_rng(9)
+    B, T, blk = 2, 5 * 64, 64
+    x = rng.integers(-128, 128, size=(B, T, 8, 16), dtype=np.int8)
+    w = rng.integers(1, 5, size=(B, 5, 8), dtype=np.int8)
+    L = np.array([T, 3 * 64 + 17], dtype=np.int32)
+    s = S.spa_index_score(dev(x), dev(x), dev(w), blk, seq_len=dev(L), mode=S.SPA_SCORE_PREFILL_TOKENS)
+    torch.cuda.synchronize()
+    for b in range(B):
+        xb = x[b:b + 1, :L[b]]
+        pooled = O.pool_blocks(xb, blk)
+        ref = O.score_prefill(pooled, pooled, w[b:b + 1, :pooled.shape[1]])
+        got = s.cpu().numpy()[b:b + 1, :pooled.shape[1], :pooled.shape[1]].astype(np.int64)
+        assert np.array_equal(got, ref)
+
+
+def test_segment_permute_bitexact():
+    rng = np.random.default_rng(4)
+    T, seg = 1000, 256
+    perm = np.concatenate([s + rng.permutation(min(seg, T - s)) for s in range(0, T, seg)]).astype(np.int32)
+    pd = dev(perm)
+    for shape, dim in (((2, 3, T, 128), 2), ((2, T, 8, 16), 1), ((T, 3), 0), ((4, T, 5), 1)):
+        x = rng.integers(-1000, 1000, size=shape).astype(np.int16 if shape[-1] == 128 else np.int8)
+        xd = dev(x)
+        y = S.spa_segment_permute(xd, pd, seg, dim)
+        z = S.spa_segment_permute(y, pd, seg, dim, inverse=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), O.segment_permute(x, perm, dim))
+        assert np.array_equal(z.cpu().numpy(), x)
+
+
+def _prefill_inputs(cfg):
+    inp = gen.make(cfg)
+    t = dict(q=dev(inp["q"], "bf16"), k=dev(inp["k"], "bf16"), v=dev(inp["v"], "bf16"), qI=dev(inp["qI_tok"]),
+             kI=dev(inp["kI_tok"]), w=dev(inp["w"]), perm=dev(inp["perm"]))
+    return inp, t
+
+
+def _pspec(cfg):
+    return S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg)
+
+
+def test_prefill_pipeline_parity():
+    cfg = gen.SMALL_PREFILL
+    print(f"[prefill parity] {cfg.name}", flush=True)
+    inp, t = _prefill_inputs(cfg)
+    step = S.PrefillStep(_pspec(cfg))
+    out = step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
+    torch.cuda.synchronize()
+    front = O.prefill_front(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
+    assert sel_lists(step.idx, step.count) == front["sel"]
+    ref = O.prefill_step(inp, front=front)
+    attn_close(out.cpu().numpy(), ref["o"])
+    assert np.allclose(step.lse_slot.cpu().numpy(), ref["lse_slot"], atol=1e-4, rtol=1e-5)
+
+
+def test_prefill_chunked_equals_one_shot_bitwise():
+    cfg = gen.SMALL_PREFILL
+    inp, t = _prefill_inputs(cfg)
+    step = S.PrefillStep(_pspec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
+    torch.cuda.synchronize()
+    full = step.out_slot.clone()
+    blk, T = cfg.blk, cfg.T
+    for c0 in range(0, T, 512):
+        b0 = c0 // blk
+        qc = step.qp[:, :, c0:c0 + 512].contiguous()
+        idx = step.idx[:, b0:b0 + 512 // blk].contiguous()
+        cnt = step.count[:, b0:b0 + 512 // blk].contiguous()
+        oc, _ = S.spa_block_sparse_prefill(qc, step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
+                                           q_blk0=b0)
+        torch.cuda.synchronize()
+        assert torch.equal(oc, full[:, :, c0:c0 + 512])
+
+
+def test_prefill_all_blocks_equals_dense_causal():
+    # identity positions, every past block selected -> dense causal attention
+    cfg = gen.SMALL_PREFILL
+    inp, t = _prefill_inputs(cfg)
+    nb = cfg.nb
+    idx = np.full((1, nb, nb), -1, dtype=np.int32)
+    cnt = np.zeros((1, nb), dtype=np.int32)
+    for i in range(nb):
+        idx[0, i, :i + 1] = np.arange(i + 1)
+        cnt[0, i] = i + 1
+    out, _ = S.spa_block_sparse_prefill(t["q"], t["k"], t["v"], dev(idx), dev(cnt), cfg.blk)
+    torch.cuda.synchronize()
+    pos = np.arange(cfg.T)
+    blocks = [0, 1, 7, nb - 1]
+    ref, _ = O.prefill_attention(inp["q"], inp["k"], inp["v"], "bf16", pos, pos,
+                                 [[list(range(i + 1)) for i in range(nb)]], cfg.blk, blocks=blocks)
+    rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in blocks])
+    attn_close(out.cpu().numpy()[:, :, rows], ref[:, :, rows])
