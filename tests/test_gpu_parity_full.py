@@ -1,0 +1,88 @@
+"""GPU parity at the five named workloads' full sizes, in the launch
+configuration the benchmark uses.  Decode workloads are checked in full
+(the oracle finishes them in seconds); the 64K permuted prefill is checked
+bit-exactly on every score and every selected block list, and on sampled
+query blocks for the attention output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+from gpu_util import attn_close, check_topp_row, dev, sel_lists
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    import block_sparse_long_int8_amd as mod
+    mod.lib()
+    return mod
+
+
+FULL_DECODE = [gen.TINY_DECODE, gen.DECODE_32K, gen.DECODE_64K_HEADSPLIT, gen.DECODE_128K_TOPP]
+
+
+@pytest.mark.parametrize("cfg", FULL_DECODE, ids=[c.name for c in FULL_DECODE])
+def test_full_decode_parity(S, cfg):
+    print(f"[full decode parity] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta, p=cfg.p,
+                        k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
+                        local_window_tok=cfg.local_window_tok)
+    step = S.DecodeStep(spec)
+    q, k, v = dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype), dev(inp["v"], cfg.dtype)
+    step(q, k, v, dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), dev(inp["head_mode"]))
+    torch.cuda.synchronize()
+    print(f"[full decode parity] {cfg.name}: oracle", flush=True)
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    if cfg.select == "topk":
+        assert gsel == ref["sel"]
+    else:
+        for b in range(cfg.B):
+            check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok)
+    ma, rl = attn_close(step.out.cpu().numpy(), o_ref)
+    print(f"[full decode parity] {cfg.name}: max|d| {ma:.2e} rel-L2 {rl:.2e}", flush=True)
+    assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
+    # the same workload with the K/V cache at another address (the benchmark's rotation) is bit-identical
+    out0 = step.out.clone()
+    step.attend(q, k.clone(), v.clone(), dev(inp["seq_len"]), dev(inp["head_mode"]))
+    torch.cuda.synchronize()
+    assert torch.equal(out0, step.out)
+
+
+def test_full_prefill_64k_parity(S):
+    cfg = gen.PREFILL_64K
+    print(f"[full prefill parity] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    step = S.PrefillStep(S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk,
+                                       H_idx=cfg.H_idx, r=cfg.r, k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                                       seg=cfg.seg))
+    out = step(dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"), dev(inp["qI_tok"]),
+               dev(inp["kI_tok"]), dev(inp["w"]), dev(inp["perm"]))
+    torch.cuda.synchronize()
+    perm = inp["perm"]
+    # permutation: sampled slots of the permuted Q/K are the source rows perm[t]
+    rows = np.array([0, 1, 4095, 4096, 30000, 65535])
+    qp = step.qp[:, :, rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(qp, inp["q"][:, :, perm[rows]])
+    print(f"[full prefill parity] {cfg.name}: oracle front end", flush=True)
+    front = O.prefill_front(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
+    assert sel_lists(step.idx, step.count) == front["sel"]
+    blocks = [0, 1, 2, 63, 64, 65, 511, 1023]
+    print(f"[full prefill parity] {cfg.name}: oracle attention on blocks {blocks}", flush=True)
+    ref = O.prefill_step(inp, front=front, blocks=blocks)
+    slots = np.concatenate([np.arange(i * cfg.blk, (i + 1) * cfg.blk) for i in blocks])
+    o_slot = step.out_slot.cpu().numpy()
+    attn_close(o_slot[:, :, slots], ref["o_slot"][:, :, slots])
+    # the inverse permutation puts slot t at original position perm[t]
+    o_final = out[:, :, torch.from_numpy(perm[slots]).long().cuda()].cpu().numpy()
+    assert np.array_equal(o_final, o_slot[:, :, slots])
