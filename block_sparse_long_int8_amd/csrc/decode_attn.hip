@@ -92,11 +92,23 @@ __device__ __forceinline__ int item_tiles(const DecodeArgs& a, int b, int g, int
   return a.count[b] * tpb;
 }
 
+// Block indices of a retrieval item, 64 at a time in the lanes of a wave, so
+// a tile's address needs no dependent global load.
+struct IdxWindow {
+  int base;  // first block slot held
+  int val;   // lane l holds idx[b, base + l]
+};
+
+__device__ __forceinline__ void load_window(const DecodeArgs& a, int b, int base, int cnt, IdxWindow& win) {
+  const int l = threadIdx.x & (kWave - 1);
+  win.base = base;
+  win.val = base + l < cnt ? a.idx[(size_t)b * a.cap + base + l] : 0;
+}
+
 // First token and number of valid tokens of tile u of item (b, g).
-__device__ __forceinline__ void tile_info(const DecodeArgs& a, int b, int g, int u, int tpb,
-                                          int& tok0, int& nvalid) {
-  const int L = a.seq_len[b];
-  if (a.head_mode && a.head_mode[g]) {
+__device__ __forceinline__ void tile_info(const DecodeArgs& a, int b, int g, int u, int tpb, int L,
+                                          bool local, int cnt, IdxWindow& win, int& tok0, int& nvalid) {
+  if (local) {
     const int ns = min(a.sink_tok, L);
     const int wstart = max(ns, L - a.window_tok);
     const int nst = (ns + kTile - 1) / kTile;
@@ -108,8 +120,10 @@ __device__ __forceinline__ void tile_info(const DecodeArgs& a, int b, int g, int
       nvalid = min(kTile, L - tok0);
     }
   } else {
-    const int j = a.idx[(size_t)b * a.cap + u / tpb];
-    const int sub = u % tpb;
+    const int slot = u / tpb;
+    if (slot - win.base >= kWave) load_window(a, b, slot, cnt, win);
+    const int j = __builtin_amdgcn_readlane(win.val, slot - win.base);
+    const int sub = u - slot * tpb;
     tok0 = j * a.blk + sub * kTile;
     nvalid = min(min(kTile, a.blk - sub * kTile), L - tok0);
   }
@@ -311,19 +325,24 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, 
 
     int u = t - item_start[item];
     const int u_end = seg_end - item_start[item];
+    const int L = a.seq_len[b];
+    const bool local = a.head_mode && a.head_mode[g];
+    const int cnt = local ? 0 : a.count[b];
+    IdxWindow win;
+    if (!local) load_window(a, b, u / tpb, cnt, win);
     TileRegs A, Bt;
     int tokA, nvA, tokB = 0, nvB = 0;
-    tile_info(a, b, g, u, tpb, tokA, nvA);
+    tile_info(a, b, g, u, tpb, L, local, cnt, win, tokA, nvA);
     if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
     while (u < u_end) {
       if (u + 1 < u_end) {
-        tile_info(a, b, g, u + 1, tpb, tokB, nvB);
+        tile_info(a, b, g, u + 1, tpb, L, local, cnt, win, tokB, nvB);
         if (nvB > 0) load_tile(kb, vb, tokB, nvB, lane, Bt);
       }
       if (nvA > 0) tile_math(A, qreg, nvA, scale_log2, lane, st);
       if (++u >= u_end) break;
       if (u + 1 < u_end) {
-        tile_info(a, b, g, u + 1, tpb, tokA, nvA);
+        tile_info(a, b, g, u + 1, tpb, L, local, cnt, win, tokA, nvA);
         if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
       }
       if (nvB > 0) tile_math(Bt, qreg, nvB, scale_log2, lane, st);
@@ -410,9 +429,14 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 #pragma unroll
       for (int c = 0; c < NDL; ++c) acc[h][c] = 0.f;
     }
+    const int L = a.seq_len[b];
+    const bool local = a.head_mode && a.head_mode[g];
+    const int cnt = local ? 0 : a.count[b];
+    IdxWindow win;
+    if (!local) load_window(a, b, (t - item_start[item]) / tpb, cnt, win);
     for (int u = t - item_start[item]; u < seg_end - item_start[item]; ++u) {
       int tok0, nvalid;
-      tile_info(a, b, g, u, tpb, tok0, nvalid);
+      tile_info(a, b, g, u, tpb, L, local, cnt, win, tok0, nvalid);
       if (nvalid <= 0) continue;
       const float* krow = kc + kv_off + (size_t)(tok0 + min(tau, nvalid - 1)) * DD;
       float sc[8];
@@ -489,34 +513,58 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 }
 
 // ----------------------------------------------------------------- merge ----
-// grid: n_items; block: G * d / 4 threads (one float4 of one head each).
-__global__ void decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
+// One workgroup per item: pass 1 finds each head's maximum over the item's
+// partials, pass 2 sums the rescaled partials; a thread owns one float4 of one
+// head, and the per-slot loads of pass 2 are independent so they overlap.
+constexpr int kMergeThreads = 256;
+
+__global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float Ms[16];
   const int G = a.Hq / a.Hkv;
   const int d = a.d;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
   const int item = blockIdx.x;
   const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
-  const int h = threadIdx.x / (d / 4);
-  const int c4 = threadIdx.x - h * (d / 4);
-  if (h >= G) return;
+  const int tid = threadIdx.x;
   const int share = ws.hdr[1];
   const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
-  float4 o = {0.f, 0.f, 0.f, 0.f};
-  float lse_v = -INFINITY;
-  if (s1 > s0 && share > 0) {
-    const int w0 = s0 / share, w1 = (s1 - 1) / share;
-    float M = -INFINITY;
-    for (int w = w0; w <= w1; ++w) M = fmaxf(M, ws.part_ml[(((size_t)item + w) * G + h) * 2]);
+  const bool any = s1 > s0 && share > 0;
+  const int w0 = any ? s0 / share : 0;
+  const int nsl = any ? (s1 - 1) / share - w0 + 1 : 0;
+  // pass 1: per-head maximum of the partial maxima
+  {
+    const int h = tid % G;
+    float mx = -INFINITY;
+    if (tid < (kMergeThreads / G) * G)
+      for (int sl = tid / G; sl < nsl; sl += kMergeThreads / G)
+        mx = fmaxf(mx, ws.part_ml[(((size_t)item + w0 + sl) * G + h) * 2]);
+    red[tid] = mx;
+    __syncthreads();
+    if (tid < G) {
+      float m = -INFINITY;
+      for (int t = tid; t < (kMergeThreads / G) * G; t += G) m = fmaxf(m, red[t]);
+      Ms[tid] = m;
+    }
+    __syncthreads();
+  }
+  const int per_head = d / 4;
+  for (int t = tid; t < G * per_head; t += kMergeThreads) {
+    const int h = t / per_head;
+    const int c4 = t - h * per_head;
+    const float M = Ms[h];
+    float4 o = {0.f, 0.f, 0.f, 0.f};
+    float lse_v = -INFINITY;
     if (M != -INFINITY) {
       float L = 0.f;
       float4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int w = w0; w <= w1; ++w) {
-        const size_t slot = (size_t)item + w;
-        const float mw = ws.part_ml[(slot * G + h) * 2];
-        const float lw = ws.part_ml[(slot * G + h) * 2 + 1];
-        const float f = exp2f(mw - M);
-        L += f * lw;
+#pragma unroll 4
+      for (int sl = 0; sl < nsl; ++sl) {
+        const size_t slot = (size_t)item + w0 + sl;
+        const float2 ml = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
         const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
+        const float f = exp2f(ml.x - M);
+        L += f * ml.y;
         acc.x += f * ow.x;
         acc.y += f * ow.y;
         acc.z += f * ow.z;
@@ -526,15 +574,15 @@ __global__ void decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
       o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
       lse_v = (M + log2f(L)) * kLn2;
     }
+    const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
+    if (a.out_bf16) {
+      uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+      *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
+    } else {
+      *reinterpret_cast<float4*>((float*)a.out + orow) = o;
+    }
+    if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
   }
-  const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
-  if (a.out_bf16) {
-    uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-    *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
-  } else {
-    *reinterpret_cast<float4*>((float*)a.out + orow) = o;
-  }
-  if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
 }
 
 int g_workers = 0;
@@ -571,8 +619,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int G = a.Hq / a.Hkv;
-  decode_merge_kernel<<<n_items, G * a.d / 4, 0, s>>>(a, n_items, workers);
+  decode_merge_kernel<<<n_items, kMergeThreads, 0, s>>>(a, n_items, workers);
   return hipGetLastError();
 }
 

@@ -5,8 +5,9 @@
 // w_h * ReLU(qI_h . kI_{h,t}); the vectors are int8 of rank r (RTPurbo page,
 // §2) and every product is accumulated exactly in int32.
 //
-//  * decode: one thread per key block; int8 dot products with v_dot4 (4 MACs
-//    per instruction) over 16-byte loads of the block's [H, r] row.
+//  * decode: one lane per (key block, head) for r = 16 (a 16-byte load, four
+//    v_dot4 of 4 MACs each, then a shuffle sum over the block's heads); a
+//    thread-per-block loop handles other r.
 //  * prefill: int8 MFMA 32x32x16 -- one MFMA per indexer head covers 32 query
 //    blocks x 32 key blocks with K = r = 16, so no MAC is padding; ReLU and the
 //    head weights are applied per head in the epilogue (the ReLU sits inside
@@ -82,6 +83,42 @@ __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restr
     }
   }
   *dst = total;
+}
+
+// Fast decode path for r == 16 and a power-of-two H <= 64: one lane per
+// (block, head) loads that head's 16 bytes (the wave reads 1 KB contiguous),
+// four v_dot4 give the head dot, ReLU * w, and H neighbouring lanes sum their
+// heads with xor shuffles.  grid: ceil(B*nKb*H / 256); block 256.
+__global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __restrict__ qI,
+                                                               const int8_t* __restrict__ kI,
+                                                               const int8_t* __restrict__ w, int H,
+                                                               int log2H, int nKb, int B,
+                                                               const int32_t* __restrict__ seq_len,
+                                                               int blk, int32_t* __restrict__ scores) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)B * nKb * H;
+  const bool in = t < total;
+  const long bj = in ? (t >> log2H) : 0;
+  const int h = (int)(t & (H - 1));
+  const int b = (int)(bj / nKb);
+  const int j = (int)(bj - (long)b * nKb);
+  int v = 0;
+  bool valid = false;
+  if (in) {
+    const int L = seq_len[b];
+    valid = j < min(nKb, (L + blk - 1) / blk);
+    if (valid) {
+      const int4 kv = *reinterpret_cast<const int4*>(kI + (size_t)t * 16);
+      const int4 qv = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+      int dot = __builtin_amdgcn_sdot4(qv.x, kv.x, 0, false);
+      dot = __builtin_amdgcn_sdot4(qv.y, kv.y, dot, false);
+      dot = __builtin_amdgcn_sdot4(qv.z, kv.z, dot, false);
+      dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
+      v = (int)w[(size_t)b * H + h] * max(dot, 0);
+    }
+  }
+  for (int o = 1; o < H; o <<= 1) v += __shfl_xor(v, o, kWave);
+  if (in && h == 0) scores[bj] = valid ? v : INT32_MIN_V;
 }
 
 // --------------------------------------------------------------- pooling ----
@@ -174,6 +211,14 @@ __global__ void __launch_bounds__(64) score_prefill_kernel(const int8_t* __restr
 hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
                                int r, int nKb, const int32_t* seq_len, int blk, int32_t* scores,
                                hipStream_t s) {
+  if (r == 16 && H <= kWave && (H & (H - 1)) == 0) {
+    int log2H = 0;
+    while ((1 << log2H) < H) ++log2H;
+    const long total = (long)B * nKb * H;
+    score_decode_r16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(qI, kI, w, H, log2H, nKb, B,
+                                                                             seq_len, blk, scores);
+    return hipGetLastError();
+  }
   dim3 grid((nKb + 255) / 256, B);
   score_decode_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, r, nKb, seq_len, blk, scores);
   return hipGetLastError();

@@ -9,7 +9,12 @@
 // A row's candidates are packed into unique 64-bit keys
 //     ((score ^ 0x80000000) << 32) | ~index
 // so that sorting keys in descending order ranks by score descending and, on
-// equal scores, by lowest block index.  The keys are bitonic-sorted in LDS;
+// equal scores, by lowest block index; when a row's score range leaves room,
+// the key is 32-bit, (score - min) << index_bits | inverted index, which halves
+// the compare and exchange work.  Keys are bitonic-sorted in registers (two to
+// four per thread): in-thread stages need no exchange, lane strides up to 8 use
+// DPP row moves, 16 a swizzle, 32 a permute, and only stages that pair
+// different waves go through LDS;
 // top-k keeps the first k, top-p turns the sorted scores into fp32 masses
 // exp(beta * (s - s_max)), scans them in rank order and keeps the shortest
 // prefix whose normalised mass reaches p (clamped to [k_min, k_max]).  A
@@ -21,8 +26,8 @@ namespace spa {
 
 namespace {
 
-constexpr int kSelThreads = 512;
-constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kMaxBlocks = 4096;
 
 __device__ __forceinline__ unsigned long long make_key(int score, int j) {
@@ -47,8 +52,8 @@ __device__ int block_excl_scan_int(int v, int* scratch, int* total) {
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
   int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
+  const int nw = blockDim.x / kWave;
+  for (int w = 0; w < nw; ++w) {
     const int s = scratch[w];
     off += (w < wid) ? s : 0;
     tot += s;
@@ -70,8 +75,8 @@ __device__ float block_excl_scan_float(float v, float* scratch, float* total) {
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
   float off = 0.f, tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kSelWaves; ++w) {
+  const int nw = blockDim.x / kWave;
+  for (int w = 0; w < nw; ++w) {
     const float s = scratch[w];
     off += (w < wid) ? s : 0.f;
     tot += s;
@@ -81,12 +86,155 @@ __device__ float block_excl_scan_float(float v, float* scratch, float* total) {
   return off + (x - v);
 }
 
-// grid: B*M rows; block kSelThreads; dynamic LDS: n_pad * 8 bytes of keys.
-__global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
-  extern __shared__ unsigned long long keys[];
+__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
+  const unsigned lo = __shfl_xor((unsigned)v, m, kWave);
+  const unsigned hi = __shfl_xor((unsigned)(v >> 32), m, kWave);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Value of lane (l ^ M) for a compile-time M: DPP lane moves for M <= 8
+// (quad permutes and row / half-row mirrors), a swizzle for 16, a permute for 32.
+template <int M>
+__device__ __forceinline__ unsigned lane_xor(unsigned v) {
+  const int x = (int)v;
+  if constexpr (M == 1) {
+    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);     // half-row mirror: l ^ 7
+    return (unsigned)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);   // quad_perm [3,2,1,0]: ^ 3
+  } else if constexpr (M == 8) {
+    const int r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);     // row mirror: l ^ 15
+    return (unsigned)__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true);  // half-row mirror: ^ 7
+  } else if constexpr (M == 16) {
+    return (unsigned)__builtin_amdgcn_ds_swizzle(x, 0x401F);              // bitmask mode, xor 16
+  } else {
+    return (unsigned)__shfl_xor(x, M, kWave);
+  }
+}
+
+// One compare-exchange stage (k, j) of a descending bitonic sort on 32-bit
+// keys, EPT keys per thread (thread t owns elements t*EPT .. t*EPT+EPT-1).
+template <int EPT, int K, int J>
+__device__ __forceinline__ void stage32(unsigned (&x)[EPT], unsigned* lds, int tid) {
+  if constexpr (J < EPT) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if ((i ^ J) > i) {
+        const int e = tid * EPT + i;
+        const bool desc = (e & K) == 0;
+        const unsigned lo = x[i], hi = x[i ^ J];
+        const unsigned mx = lo > hi ? lo : hi, mn = lo > hi ? hi : lo;
+        x[i] = desc ? mx : mn;
+        x[i ^ J] = desc ? mn : mx;
+      }
+    }
+  } else if constexpr (J < EPT * kWave) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
+      const unsigned p = lane_xor<J / EPT>(x[i]);
+      const bool take_max = ((e & J) == 0) == ((e & K) == 0);
+      x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] > p ? p : x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) lds[tid * EPT + i] = x[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = tid * EPT + i;
+      const unsigned p = lds[e ^ J];
+      const bool take_max = ((e & J) == 0) == ((e & K) == 0);
+      x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] > p ? p : x[i]);
+    }
+    __syncthreads();
+  }
+}
+
+template <int EPT, int K, int J>
+__device__ __forceinline__ void merge_steps32(unsigned (&x)[EPT], unsigned* lds, int tid) {
+  stage32<EPT, K, J>(x, lds, tid);
+  if constexpr (J > 1) merge_steps32<EPT, K, J / 2>(x, lds, tid);
+}
+
+template <int EPT, int N, int K>
+__device__ __forceinline__ void bitonic32(unsigned (&x)[EPT], unsigned* lds, int tid) {
+  merge_steps32<EPT, K, K / 2>(x, lds, tid);
+  if constexpr (K < N) bitonic32<EPT, N, K * 2>(x, lds, tid);
+}
+
+// Descending bitonic sort of 64-bit keys (fallback when a row's score range
+// does not fit a 32-bit key); same layout, runtime stage loop.
+template <int EPT>
+__device__ void bitonic64(unsigned long long (&x)[EPT], int n_sort, unsigned long long* lds) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= n_sort; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < EPT) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const int pi = i ^ j;
+          if (pi > i) {
+            const int e = tid * EPT + i;
+            const bool desc = (e & k) == 0;
+            const unsigned long long lo = x[i], hi = x[pi];
+            if (desc ? (lo < hi) : (lo > hi)) {
+              x[i] = hi;
+              x[pi] = lo;
+            }
+          }
+        }
+      } else if (j < EPT * kWave) {
+        const int lm = j / EPT;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const int e = tid * EPT + i;
+          const unsigned long long p = shfl_xor_u64(x[i], lm);
+          const bool take_max = ((e & j) == 0) == ((e & k) == 0);
+          x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] < p ? x[i] : p);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) lds[tid * EPT + i] = x[i];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const int e = tid * EPT + i;
+          const unsigned long long p = lds[e ^ j];
+          const bool take_max = ((e & j) == 0) == ((e & k) == 0);
+          x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] < p ? x[i] : p);
+        }
+        __syncthreads();
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int block_max_int(int v, int* scratch) {
+  for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o, kWave));
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[wid] = v;
+  __syncthreads();
+  int r = scratch[0];
+  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) r = max(r, scratch[w]);
+  __syncthreads();
+  return r;
+}
+
+// grid: B*M rows; block N / EPT threads; dynamic LDS: N * 8 bytes.
+// Sorts the row's candidates (N = 2^LOG2N >= candidates) in rank order.
+template <int LOG2N>
+__global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
+  constexpr int N = 1 << LOG2N;
+  constexpr int EPT = N > 2 * kMaxThreads ? N / kMaxThreads : 2;
+  extern __shared__ unsigned long long lds64[];
+  unsigned* lds32 = reinterpret_cast<unsigned*>(lds64);
   __shared__ unsigned mask[kMaxBlocks / 32];
-  __shared__ int iscratch[kSelWaves];
-  __shared__ float fscratch[kSelWaves];
+  __shared__ int iscratch[kMaxWaves];
+  __shared__ float fscratch[kMaxWaves];
+  __shared__ int smax_s;
 
   const int row = blockIdx.x;
   const int b = row / a.M;
@@ -96,49 +244,76 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
 
   // valid blocks, reserved ranges and the candidate range [c0, c1)
   const int nbv = a.seq_len ? min(nKb, (a.seq_len[b] + a.blk - 1) / a.blk) : nKb;
-  int e, sink_end, loc0, loc1, diag, c0, c1;
+  int sink_end, loc0, loc1, diag, c0, c1;
   if (!a.prefill) {
-    e = nbv;
-    sink_end = min(a.n_sink, e);
-    loc0 = max(0, e - a.n_local);
-    loc1 = e;
+    sink_end = min(a.n_sink, nbv);
+    loc0 = max(0, nbv - a.n_local);
+    loc1 = nbv;
     diag = -1;
     c0 = a.n_sink;
-    c1 = e - a.n_local;
+    c1 = nbv - a.n_local;
   } else {
     const int qa = a.q_blk0 + i;
-    e = min(qa, nbv);
     sink_end = min(min(a.n_sink, qa + 1), nKb);
     loc0 = max(0, qa - a.n_local);
     loc1 = min(qa, nKb);
     diag = qa < nKb ? qa : -1;
     c0 = a.n_sink;
-    c1 = min(e, qa - a.n_local);
+    c1 = min(min(qa, nbv), qa - a.n_local);
   }
   const int n_cand = max(0, c1 - c0);
-  int n_pad = 1;
-  while (n_pad < n_cand) n_pad <<= 1;
 
   const int32_t* srow = a.scores + (size_t)row * nKb;
-  for (int t = tid; t < n_pad; t += kSelThreads)
-    keys[t] = t < n_cand ? make_key(srow[c0 + t], c0 + t) : 0ull;
-  for (int t = tid; t < kMaxBlocks / 32; t += kSelThreads) mask[t] = 0u;
-  __syncthreads();
+  int sc[EPT];
+  int lmax = INT32_MIN, lmin = INT32_MAX;
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int r = tid * EPT + e;
+    sc[e] = r < n_cand ? srow[c0 + r] : 0;
+    if (r < n_cand) {
+      lmax = max(lmax, sc[e]);
+      lmin = min(lmin, sc[e]);
+    }
+  }
+  for (int t = tid; t < kMaxBlocks / 32; t += blockDim.x) mask[t] = 0u;
+  const int smax = block_max_int(lmax, iscratch);
+  const int smin = -block_max_int(lmin == INT32_MIN ? INT32_MAX : -lmin, iscratch);
+  // 32-bit keys when (score - smin) and the inverted index fit side by side
+  int ib = 1;
+  while ((1 << ib) <= nKb) ++ib;
+  const bool key32 = n_cand > 0 && ib < 32 &&
+                     (unsigned long long)((long long)smax - (long long)smin) < (1ull << (32 - ib));
 
-  // bitonic sort, descending
-  for (int kk = 2; kk <= n_pad; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-      for (int t = tid; t < (n_pad >> 1); t += kSelThreads) {
-        const int lo = 2 * jj * (t / jj) + (t % jj);
-        const int hi = lo + jj;
-        const unsigned long long x = keys[lo], y = keys[hi];
-        const bool desc = (lo & kk) == 0;
-        if (desc ? (x < y) : (x > y)) {
-          keys[lo] = y;
-          keys[hi] = x;
-        }
-      }
-      __syncthreads();
+  int rscore[EPT];  // scores in rank order
+  int rindex[EPT];  // block indices in rank order
+  if (key32) {
+    const unsigned imask = (1u << ib) - 1u;
+    unsigned x[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      x[e] = r < n_cand ? (((unsigned)(sc[e] - smin) << ib) | (imask - (unsigned)(c0 + r))) : 0u;
+    }
+    bitonic32<EPT, N, 2>(x, lds32, tid);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      rscore[e] = (int)(x[e] >> ib) + smin;
+      rindex[e] = (int)(imask - (x[e] & imask));
+    }
+  } else {
+    unsigned long long x[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      x[e] = r < n_cand ? make_key(sc[e], c0 + r) : 0ull;
+    }
+    int n_sort = 2;
+    while (n_sort < n_cand) n_sort <<= 1;
+    bitonic64<EPT>(x, n_sort, lds64);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      rscore[e] = key_score(x[e]);
+      rindex[e] = key_index(x[e]);
     }
   }
 
@@ -149,21 +324,23 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
   } else if (n_cand == 0) {
     k_sel = 0;
   } else {
-    // each thread owns a contiguous run of ranks
-    const int per = (n_cand + kSelThreads - 1) / kSelThreads;
-    const int r0 = tid * per;
-    const int r1 = min(n_cand, r0 + per);
-    const int smax = key_score(keys[0]);
+    float mass[EPT];
     float local = 0.f;
-    for (int t = r0; t < r1; ++t) local += expf(a.beta * (float)(key_score(keys[t]) - smax));
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      mass[e] = r < n_cand ? expf(a.beta * (float)(rscore[e] - smax)) : 0.f;
+      local += mass[e];
+    }
     float Z;
-    const float off = block_excl_scan_float(local, fscratch, &Z);
-    // count ranks whose normalised cumulative mass is still below p
-    float run = off;
+    float run = block_excl_scan_float(local, fscratch, &Z);
+    // ranks whose normalised cumulative mass is still below p
     int below = 0;
-    for (int t = r0; t < r1; ++t) {
-      run += expf(a.beta * (float)(key_score(keys[t]) - smax));
-      below += (run / Z < a.p) ? 1 : 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      run += mass[e];
+      below += (r < n_cand && run / Z < a.p) ? 1 : 0;
     }
     int n_below;
     block_excl_scan_int(below, iscratch, &n_below);
@@ -171,13 +348,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     k_sel = min(n_cand, max(a.k_min, min(kp, a.k_max)));
   }
 
-  // mark reserved and kept blocks
-  for (int t = tid; t < k_sel; t += kSelThreads) {
-    const int j = key_index(keys[t]);
-    atomicOr(&mask[j >> 5], 1u << (j & 31));
+  // mark kept and reserved blocks
+#pragma unroll
+  for (int e = 0; e < EPT; ++e) {
+    const int r = tid * EPT + e;
+    if (r < k_sel) atomicOr(&mask[rindex[e] >> 5], 1u << (rindex[e] & 31));
   }
-  for (int j = tid; j < sink_end; j += kSelThreads) atomicOr(&mask[j >> 5], 1u << (j & 31));
-  for (int j = loc0 + tid; j < loc1; j += kSelThreads) atomicOr(&mask[j >> 5], 1u << (j & 31));
+  for (int j = tid; j < sink_end; j += blockDim.x) atomicOr(&mask[j >> 5], 1u << (j & 31));
+  for (int j = loc0 + tid; j < loc1; j += blockDim.x) atomicOr(&mask[j >> 5], 1u << (j & 31));
   if (tid == 0 && diag >= 0) atomicOr(&mask[diag >> 5], 1u << (diag & 31));
   __syncthreads();
 
@@ -185,7 +363,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
   const int nwords = (nKb + 31) >> 5;
   int32_t* out = a.idx + (size_t)row * a.cap;
   int written = 0;
-  for (int w0 = 0; w0 < nwords; w0 += kSelThreads) {
+  for (int w0 = 0; w0 < nwords; w0 += blockDim.x) {
     const int wdx = w0 + tid;
     const unsigned m = wdx < nwords ? mask[wdx] : 0u;
     int tot;
@@ -199,7 +377,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
     }
     written += tot;
   }
-  for (int t = written + tid; t < a.cap; t += kSelThreads) out[t] = -1;
+  for (int t = written + tid; t < a.cap; t += blockDim.x) out[t] = -1;
   if (tid == 0) a.count[row] = min(written, a.cap);
 }
 
@@ -208,11 +386,22 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs a) {
 int select_max_blocks() { return kMaxBlocks; }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  // LDS for keys sized by the widest candidate range any row can have
-  int n_pad = 1;
-  while (n_pad < a.nKb) n_pad <<= 1;
-  const size_t lds = (size_t)n_pad * sizeof(unsigned long long);
-  select_kernel<<<a.B * a.M, kSelThreads, lds, s>>>(a);
+  // N: the smallest power of two >= every row's candidate count (>= 128)
+  int log2n = 7;
+  while ((1 << log2n) < a.nKb) ++log2n;
+  const int n = 1 << log2n;
+  const int ept = n > 2 * kMaxThreads ? n / kMaxThreads : 2;
+  const int threads = n / ept;
+  const size_t lds = (size_t)n * sizeof(unsigned long long);
+  const int grid = a.B * a.M;
+  switch (log2n) {
+    case 7: select_kernel<7><<<grid, threads, lds, s>>>(a); break;
+    case 8: select_kernel<8><<<grid, threads, lds, s>>>(a); break;
+    case 9: select_kernel<9><<<grid, threads, lds, s>>>(a); break;
+    case 10: select_kernel<10><<<grid, threads, lds, s>>>(a); break;
+    case 11: select_kernel<11><<<grid, threads, lds, s>>>(a); break;
+    default: select_kernel<12><<<grid, threads, lds, s>>>(a); break;
+  }
   return hipGetLastError();
 }
 
