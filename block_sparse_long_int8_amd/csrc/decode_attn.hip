@@ -12,10 +12,12 @@
 //   * all items' tiles are laid end to end and split evenly over a persistent
 //     grid of waves, so load balance does not depend on how budgets vary per
 //     sequence (dual top-p gives 21..185 blocks per sequence);
-//   * a wave that crosses an item boundary writes one partial (unnormalised o,
-//     running max m, running sum l) per item it touched, into slot item + wave;
-//     the merge kernel finds the partials of item i at slots i + w for
-//     w = first_tile(i)/share .. last_tile(i)/share.
+//   * a wave writes one partial (unnormalised o, running max m, running sum l)
+//     per item it touched, into slot item + wave; a second kernel merges the
+//     partials of item i (slots i + w for w = first_tile(i)/share ..
+//     last_tile(i)/share) by log-sum-exp.  (Merging inside the main kernel
+//     would need a device-scope release per wave, which on this chip writes
+//     back and invalidates the whole L2 of the XCD: far slower than a launch.)
 //
 // bf16 tile (d = 128, up to 16 query heads per KV head, GQA sharing: K/V are
 // read once per KV head for all its query heads):
@@ -30,8 +32,10 @@
 //     d = 8m + jj.  No LDS round trip.
 //   - P^T needs no data movement: the C layout of S^T already puts each
 //     lane's 8 token probabilities where the B operand wants them.
-//   - the next tile's 16 x 16-byte loads are issued before the current tile's
-//     math (two register buffers).
+//   - each wave walks its tile range in one flat loop with two tiles in
+//     flight (register ring), prefetching across item boundaries; tile
+//     descriptors (item, first token, valid count) are computed 64 at a time,
+//     one per lane, so no tile waits on a dependent index load.
 // fp32 tile (d in {64, 128}): plain VALU version of the same online softmax.
 #include "spa_internal.h"
 
@@ -46,12 +50,14 @@ constexpr int kTile = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr size_t kHeader = 256;
+constexpr int kQCache = 2;  // items whose Q a wave keeps in LDS
+constexpr int kOcc = 2;     // bf16 workgroups (4 waves each) resident per CU
 
 struct WsLayout {
   int* hdr;         // [0] total tiles, [1] share, [2] workers
-  int* item_start;  // [n_items + 1]
-  float* part_ml;   // [slots][G][2]
-  float* part_o;    // [slots][G][d]
+  int* item_start;  // [n_items + 1] first tile of each item (copy of the plan)
+  float* part_ml;  // [slots][G][2]
+  float* part_o;   // [slots][G][d]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -71,8 +77,8 @@ __host__ __device__ inline WsLayout ws_layout(void* ws, int n_items, int workers
 
 __host__ __device__ inline size_t ws_total(int n_items, int workers, int G, int d) {
   const size_t slots = (size_t)n_items + workers;
-  return kHeader + align256((size_t)(n_items + 1) * sizeof(int)) +
-         align256(slots * G * 2 * sizeof(float)) + align256(slots * G * d * sizeof(float));
+  return kHeader + align256((size_t)(n_items + 1) * sizeof(int)) + align256(slots * G * 2 * sizeof(float)) +
+         align256(slots * G * d * sizeof(float));
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -176,6 +182,33 @@ __device__ __forceinline__ int find_item(const int* item_start, int n_items, int
   return lo;
 }
 
+// ------------------------------------------------------------- merging ----
+// Items without any token (no selected block, empty window): out = 0, lse = -inf.
+// Called by workgroup 0 after the plan; every thread of it must call.
+__device__ void write_empty_items(const DecodeArgs& a, const int* item_start, int n_items, int G, int d,
+                                  int* flag) {
+  if (threadIdx.x == 0) *flag = 0;
+  __syncthreads();
+  for (int it = threadIdx.x; it < n_items; it += blockDim.x)
+    if (item_start[it + 1] == item_start[it]) *flag = 1;
+  __syncthreads();
+  if (*flag == 0) return;
+  const int per_item = G * d;
+  for (long e = threadIdx.x; e < (long)n_items * per_item; e += blockDim.x) {
+    const int it = (int)(e / per_item);
+    if (item_start[it + 1] != item_start[it]) continue;
+    const int r = (int)(e - (long)it * per_item);
+    const int h = r / d, c = r - h * d;
+    const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
+    const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + c;
+    if (a.out_bf16)
+      ((uint16_t*)a.out)[orow] = 0;
+    else
+      ((float*)a.out)[orow] = 0.f;
+    if (a.lse && c == 0) a.lse[(size_t)b * a.Hq + g * G + h] = -INFINITY;
+  }
+}
+
 // ------------------------------------------------------------ bf16 path ----
 constexpr int D = 128;
 
@@ -192,12 +225,12 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, const
     const int tau = min(16 * mt + m, nvalid - 1);
     const uint16_t* row = kb + (size_t)(tok0 + tau) * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = *reinterpret_cast<const uint4*>(row + 8 * (4 * j + g4));
+    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = load_nt16(row + 8 * (4 * j + g4));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nvalid - 1);
-    t.v[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(tok0 + tau) * D + 8 * m);
+    t.v[i] = load_nt16(vb + (size_t)(tok0 + tau) * D + 8 * m);
   }
 }
 
@@ -271,10 +304,58 @@ __device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg,
   }
 }
 
-__global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, int n_items,
-                                                               int workers) {
+// Per-lane descriptors of 64 consecutive tiles of a wave's range: lane l
+// describes tile base + l (its item, first token and valid-token count), so
+// the tile loop only reads lanes (no dependent global loads per tile).
+struct TileWindow {
+  int base;
+  int item, tok0, nvalid;
+};
+
+__device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item_start, int n_items,
+                                            int total, int tpb, int base, TileWindow& win) {
+  const int tt = base + (threadIdx.x & (kWave - 1));
+  win.base = base;
+  win.item = 0;
+  win.tok0 = 0;
+  win.nvalid = 0;
+  if (tt < total) {
+    const int it = find_item(item_start, n_items, tt);
+    const int u = tt - item_start[it];
+    const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
+    const int L = a.seq_len[b];
+    win.item = it;
+    if (a.head_mode && a.head_mode[g]) {
+      const int ns = min(a.sink_tok, L);
+      const int wstart = max(ns, L - a.window_tok);
+      const int nst = (ns + kTile - 1) / kTile;
+      if (u < nst) {
+        win.tok0 = u * kTile;
+        win.nvalid = min(kTile, ns - win.tok0);
+      } else {
+        win.tok0 = wstart + (u - nst) * kTile;
+        win.nvalid = min(kTile, L - win.tok0);
+      }
+    } else {
+      const int slot = u / tpb;
+      const int sub = u - slot * tpb;
+      const int j = a.idx[(size_t)b * a.cap + slot];
+      win.tok0 = j * a.blk + sub * kTile;
+      win.nvalid = min(min(kTile, a.blk - sub * kTile), L - win.tok0);
+    }
+  }
+}
+
+// grid: workers / 4 workgroups of 4 waves.  Each wave walks its tile range
+// with two register buffers: the loads of tile t + 1 are issued before the
+// math of tile t, across item boundaries; the Q operands of the wave's items
+// are staged in LDS up front.  Two workgroups per CU (two waves per SIMD, <= 256 registers
+// each) let one wave's math overlap the other's loads.
+template <int OCC>
+__global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a, int n_items, int workers) {
   __shared__ int item_start[kMaxItems + 1];
   __shared__ int scratch[kWPB];
+  __shared__ uint4 qcache[kWPB][kQCache][4][kWave];  // Q operands of a wave's first items
   const int total = build_plan(a, n_items, item_start, scratch);
   const int share = (total + workers - 1) / workers;
   const int G = a.Hq / a.Hkv;
@@ -286,13 +367,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, 
       ws.hdr[1] = share;
       ws.hdr[2] = workers;
     }
+    write_empty_items(a, item_start, n_items, G, D, &scratch[0]);
   }
   if (share == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = blockIdx.x * kWPB + threadIdx.x / kWave;
-  int t = w * share;
-  const int t_end = min(total, t + share);
-  if (t >= t_end) return;
+  const int t0 = w * share;
+  const int t1 = min(total, t0 + share);
+  if (t0 >= t1) return;
 
   const int tpb = (a.blk + kTile - 1) / kTile;
   const int m = lane & 15, g4 = lane >> 4;
@@ -301,55 +383,68 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, 
   const uint16_t* kc = (const uint16_t*)a.k;
   const uint16_t* vc = (const uint16_t*)a.v;
 
-  int item = find_item(item_start, n_items, t);
-  while (t < t_end) {
-    while (item_start[item + 1] <= t) ++item;
-    const int seg_end = min(t_end, item_start[item + 1]);
-    const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
-    const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * D;
-    const uint16_t* kb = kc + kv_off;
-    const uint16_t* vb = vc + kv_off;
+  TileWindow win;
+  fill_window(a, item_start, n_items, total, tpb, t0, win);
+  const int wv = threadIdx.x / kWave;
+  const int it_first = find_item(item_start, n_items, t0);
 
-    bf16x8 qreg[4];
+  // descriptor of tile t (uniform): item, first token, valid tokens
+  auto desc = [&](int t, int& it, int& tok0, int& nv) {
+    if (t - win.base >= kWave) fill_window(a, item_start, n_items, total, tpb, t, win);
+    const int off = t - win.base;
+    it = __builtin_amdgcn_readlane(win.item, off);
+    tok0 = __builtin_amdgcn_readlane(win.tok0, off);
+    nv = __builtin_amdgcn_readlane(win.nvalid, off);
+  };
+  auto load_q = [&](int it, uint4* qr) {
+    const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       uint4 qv = {0u, 0u, 0u, 0u};
       if (m < G) qv = *reinterpret_cast<const uint4*>(q + ((size_t)b * a.Hq + g * G + m) * D + 8 * (4 * j + g4));
-      qreg[j] = as_bf16x8(qv);
+      qr[j] = qv;
     }
-    HeadState st;
+  };
+  // Q of the wave's first kQCache items goes to LDS once, so an item switch
+  // inside the tile loop reads LDS instead of waiting on a global load
+  // (global loads complete in order, so that wait would drain the prefetch)
+  {
+    const int it_last = find_item(item_start, n_items, t1 - 1);
+    for (int c = 0; c < kQCache && it_first + c <= it_last; ++c) {
+      uint4 qr[4];
+      load_q(it_first + c, qr);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qcache[wv][c][j][lane] = qr[j];
+    }
+  }
+  bf16x8 qcur[4];
+  auto set_q = [&](int it) {
+    const int c = it - it_first;
+    uint4 qr[4];
+    if (c < kQCache) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) qr[j] = qcache[wv][c][j][lane];
+    } else {
+      load_q(it, qr);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qcur[j] = as_bf16x8(qr[j]);
+  };
+  // a tile with no valid token still loads a valid row (and is fully masked)
+  auto load_kv = [&](int it, int tok0, int nv, TileRegs& tr) {
+    const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
+    const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * D;
+    load_tile(kc + kv_off, vc + kv_off, nv > 0 ? tok0 : 0, nv > 0 ? nv : 1, lane, tr);
+  };
+
+  HeadState st;
+  auto reset = [&]() {
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) st.o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int u = t - item_start[item];
-    const int u_end = seg_end - item_start[item];
-    const int L = a.seq_len[b];
-    const bool local = a.head_mode && a.head_mode[g];
-    const int cnt = local ? 0 : a.count[b];
-    IdxWindow win;
-    if (!local) load_window(a, b, u / tpb, cnt, win);
-    TileRegs A, Bt;
-    int tokA, nvA, tokB = 0, nvB = 0;
-    tile_info(a, b, g, u, tpb, L, local, cnt, win, tokA, nvA);
-    if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
-    while (u < u_end) {
-      if (u + 1 < u_end) {
-        tile_info(a, b, g, u + 1, tpb, L, local, cnt, win, tokB, nvB);
-        if (nvB > 0) load_tile(kb, vb, tokB, nvB, lane, Bt);
-      }
-      if (nvA > 0) tile_math(A, qreg, nvA, scale_log2, lane, st);
-      if (++u >= u_end) break;
-      if (u + 1 < u_end) {
-        tile_info(a, b, g, u + 1, tpb, L, local, cnt, win, tokA, nvA);
-        if (nvA > 0) load_tile(kb, vb, tokA, nvA, lane, A);
-      }
-      if (nvB > 0) tile_math(Bt, qreg, nvB, scale_log2, lane, st);
-      ++u;
-    }
-
-    // partial for (item, wave)
+  };
+  auto flush = [&](int item) {
     const size_t slot = (size_t)item + w;
     float lt = st.l;
     lt += shfl_xor_f(lt, 16);
@@ -368,8 +463,25 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(DecodeArgs a, 
         ws.part_ml[(slot * G + m) * 2 + 1] = lt;
       }
     }
-    t = seg_end;
+  };
+
+  // one tile in flight per wave; latency is hidden by the other waves of the
+  // CU (OCC waves per SIMD), so no wave waits on a prefetch of its own
+  TileRegs A;
+  int cur = -1;
+  for (int t = t0; t < t1; ++t) {
+    int it, tok0, nv;
+    desc(t, it, tok0, nv);
+    load_kv(it, tok0, nv, A);
+    if (it != cur) {
+      if (cur >= 0) flush(cur);
+      cur = it;
+      reset();
+      set_q(cur);
+    }
+    tile_math(A, qcur, nv, scale_log2, lane, st);
   }
+  flush(cur);
 }
 
 // ------------------------------------------------------------ fp32 path ----
@@ -396,6 +508,7 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
       ws.hdr[1] = share;
       ws.hdr[2] = workers;
     }
+    write_empty_items(a, item_start, n_items, G, DD, &scratch[0]);
   }
   if (share == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
@@ -513,76 +626,93 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 }
 
 // ----------------------------------------------------------------- merge ----
-// One workgroup per item: pass 1 finds each head's maximum over the item's
-// partials, pass 2 sums the rescaled partials; a thread owns one float4 of one
-// head, and the per-slot loads of pass 2 are independent so they overlap.
-constexpr int kMergeThreads = 256;
+// One workgroup of 1024 threads per item.  Thread (sub, pair) owns one float4
+// of one head (pair) and every nsub-th partial (sub): pass 1 finds the head
+// maxima, pass 2 rescales and sums its partials, and the nsub sums are added
+// in LDS.  Items with no tile were written by workgroup 0 of the main kernel.
+constexpr int kMergeThreads = 1024;
 
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
   __shared__ float red[kMergeThreads];
+  __shared__ float4 acc_s[kMergeThreads];
   __shared__ float Ms[16];
   const int G = a.Hq / a.Hkv;
   const int d = a.d;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
   const int item = blockIdx.x;
-  const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
-  const int tid = threadIdx.x;
   const int share = ws.hdr[1];
   const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
-  const bool any = s1 > s0 && share > 0;
-  const int w0 = any ? s0 / share : 0;
-  const int nsl = any ? (s1 - 1) / share - w0 + 1 : 0;
-  // pass 1: per-head maximum of the partial maxima
-  {
-    const int h = tid % G;
-    float mx = -INFINITY;
-    if (tid < (kMergeThreads / G) * G)
-      for (int sl = tid / G; sl < nsl; sl += kMergeThreads / G)
-        mx = fmaxf(mx, ws.part_ml[(((size_t)item + w0 + sl) * G + h) * 2]);
-    red[tid] = mx;
-    __syncthreads();
-    if (tid < G) {
-      float m = -INFINITY;
-      for (int t = tid; t < (kMergeThreads / G) * G; t += G) m = fmaxf(m, red[t]);
-      Ms[tid] = m;
-    }
-    __syncthreads();
-  }
+  if (s1 <= s0 || share <= 0) return;
+  const int w0 = s0 / share;
+  const int nparts = (s1 - 1) / share - w0 + 1;
   const int per_head = d / 4;
-  for (int t = tid; t < G * per_head; t += kMergeThreads) {
-    const int h = t / per_head;
-    const int c4 = t - h * per_head;
-    const float M = Ms[h];
-    float4 o = {0.f, 0.f, 0.f, 0.f};
-    float lse_v = -INFINITY;
-    if (M != -INFINITY) {
-      float L = 0.f;
-      float4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int sl = 0; sl < nsl; ++sl) {
-        const size_t slot = (size_t)item + w0 + sl;
-        const float2 ml = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
-        const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
-        const float f = exp2f(ml.x - M);
-        L += f * ml.y;
-        acc.x += f * ow.x;
-        acc.y += f * ow.y;
-        acc.z += f * ow.z;
-        acc.w += f * ow.w;
-      }
-      const float inv = 1.f / L;
-      o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-      lse_v = (M + log2f(L)) * kLn2;
-    }
-    const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
-    if (a.out_bf16) {
-      uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-      *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
-    } else {
-      *reinterpret_cast<float4*>((float*)a.out + orow) = o;
-    }
-    if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
+  const int pairs = G * per_head;            // <= 1024 (G * d <= 4096)
+  const int nsub = kMergeThreads / pairs;
+  const int tid = threadIdx.x;
+  const int sub = tid / pairs;
+  const int pair = tid - sub * pairs;
+  const bool active = sub < nsub;
+  const int h = pair / per_head;
+  const int c4 = pair - h * per_head;
+  // pass 1: head maxima
+  float mx = -INFINITY;
+  if (active)
+    for (int p = sub; p < nparts; p += nsub) mx = fmaxf(mx, ws.part_ml[(((size_t)item + w0 + p) * G + h) * 2]);
+  red[tid] = mx;
+  __syncthreads();
+  if (tid < G) {
+    float m = -INFINITY;
+    for (int t = tid * per_head; t < nsub * pairs; t += pairs)
+      for (int c = 0; c < per_head; ++c) m = fmaxf(m, red[t + c]);
+    Ms[tid] = m;
   }
+  __syncthreads();
+  // pass 2: rescaled sums of this thread's partials
+  float L = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  const float M = active ? Ms[h] : 0.f;
+  if (active && M != -INFINITY) {
+#pragma unroll 4
+    for (int p = sub; p < nparts; p += nsub) {
+      const size_t slot = (size_t)item + w0 + p;
+      const float2 ml = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
+      const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
+      const float f = exp2f(ml.x - M);
+      L += f * ml.y;
+      acc.x += f * ow.x;
+      acc.y += f * ow.y;
+      acc.z += f * ow.z;
+      acc.w += f * ow.w;
+    }
+  }
+  red[tid] = L;
+  acc_s[tid] = acc;
+  __syncthreads();
+  if (sub != 0) return;
+  const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
+  for (int u = 1; u < nsub; ++u) {
+    L += red[u * pairs + pair];
+    const float4 o2 = acc_s[u * pairs + pair];
+    acc.x += o2.x;
+    acc.y += o2.y;
+    acc.z += o2.z;
+    acc.w += o2.w;
+  }
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = -INFINITY;
+  if (M != -INFINITY && L > 0.f) {
+    const float inv = 1.f / L;
+    o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    lse_v = (M + log2f(L)) * kLn2;
+  }
+  const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
+  if (a.out_bf16) {
+    const uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
+  } else {
+    *reinterpret_cast<float4*>((float*)a.out + orow) = o;
+  }
+  if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
 }
 
 int g_workers = 0;
@@ -596,8 +726,8 @@ int decode_workers() {
       int v = 0;
       if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
     }
-    // two 4-wave workgroups per CU: eight 32-token tiles in flight per CU
-    g_workers = cus * 2 * kWPB;
+    // kOcc 4-wave workgroups per CU, one tile in flight per wave
+    g_workers = cus * kOcc * kWPB;
   }
   return g_workers;
 }
@@ -611,13 +741,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int workers = decode_workers();
   const int blocks = workers / kWPB;
   if (a.io_bf16) {
-    decode_bf16_kernel<<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+    decode_bf16_kernel<kOcc><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
   } else if (a.d == 64) {
     decode_f32_kernel<64><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
   } else {
     decode_f32_kernel<128><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
   }
-  hipError_t e = hipGetLastError();
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_merge_kernel<<<n_items, kMergeThreads, 0, s>>>(a, n_items, workers);
   return hipGetLastError();
