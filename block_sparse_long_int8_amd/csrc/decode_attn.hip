@@ -234,6 +234,36 @@ __device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, const
   }
 }
 
+// Same operand layout through raw buffer loads on the (b, g) slab.  An offset
+// past num_records returns zeros without touching memory, so a tile can be
+// "loaded" as a placeholder at no cost: every loop iteration then issues the
+// same number of loads, which keeps the compiler's in-order wait counts exact.
+constexpr int kBufOOB = 0x7FFFFFF0;
+constexpr int kBufNT = 2;  // cache policy: non-temporal
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kBufNT);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int tok0,
+                                              int nvalid, bool real, int lane, TileRegs& t) {
+  const int m = lane & 15, g4 = lane >> 4;
+  const int nv = real ? nvalid : 1;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int tau = min(16 * mt + m, nv - 1);
+    const int row = real ? (tok0 + tau) * (D * 2) : kBufOOB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = buf_ld16(rk, row + (real ? 16 * (4 * j + g4) : 0));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nv - 1);
+    t.v[i] = buf_ld16(rv, real ? (tok0 + tau) * (D * 2) + 16 * m : kBufOOB);
+  }
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
 __device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
@@ -346,16 +376,17 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item
   }
 }
 
-// grid: workers / 4 workgroups of 4 waves.  Each wave walks its tile range
-// with two register buffers: the loads of tile t + 1 are issued before the
-// math of tile t, across item boundaries; the Q operands of the wave's items
-// are staged in LDS up front.  Two workgroups per CU (two waves per SIMD, <= 256 registers
+// grid: workers / 4 workgroups of 4 waves (kOcc per CU).  Each wave walks its
+// tile range with two register buffers: the loads of tile t + 1 are issued
+// before the math of tile t, across item boundaries; the Q operands of the
+// wave's items are staged in LDS up front.  Two workgroups per CU (two waves per SIMD, <= 256 registers
 // each) let one wave's math overlap the other's loads.
 template <int OCC>
 __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a, int n_items, int workers) {
   __shared__ int item_start[kMaxItems + 1];
   __shared__ int scratch[kWPB];
   __shared__ uint4 qcache[kWPB][kQCache][4][kWave];  // Q operands of a wave's first items
+  __shared__ int4 tdesc[kWPB][kWave];                 // descriptors of 64 consecutive tiles
   const int total = build_plan(a, n_items, item_start, scratch);
   const int share = (total + workers - 1) / workers;
   const int G = a.Hq / a.Hkv;
@@ -383,18 +414,26 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   const uint16_t* kc = (const uint16_t*)a.k;
   const uint16_t* vc = (const uint16_t*)a.v;
 
-  TileWindow win;
-  fill_window(a, item_start, n_items, total, tpb, t0, win);
   const int wv = threadIdx.x / kWave;
   const int it_first = find_item(item_start, n_items, t0);
-
-  // descriptor of tile t (uniform): item, first token, valid tokens
+  // Tile descriptors sit in LDS: reading one is an LDS access, so it never
+  // waits behind the K/V loads in flight (global loads complete in order).
+  int win_base = t0;
+  auto refill = [&](int base) {
+    TileWindow win;
+    fill_window(a, item_start, n_items, total, tpb, base, win);
+    wave_sync();
+    tdesc[wv][lane] = int4{win.item, win.tok0, win.nvalid, 0};
+    wave_sync();
+    win_base = base;
+  };
+  refill(t0);
   auto desc = [&](int t, int& it, int& tok0, int& nv) {
-    if (t - win.base >= kWave) fill_window(a, item_start, n_items, total, tpb, t, win);
-    const int off = t - win.base;
-    it = __builtin_amdgcn_readlane(win.item, off);
-    tok0 = __builtin_amdgcn_readlane(win.tok0, off);
-    nv = __builtin_amdgcn_readlane(win.nvalid, off);
+    if (t - win_base >= kWave) refill(t);
+    const int4 dd = tdesc[wv][t - win_base];
+    it = __builtin_amdgcn_readfirstlane(dd.x);
+    tok0 = __builtin_amdgcn_readfirstlane(dd.y);
+    nv = __builtin_amdgcn_readfirstlane(dd.z);
   };
   auto load_q = [&](int it, uint4* qr) {
     const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
@@ -430,11 +469,21 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
 #pragma unroll
     for (int j = 0; j < 4; ++j) qcur[j] = as_bf16x8(qr[j]);
   };
-  // a tile with no valid token still loads a valid row (and is fully masked)
-  auto load_kv = [&](int it, int tok0, int nv, TileRegs& tr) {
-    const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
-    const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * D;
-    load_tile(kc + kv_off, vc + kv_off, nv > 0 ? tok0 : 0, nv > 0 ? nv : 1, lane, tr);
+  // (b, g) slab of the K and V caches as buffer resources
+  const unsigned slab_bytes = (unsigned)((size_t)a.Tcap * D * 2);
+  auto rsrc = [&](const uint16_t* base, int it) {
+    it = __builtin_amdgcn_readfirstlane(it);  // the item is wave-uniform
+    // item = b * Hkv + g is also the index of its [Tcap, d] slab
+    const uintptr_t p = (uintptr_t)(base + (size_t)it * a.Tcap * D);
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)p);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+    void* up = (void*)(((uintptr_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(up, 0, slab_bytes, 0x00020000);
+  };
+  // placeholder loads (real == false) fetch nothing; a tile with no valid token
+  // is one of them and its math is fully masked
+  auto load_kv = [&](int it, int tok0, int nv, bool real, TileRegs& tr) {
+    load_tile_buf(rsrc(kc, it), rsrc(vc, it), tok0, nv, real && nv > 0, lane, tr);
   };
 
   HeadState st;
@@ -465,21 +514,43 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
     }
   };
 
-  // one tile in flight per wave; latency is hidden by the other waves of the
-  // CU (OCC waves per SIMD), so no wave waits on a prefetch of its own
-  TileRegs A;
-  int cur = -1;
-  for (int t = t0; t < t1; ++t) {
-    int it, tok0, nv;
-    desc(t, it, tok0, nv);
-    load_kv(it, tok0, nv, A);
-    if (it != cur) {
-      if (cur >= 0) flush(cur);
-      cur = it;
+  // Two register buffers: tile t + 1 (or a placeholder after the last tile)
+  // is requested before the math of tile t.
+  TileRegs A, Bt;
+  int itA, tokA, nvA, itB = 0, tokB = 0, nvB = 0;
+  desc(t0, itA, tokA, nvA);
+  set_q(itA);
+  load_kv(itA, tokA, nvA, true, A);
+  int cur = itA;
+  reset();
+  int t = t0;
+  while (true) {
+    const bool moreB = t + 1 < t1;
+    if (moreB) desc(t + 1, itB, tokB, nvB);
+    load_kv(moreB ? itB : itA, tokB, nvB, moreB, Bt);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the math
+    tile_math(A, qcur, nvA, scale_log2, lane, st);
+    if (!moreB) break;
+    ++t;
+    if (itB != cur) {
+      flush(cur);
+      cur = itB;
       reset();
       set_q(cur);
     }
-    tile_math(A, qcur, nv, scale_log2, lane, st);
+    const bool moreA = t + 1 < t1;
+    if (moreA) desc(t + 1, itA, tokA, nvA);
+    load_kv(moreA ? itA : itB, tokA, nvA, moreA, A);
+    __builtin_amdgcn_sched_barrier(0);
+    tile_math(Bt, qcur, nvB, scale_log2, lane, st);
+    if (!moreA) break;
+    ++t;
+    if (itA != cur) {
+      flush(cur);
+      cur = itA;
+      reset();
+      set_q(cur);
+    }
   }
   flush(cur);
 }
