@@ -1,8 +1,8 @@
 """Throughput of one sparse decode step at 128K context on one MI355X.
 
 A step is the whole decode hot path for one attention layer over one batch:
-int8 indexer scores -> dual top-p selection -> split sparse flash-decode and
-its log-sum-exp merge.  Workload: B = 16 sequences of 131072 tokens, 64 query
+int8 indexer scores and dual top-p selection (one fused launch) -> split
+sparse flash-decode and its log-sum-exp merge.  Workload: B = 16 sequences of 131072 tokens, 64 query
 heads over 8 KV heads, d = 128, 64-token blocks, top-p 0.9 over softmax(s/8)
 with K_min 16 / K_max 512 plus 1 sink and 4 local blocks (seeded synthetic
 inputs, planted relevant blocks per sequence drawn from 1..200).
@@ -136,15 +136,12 @@ def main():
         c = i % args.copies
         if ev is not None:
             ev[0].record()
-        step.score(qI, kI, w, seq_len)
+        step.score_select(qI, kI, w, seq_len)
         if ev is not None:
             ev[1].record()
-        step.select(seq_len)
-        if ev is not None:
-            ev[2].record()
         step.attend(q, ks[c], vs[c], seq_len)
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
 
     for i in range(args.warmup):
         run(i)
@@ -160,7 +157,7 @@ def main():
         del src, dst
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -173,9 +170,8 @@ def main():
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    score_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    select_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    attn_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    select_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
 
     counts = step.count.cpu().numpy()
@@ -210,8 +206,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "spa_sparse_decode_attn (decode_bf16_kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": ab, "avg_launch_ms": attn_avg_s * 1e3},
-        "stages_ms": {"score": float(np.mean(score_ms)), "select_topp": float(np.mean(select_ms)),
-                      "attention": float(np.mean(attn_ms))},
+        "stages_ms": {"score_select_topp": float(np.mean(select_ms)), "attention": float(np.mean(attn_ms))},
         "selected_blocks": {"mean": float(counts.mean()), "min": int(counts.min()), "max": int(counts.max())},
         "step_algorithmic_bytes": ab + index_bytes(cfg),
     }

@@ -7,7 +7,8 @@ paths wired as sequences of calls.
 from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORTED, SPA_ERR_WORKSPACE, SPA_F32,
                    SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, LIB_PATH,
                    SpaError, declared_symbols, lib, spa_block_sparse_prefill, spa_index_score,
-                   spa_index_score_workspace_size, spa_segment_permute, spa_select_topk, spa_select_topp,
+                   spa_index_score_workspace_size, spa_score_select_decode, spa_segment_permute, spa_select_topk,
+                   spa_select_topp,
                    spa_sparse_decode_attn, spa_sparse_decode_attn_workspace_size)
 from .pipeline import DecodeSpec, DecodeStep, PrefillSpec, PrefillStep
 

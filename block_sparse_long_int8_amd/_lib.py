@@ -45,6 +45,8 @@ _SIGS = {
     "spa_index_score_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "spa_select_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "spa_select_topp": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "spa_score_select_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _i, _vp,
+                                     _vp, _vp, _i, _vp]),
     "spa_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                     _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_sparse_decode_attn_workspace_size": (_sz, [_i, _i, _i, _i]),
@@ -191,6 +193,26 @@ def spa_select_topp(scores, blk, n_sink, n_local, beta, p, k_min, k_max, cap, se
     st = lib().spa_select_topp(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
                                float(beta), float(p), k_min, k_max, _ptr(idx), _ptr(count), cap, None, 0, _stream())
     _check("spa_select_topp", st)
+    return idx, count
+
+
+def spa_score_select_decode(qI, kI, w, seq_len, blk, n_sink, n_local, cap, mode="topp", k=0, beta=1.0, p=0.9,
+                            k_min=0, k_max=0, scores_out=None, idx=None, count=None):
+    """Fused decode scoring + selection; returns (idx, count)."""
+    _dev(qI, "qI", torch.int8)
+    _dev(kI, "kI", torch.int8)
+    _dev(w, "w", torch.int8)
+    _dev(seq_len, "seq_len", torch.int32)
+    B, H, r = qI.shape
+    nKb = kI.shape[1]
+    if idx is None:
+        idx = torch.empty((B, cap), dtype=torch.int32, device=qI.device)
+    if count is None:
+        count = torch.empty((B,), dtype=torch.int32, device=qI.device)
+    st = lib().spa_score_select_decode(_ptr(qI), _ptr(kI), _ptr(w), B, H, r, nKb, _ptr(seq_len), blk, n_sink,
+                                       n_local, 0 if mode == "topk" else 1, k, float(beta), float(p), k_min, k_max,
+                                       _ptr(scores_out), _ptr(idx), _ptr(count), cap, _stream())
+    _check("spa_score_select_decode", st)
     return idx, count
 
 

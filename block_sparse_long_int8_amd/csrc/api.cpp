@@ -118,7 +118,9 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
 static spa_status select_common(const char* fn, const int32_t* scores, int B, int M, int nKb,
                                 int q_blk0, const int32_t* seq_len, int blk, int n_sink, int n_local,
                                 int prefill, int mode, int k, float beta, float p, int k_min,
-                                int k_max, int32_t* idx, int32_t* count, int cap, void* stream) {
+                                int k_max, int32_t* idx, int32_t* count, int cap, void* stream,
+                                const int8_t* qI = nullptr, const int8_t* kI = nullptr,
+                                const int8_t* w = nullptr, int H = 0, int32_t* scores_out = nullptr) {
   REQUIRE(prefill == 0 || prefill == 1, SPA_ERR_INVALID_ARG, "prefill must be 0 or 1 (got %d)", prefill);
   REQUIRE(B >= 0 && M >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG, "negative size");
   REQUIRE(blk >= 1 && n_sink >= 0 && n_local >= 0, SPA_ERR_INVALID_ARG, "need blk >= 1, n_sink >= 0, n_local >= 0");
@@ -135,9 +137,11 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
   REQUIRE(cap >= 1 && (long)cap >= need_cap, SPA_ERR_INVALID_ARG, "cap %d < reserved + budget = %ld", cap, need_cap);
   REQUIRE(nKb <= spa::select_max_blocks(), SPA_ERR_UNSUPPORTED, "nKb %d exceeds %d", nKb, spa::select_max_blocks());
   if (B == 0 || M == 0) return ok();
-  REQUIRE(scores && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE((scores || (qI && kI && w)) && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");
   if (!prefill) REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode selection needs seq_len");
-  REQUIRE(aligned16(scores) && aligned16(idx) && aligned16(count), SPA_ERR_INVALID_ARG, "scores, idx and count must be 16-byte aligned");
+  REQUIRE(aligned16(scores) && aligned16(idx) && aligned16(count) && aligned16(qI) && aligned16(kI) &&
+              aligned16(scores_out),
+          SPA_ERR_INVALID_ARG, "scores, idx, count, qI, kI and scores_out must be 16-byte aligned");
   spa::SelectArgs a;
   a.scores = scores;
   a.B = B;
@@ -158,7 +162,27 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
   a.idx = idx;
   a.count = count;
   a.cap = cap;
+  a.qI = qI;
+  a.kI = kI;
+  a.w = w;
+  a.H = H;
+  a.scores_out = scores_out;
   return from_hip(spa::launch_select(a, (hipStream_t)stream), fn);
+}
+
+spa_status spa_score_select_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
+                                   int r, int nKb, const int32_t* seq_len, int blk, int n_sink,
+                                   int n_local, int mode, int k, float beta, float p, int k_min,
+                                   int k_max, int32_t* scores_out, int32_t* idx, int32_t* count,
+                                   int cap, void* stream) {
+  const char* fn = "spa_score_select_decode";
+  REQUIRE(mode == 0 || mode == 1, SPA_ERR_INVALID_ARG, "mode must be 0 (top-k) or 1 (top-p), got %d", mode);
+  REQUIRE(H_idx >= 1 && r >= 4 && r % 4 == 0, SPA_ERR_INVALID_ARG, "need H_idx >= 1 and r a positive multiple of 4 (H_idx=%d r=%d)", H_idx, r);
+  REQUIRE(r == 16 && H_idx <= 64 && (H_idx & (H_idx - 1)) == 0, SPA_ERR_UNSUPPORTED,
+          "fused scoring supports r == 16 and a power-of-two H_idx <= 64 (got r=%d, H_idx=%d)", r, H_idx);
+  if (B > 0) REQUIRE(qI && kI && w, SPA_ERR_INVALID_ARG, "null indexer pointer");
+  return select_common(fn, nullptr, B, 1, nKb, 0, seq_len, blk, n_sink, n_local, 0, mode, k, beta, p, k_min,
+                       k_max, idx, count, cap, stream, qI, kI, w, H_idx, scores_out);
 }
 
 spa_status spa_select_topk(const int32_t* scores, int B, int M, int nKb, int q_blk0,

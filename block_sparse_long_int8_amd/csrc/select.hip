@@ -225,7 +225,7 @@ __device__ __forceinline__ int block_max_int(int v, int* scratch) {
 
 // grid: B*M rows; block N / EPT threads; dynamic LDS: N * 8 bytes.
 // Sorts the row's candidates (N = 2^LOG2N >= candidates) in rank order.
-template <int LOG2N>
+template <int LOG2N, bool SCORED>
 __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   constexpr int N = 1 << LOG2N;
   constexpr int EPT = N > 2 * kMaxThreads ? N / kMaxThreads : 2;
@@ -263,13 +263,65 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   }
   const int n_cand = max(0, c1 - c0);
 
-  const int32_t* srow = a.scores + (size_t)row * nKb;
   int sc[EPT];
   int lmax = INT32_MIN, lmin = INT32_MAX;
+  if constexpr (SCORED) {
+    // one lane per (block, head): coalesced 16-byte loads, four v_dot4, a
+    // shuffle sum over the block's H lanes; scores land in LDS
+    __shared__ int4 q4[64];
+    __shared__ int w_s[64];
+    __shared__ int s_lds[kMaxBlocks];
+    for (int t = tid; t < a.H; t += blockDim.x) {
+      q4[t] = reinterpret_cast<const int4*>(a.qI)[(size_t)b * a.H + t];
+      w_s[t] = a.w[(size_t)b * a.H + t];
+    }
+    __syncthreads();
+    int log2H = 0;
+    while ((1 << log2H) < a.H) ++log2H;
+    const int H = a.H;
+    const int4* krow = reinterpret_cast<const int4*>(a.kI + (size_t)b * nKb * H * 16);
+    const int npairs = nbv << log2H;
+    constexpr int U = 8;  // loads in flight per thread
+    for (int p0 = 0; p0 < npairs; p0 += U * (int)blockDim.x) {
+      int4 kv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * blockDim.x + tid;
+        kv[u] = p < npairs ? krow[p] : int4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + u * blockDim.x + tid;
+        const int h = p & (H - 1);
+        const int4 qv = q4[h];
+        int dot = __builtin_amdgcn_sdot4(qv.x, kv[u].x, 0, false);
+        dot = __builtin_amdgcn_sdot4(qv.y, kv[u].y, dot, false);
+        dot = __builtin_amdgcn_sdot4(qv.z, kv[u].z, dot, false);
+        dot = __builtin_amdgcn_sdot4(qv.w, kv[u].w, dot, false);
+        int v = p < npairs ? w_s[h] * max(dot, 0) : 0;
+        for (int o = 1; o < H; o <<= 1) v += __shfl_xor(v, o, kWave);
+        if (p < npairs && h == 0) s_lds[p >> log2H] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      sc[e] = r < n_cand ? s_lds[c0 + r] : 0;
+    }
+    if (a.scores_out)
+      for (int j = tid; j < nKb; j += blockDim.x) a.scores_out[(size_t)b * nKb + j] = j < nbv ? s_lds[j] : INT32_MIN;
+  } else {
+    const int32_t* srow = a.scores + (size_t)row * nKb;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const int r = tid * EPT + e;
+      sc[e] = r < n_cand ? srow[c0 + r] : 0;
+    }
+  }
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     const int r = tid * EPT + e;
-    sc[e] = r < n_cand ? srow[c0 + r] : 0;
     if (r < n_cand) {
       lmax = max(lmax, sc[e]);
       lmin = min(lmin, sc[e]);
@@ -394,14 +446,28 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const int threads = n / ept;
   const size_t lds = (size_t)n * sizeof(unsigned long long);
   const int grid = a.B * a.M;
+  const bool scored = a.scores == nullptr;
+#define SPA_SEL_CASE(L)                                                   \
+  case L:                                                                 \
+    if (scored)                                                           \
+      select_kernel<L, true><<<grid, threads, lds, s>>>(a);               \
+    else                                                                  \
+      select_kernel<L, false><<<grid, threads, lds, s>>>(a);              \
+    break;
   switch (log2n) {
-    case 7: select_kernel<7><<<grid, threads, lds, s>>>(a); break;
-    case 8: select_kernel<8><<<grid, threads, lds, s>>>(a); break;
-    case 9: select_kernel<9><<<grid, threads, lds, s>>>(a); break;
-    case 10: select_kernel<10><<<grid, threads, lds, s>>>(a); break;
-    case 11: select_kernel<11><<<grid, threads, lds, s>>>(a); break;
-    default: select_kernel<12><<<grid, threads, lds, s>>>(a); break;
+    SPA_SEL_CASE(7)
+    SPA_SEL_CASE(8)
+    SPA_SEL_CASE(9)
+    SPA_SEL_CASE(10)
+    SPA_SEL_CASE(11)
+    default:
+      if (scored)
+        select_kernel<12, true><<<grid, threads, lds, s>>>(a);
+      else
+        select_kernel<12, false><<<grid, threads, lds, s>>>(a);
+      break;
   }
+#undef SPA_SEL_CASE
   return hipGetLastError();
 }
 

@@ -65,6 +65,12 @@ struct SelectArgs {
   int32_t* idx;
   int32_t* count;
   int cap;
+  // fused decode scoring (scores == nullptr): int8 indexer inputs, r == 16
+  const int8_t* qI;
+  const int8_t* kI;
+  const int8_t* w;
+  int H;
+  int32_t* scores_out;  // optional copy of every block's score
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 int select_max_blocks();

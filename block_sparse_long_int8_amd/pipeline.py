@@ -1,6 +1,8 @@
 """The two hot paths as sequences of library calls, with buffers preallocated.
 
-DecodeStep:  spa_index_score -> spa_select_topk | spa_select_topp -> spa_sparse_decode_attn
+DecodeStep:  spa_score_select_decode (scoring and selection in one launch; or
+             spa_index_score -> spa_select_topk | spa_select_topp)
+             -> spa_sparse_decode_attn
 PrefillStep: spa_segment_permute (Q, K, V, per-token indexer vectors)
              -> spa_index_score (per-token, pooled) -> spa_select_topk (prefill rows)
              -> spa_block_sparse_prefill -> spa_segment_permute (inverse, on O)
@@ -51,10 +53,15 @@ class DecodeSpec:
 
 
 class DecodeStep:
-    """One decode step of one attention layer; owns its scratch and output buffers."""
+    """One decode step of one attention layer; owns its scratch and output buffers.
 
-    def __init__(self, spec: DecodeSpec, device="cuda"):
+    ``fused=True`` scores and selects in one launch (spa_score_select_decode);
+    ``fused=False`` runs spa_index_score then spa_select_*.
+    """
+
+    def __init__(self, spec: DecodeSpec, device="cuda", fused: bool = True):
         self.spec = s = spec
+        self.fused = fused
         dev = torch.device(device)
         self.scores = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
         self.idx = torch.empty((s.B, s.cap), dtype=torch.int32, device=dev)
@@ -76,6 +83,14 @@ class DecodeStep:
         return L.spa_select_topp(self.scores, s.blk, s.n_sink, s.n_local, s.beta, s.p, s.k_min, s.k_max, s.cap,
                                  seq_len=seq_len, idx=self.idx, count=self.count)
 
+    def score_select(self, qI, kI, w, seq_len, keep_scores: bool = False):
+        """Fused scoring + selection (scores are written only if keep_scores)."""
+        s = self.spec
+        return L.spa_score_select_decode(qI, kI, w, seq_len, s.blk, s.n_sink, s.n_local, s.cap, mode=s.select,
+                                         k=s.k, beta=s.beta, p=s.p, k_min=s.k_min, k_max=s.k_max,
+                                         scores_out=self.scores if keep_scores else None, idx=self.idx,
+                                         count=self.count)
+
     def attend(self, q, k_cache, v_cache, seq_len, head_mode=None):
         s = self.spec
         return L.spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, self.idx, self.count, s.blk,
@@ -83,9 +98,12 @@ class DecodeStep:
                                         local_window_tok=s.local_window_tok, out=self.out, lse=self.lse,
                                         ws=self.ws)
 
-    def __call__(self, q, k_cache, v_cache, qI, kI, w, seq_len, head_mode=None):
-        self.score(qI, kI, w, seq_len)
-        self.select(seq_len)
+    def __call__(self, q, k_cache, v_cache, qI, kI, w, seq_len, head_mode=None, keep_scores: bool = False):
+        if self.fused:
+            self.score_select(qI, kI, w, seq_len, keep_scores=keep_scores)
+        else:
+            self.score(qI, kI, w, seq_len)
+            self.select(seq_len)
         return self.attend(q, k_cache, v_cache, seq_len, head_mode)
 
 

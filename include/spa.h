@@ -133,6 +133,26 @@ spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_b
                            int cap, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * spa_score_select_decode -- spa_index_score (decode) and spa_select_topk /
+ * spa_select_topp fused into one launch.
+ *
+ * Same definitions as the two calls it replaces (SpotAttention page §1 for the
+ * score, RTPurbo page §3 and SpotAttention page §3 for the selection): each
+ * sequence's workgroup computes its blocks' scores from qI [B, H_idx, 16],
+ * kI [B, nKb, H_idx, 16] and w [B, H_idx] and selects from them directly, so
+ * the scores never travel through HBM.  mode 0 = top-k (uses k), 1 = top-p
+ * (uses beta, p, k_min, k_max).  scores_out [B, nKb] may be NULL; when given it
+ * receives every block's score exactly as spa_index_score writes it.
+ * Outputs and errors as spa_select_topk / spa_select_topp (decode rows).
+ * Supported: r == 16, H_idx a power of two <= 64, nKb <= 4096.
+ */
+spa_status spa_score_select_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
+                                   int r, int nKb, const int32_t* seq_len, int blk, int n_sink,
+                                   int n_local, int mode, int k, float beta, float p, int k_min,
+                                   int k_max, int32_t* scores_out, int32_t* idx, int32_t* count,
+                                   int cap, void* stream);
+
+/*
  * spa_sparse_decode_attn -- exact softmax attention over the selected tokens.
  *
  * HGA page, "Atención Exacta de Token": a standard softmax over exactly the

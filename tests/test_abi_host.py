@@ -5,7 +5,13 @@ import ctypes
 
 import pytest
 
+import torch
+
 import block_sparse_long_int8_amd as S
+
+# These calls pass fake host addresses that must be rejected before any launch.
+# They are host-logic tests: never run them where a GPU could execute a launch.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(), reason="fake-pointer rejection tests are host-only")
 
 L = S.lib()
 N = None
@@ -113,3 +119,23 @@ def test_prefill_and_permute_rejections():
     assert p(_fake(), _fake(), 4, 100, 256, _fake(3), 64, 0, N) == S.SPA_ERR_INVALID_ARG   # overlap
     assert p(_fake(), _fake(2), 4, 100, 256, N, 64, 0, N) == S.SPA_ERR_INVALID_ARG
     assert p(N, N, 0, 100, 256, N, 64, 0, N) == S.SPA_OK
+
+
+def test_score_select_rejections():
+    f = L.spa_score_select_decode
+    base = [_fake(), _fake(2), _fake(3), 1, 8, 16, 100, _fake(4), 64, 1, 4, 1, 0, 0.125, 0.9, 16, 64, N, _fake(5),
+            _fake(6), 85, N]
+    b = list(base); b[11] = 3
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # mode
+    b = list(base); b[5] = 8
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # r must be 16
+    b = list(base); b[4] = 65
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # H_idx <= 64
+    b = list(base); b[20] = 68
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # cap < 1 + 4 + k_max
+    b = list(base); b[1] = N
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[7] = N
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # decode rows need seq_len
+    b = list(base); b[3] = 0
+    assert f(*b) == S.SPA_OK                                   # empty batch

@@ -46,12 +46,13 @@ def _spec(cfg):
                         local_window_tok=cfg.local_window_tok)
 
 
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
 @pytest.mark.parametrize("cfg", DECODE_CFGS, ids=[c.name for c in DECODE_CFGS])
-def test_decode_step_parity(cfg):
-    print(f"[decode parity] {cfg.name}", flush=True)
+def test_decode_step_parity(cfg, fused):
+    print(f"[decode parity] {cfg.name} fused={fused}", flush=True)
     inp, t = _decode_inputs(cfg)
-    step = S.DecodeStep(_spec(cfg))
-    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    step = S.DecodeStep(_spec(cfg), fused=fused)
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
     torch.cuda.synchronize()
     ref = O.decode_step(inp)
     # scores: bit-exact over every block (past-the-end blocks carry INT32_MIN)

@@ -35,7 +35,8 @@ def test_full_decode_parity(S, cfg):
                         local_window_tok=cfg.local_window_tok)
     step = S.DecodeStep(spec)
     q, k, v = dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype), dev(inp["v"], cfg.dtype)
-    step(q, k, v, dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), dev(inp["head_mode"]))
+    step(q, k, v, dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), dev(inp["head_mode"]),
+         keep_scores=True)
     torch.cuda.synchronize()
     print(f"[full decode parity] {cfg.name}: oracle", flush=True)
     ref = O.decode_step(inp)
@@ -56,6 +57,13 @@ def test_full_decode_parity(S, cfg):
     step.attend(q, k.clone(), v.clone(), dev(inp["seq_len"]), dev(inp["head_mode"]))
     torch.cuda.synchronize()
     assert torch.equal(out0, step.out)
+    # the separate score + select calls give the same scores and selection
+    sep = S.DecodeStep(spec, fused=False)
+    sep.score(dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]))
+    sep.select(dev(inp["seq_len"]))
+    torch.cuda.synchronize()
+    assert torch.equal(sep.scores, step.scores)
+    assert torch.equal(sep.idx, step.idx) and torch.equal(sep.count, step.count)
 
 
 def test_full_prefill_64k_parity(S):
