@@ -1,25 +1,35 @@
-"""Throughput of one sparse decode step at 128K context on one MI355X.
+"""Throughput of the block-sparse attention hot path on one MI355X.
 
-A step is the whole decode hot path for one attention layer over one batch:
-int8 indexer scores and dual top-p selection (one fused launch) -> split
-sparse flash-decode and its log-sum-exp merge.  Workload: B = 16 sequences of 131072 tokens, 64 query
-heads over 8 KV heads, d = 128, 64-token blocks, top-p 0.9 over softmax(s/8)
-with K_min 16 / K_max 512 plus 1 sink and 4 local blocks (seeded synthetic
-inputs, planted relevant blocks per sequence drawn from 1..200).
+Default workload: one sparse decode step at 128K context.  A step is the
+whole decode hot path of one attention layer over one batch: int8 indexer
+scores and dual top-p selection (one fused launch), then the split sparse
+flash-decode and its log-sum-exp merge.  B = 16 sequences of 131072 tokens,
+64 query heads over 8 KV heads, d = 128, 64-token blocks, top-p 0.9 over
+softmax(s/8) with K_min 16 / K_max 512 plus 1 sink and 4 local blocks
+(seeded synthetic inputs, planted relevant blocks per sequence drawn from
+1..200).  value = sequences decoded per second (tokens/s).
 
-Prints one JSON line.  value = sequences decoded per second (tokens/s) with
-all inputs resident in HBM.  The K/V cache is replicated in `--copies`
-buffers that consecutive steps rotate through, so a step cannot be served
-from the 256 MB Infinity Cache left warm by the previous one.
+``--workload`` selects another of the named workloads: the other decode
+shapes (tokens/s, same definition) or the 64K permuted block-sparse prefill
+(prompt tokens/s; a step is permute Q/K/V and the per-token indexer vectors,
+pool + score, select, sparse attention, inverse permute of O).
 
-roofline: the dominant op is the sparse attention (main kernel + merge);
-its algorithmic bytes (selected K/V rows, Q, O, lse, the block list) over
-its event-timed duration, against 8 TB/s.
-cpu_baseline: the CPU oracle (numpy fp64) on the same inputs, one full step.
+All inputs are resident in HBM before the timed region.  Every per-step input
+is replicated in ``--copies`` buffer sets that consecutive steps rotate
+through, so that the union of the bytes one rotation touches is at least
+1 GiB and a step cannot be served from the 256 MB Infinity Cache left warm by
+the previous one (0 = choose that count automatically).
+
+Prints one JSON line.  roofline: the dominant launch (decode: the sparse
+attention entry point, main kernel + merge, against 8 TB/s of HBM; prefill:
+the block-sparse attention kernel against the bf16 dense MFMA peak), timed
+with HIP events on the stream it runs on.  cpu_baseline: the CPU oracle on a
+bounded sample of the same inputs.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,8 +39,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-METRIC = "sparse-decode tokens/s at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
 HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+INT8_MFMA_PEAK_TOPS = 5000.0
+ROTATE_BYTES = 1 << 30          # bytes one rotation over the copies must touch
+COPY_MEM_LIMIT = 64 << 30       # device bytes all copies together may take
+
+DECODE_METRIC = "sparse-decode tokens/s at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
+WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "tiny_decode", "prefill_64k")
 
 
 def log(*a):
@@ -40,106 +56,172 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--copies", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default 50 decode, 20 prefill)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10 decode, 3 prefill)")
+    ap.add_argument("--workload", choices=WORKLOADS, default="decode_128k_topp")
+    ap.add_argument("--copies", type=int, default=0, help="input buffer sets to rotate through (0 = auto)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_128k_traffic.json"))
+    ap.add_argument("--traffic-json", default=None,
+                    help="counter-measured HBM traffic of the dominant launch (default profiles/<workload>_traffic.json)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size before the timed steps (counter calibration)")
-    return ap.parse_args()
+    a = ap.parse_args()
+    prefill = a.workload.startswith("prefill")
+    if a.steps is None:
+        a.steps = 20 if prefill else 50
+    if a.warmup is None:
+        a.warmup = 3 if prefill else 10
+    if a.traffic_json is None:
+        a.traffic_json = os.path.join(ROOT, "profiles", f"{a.workload}_traffic.json")
+    return a
 
 
-def attn_bytes(cfg, counts, seq_len) -> int:
+def config_of(name):
+    import gen
+    return {"decode_128k_topp": gen.DECODE_128K_TOPP, "decode_32k": gen.DECODE_32K,
+            "decode_64k_headsplit": gen.DECODE_64K_HEADSPLIT, "tiny_decode": gen.TINY_DECODE,
+            "prefill_64k": gen.PREFILL_64K}[name]
+
+
+def source_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_long_int8_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(path, sha):
+    """Counter-measured bytes per launch, if they were taken on the current kernel source."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tj = json.load(f)
+    return tj.get("traffic_bytes_per_launch") if tj.get("kernel_source_sha") == sha else None
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def dev(x, dt=None):
+    import numpy as np
+    import torch
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def calibration_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log(f"[bench] calibration copy of {mib} MiB done")
+
+
+def n_copies(args, touched, per_copy):
+    if args.copies > 0:
+        return args.copies
+    want = max(3, -(-ROTATE_BYTES // max(1, touched)))
+    return int(max(1, min(want, 4096, COPY_MEM_LIMIT // max(1, per_copy))))
+
+
+# ---------------------------------------------------------------- decode ----
+
+def decode_attn_bytes(cfg, idx, counts, seq_len, head_mode) -> int:
     """Algorithmic HBM bytes of one sparse attention launch.
 
-    Selected K and V rows (bf16) of every KV head, clipped to the sequence,
-    plus Q (bf16), O (fp32), lse (fp32), the block lists and counts (int32).
+    K and V rows of the tokens each KV group attends (selected blocks clipped
+    to the sequence for retrieval groups, sink tokens + window for local
+    groups), plus Q, O (fp32), lse (fp32), the block lists and counts.
     """
-    tok = 0
-    for b, c in enumerate(counts):
-        tok += int(c) * cfg.blk  # every selected block is a whole block in this workload
-    kv = tok * cfg.Hkv * cfg.d * 2 * 2
-    q = cfg.B * cfg.Hq * cfg.d * 2
+    el = 4 if cfg.dtype == "f32" else 2
+    row = cfg.d * el
+    kv = 0
+    for b in range(cfg.B):
+        L = int(seq_len[b])
+        sel_tok = sum(min(cfg.blk, L - int(j) * cfg.blk) for j in idx[b, :counts[b]])
+        loc_tok = min(L, cfg.local_sink_tok + cfg.local_window_tok) if cfg.local_window_tok else 0
+        for g in range(cfg.Hkv):
+            kv += 2 * row * (loc_tok if head_mode[g] else sel_tok)
+    q = cfg.B * cfg.Hq * cfg.d * el
     o = cfg.B * cfg.Hq * cfg.d * 4
     lse = cfg.B * cfg.Hq * 4
-    idx = int(sum(int(c) for c in counts)) * 4 + cfg.B * 4 * 2
-    return kv + q + o + lse + idx
+    lists = int(counts.sum()) * 4 + cfg.B * 4 * 2
+    return kv + q + o + lse + lists
 
 
-def index_bytes(cfg) -> int:
-    """Algorithmic bytes of scoring + selection: kI, qI, w, scores written and read."""
-    return cfg.B * (cfg.nb * cfg.H_idx * cfg.r + cfg.H_idx * (cfg.r + 1) + cfg.nb * 4 * 2)
+def decode_index_bytes(cfg, seq_len) -> int:
+    """Algorithmic bytes of scoring + selection: kI of the valid blocks, qI, w, block lists."""
+    nbv = sum(-(-int(L) // cfg.blk) for L in seq_len)
+    return nbv * cfg.H_idx * cfg.r + cfg.B * cfg.H_idx * (cfg.r + 1) + cfg.B * 4
 
 
-def cpu_baseline(inp, cfg):
-    """Time the CPU oracle on one full decode step (all sequences)."""
-    import numpy as np
+def decode_cpu_baseline(inp, cfg):
+    """The CPU oracle on one full decode step (all sequences), repeated to about 10 s."""
     from threadpoolctl import threadpool_info
 
     import oracle as O
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     t0 = time.perf_counter()
     O.decode_step(inp)
-    dt = time.perf_counter() - t0
     reps = 1
-    # repeat to roughly 10 s of CPU work, bounded
     while time.perf_counter() - t0 < 10.0 and reps < 20:
         O.decode_step(inp)
         reps += 1
     dt = (time.perf_counter() - t0) / reps
     return {"value": cfg.B / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full decode step of all {cfg.B} sequences (score, top-p, fp64 attention), "
+            "sample": f"full decode step of all {cfg.B} sequences (integer scores, selection, fp64 attention), "
                       f"mean of {reps} runs, {dt:.3f} s each"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
-              file=sys.stderr)
-        sys.exit(2)
+def bench_decode(args, cfg):
     import numpy as np
     import torch
 
     import block_sparse_long_int8_amd as S
     import gen
 
-    cfg = gen.DECODE_128K_TOPP
     t0 = time.time()
     inp = gen.make(cfg, seed=args.seed)
     log(f"[bench] generated {cfg.name} in {time.time() - t0:.1f} s")
-
     torch.cuda.set_device(0)
-
-    def dev(x, dt=None):
-        if dt == "bf16":
-            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-
-    q = dev(inp["q"], "bf16")
-    k0 = dev(inp["k"], "bf16")
-    v0 = dev(inp["v"], "bf16")
-    ks = [k0] + [k0.clone() for _ in range(args.copies - 1)]
-    vs = [v0] + [v0.clone() for _ in range(args.copies - 1)]
-    qI, kI, w, seq_len = dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"])
-    torch.cuda.synchronize()
-    log(f"[bench] inputs resident: {args.copies} copies of the {2 * k0.numel() * 2 / 2**30:.1f} GiB K/V cache")
-
+    dt = cfg.dtype
+    base = {"q": dev(inp["q"], dt), "k": dev(inp["k"], dt), "v": dev(inp["v"], dt), "qI": dev(inp["qI"]),
+            "kI": dev(inp["kI"]), "w": dev(inp["w"])}
+    seq_len, head_mode = dev(inp["seq_len"]), dev(inp["head_mode"])
     spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx,
-                        r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select="topp", beta=cfg.beta, p=cfg.p,
-                        k_min=cfg.k_min, k_max=cfg.k_max)
+                        r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta,
+                        p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
+                        local_window_tok=cfg.local_window_tok)
     step = S.DecodeStep(spec)
+    step(base["q"], base["k"], base["v"], base["qI"], base["kI"], base["w"], seq_len, head_mode)
+    torch.cuda.synchronize()
+    idx, counts = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    ab = decode_attn_bytes(cfg, idx, counts, inp["seq_len"], inp["head_mode"])
+    ib = decode_index_bytes(cfg, inp["seq_len"])
+    per_copy = sum(t.numel() * t.element_size() for t in base.values())
+    copies = n_copies(args, ab + ib, per_copy)
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(copies - 1)]
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {copies} copies of {per_copy / 2**30:.3f} GiB; "
+        f"{(ab + ib) / 1e6:.1f} MB touched per step")
 
     def run(i, ev=None):
-        c = i % args.copies
+        x = sets[i % copies]
         if ev is not None:
             ev[0].record()
-        step.score_select(qI, kI, w, seq_len)
+        step.score_select(x["qI"], x["kI"], x["w"], seq_len)
         if ev is not None:
             ev[1].record()
-        step.attend(q, ks[c], vs[c], seq_len)
+        step.attend(x["q"], x["k"], x["v"], seq_len, head_mode)
         if ev is not None:
             ev[2].record()
 
@@ -148,18 +230,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        calibration_copy(args.copy_calibration_mib)
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
@@ -170,24 +244,164 @@ def main():
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    select_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
 
-    counts = step.count.cpu().numpy()
-    ab = attn_bytes(cfg, counts, inp["seq_len"])
-    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
-    achieved = ab / attn_avg_s / 1e9
-    traffic = None
-    if os.path.exists(args.traffic_json):
-        with open(args.traffic_json) as f:
-            tj = json.load(f)
-        if tj.get("kernel_source_sha") == _kernel_sha():
-            traffic = tj.get("traffic_bytes_per_launch")
-
+    attn_s = float(np.mean(attn_ms)) * 1e-3
+    achieved = ab / attn_s / 1e9
+    traffic = load_traffic(args.traffic_json, source_sha("decode_attn.hip"))
+    select_name = "score_select_topp" if cfg.select == "topp" else "score_select_topk"
     res = {
-        "metric": METRIC,
+        "metric": DECODE_METRIC if cfg is config_of("decode_128k_topp")
+        else f"sparse-decode tokens/s ({cfg.name}, 1 GPU); achieved HBM GB/s vs peak",
         "value": cfg.B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
+                   "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "select": cfg.select, "k": cfg.k, "p": cfg.p,
+                   "beta": cfg.beta, "k_min": cfg.k_min, "k_max": cfg.k_max, "n_sink": cfg.n_sink,
+                   "n_local": cfg.n_local, "retrieval_groups": int(sum(1 for m in inp["head_mode"] if m == 0)),
+                   "local_sink_tok": cfg.local_sink_tok, "local_window_tok": cfg.local_window_tok,
+                   "input_copies_rotated": copies, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "spa_sparse_decode_attn (decode main kernel + decode_merge_kernel)",
+                     "algorithmic_bytes_per_launch": ab, "avg_launch_ms": attn_s * 1e3},
+        "stages_ms": {select_name: float(np.mean(sel_ms)), "attention": float(np.mean(attn_ms))},
+        "step_ms_p10_p50_p90": [pct(step_ms, 10), pct(step_ms, 50), pct(step_ms, 90)],
+        "selected_blocks": {"mean": float(counts.mean()), "min": int(counts.min()), "max": int(counts.max())},
+        "step_algorithmic_bytes": ab + ib,
+        "step_hbm_gbs": (ab + ib) / (ms_step * 1e-3) / 1e9,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        res["cpu_baseline"] = decode_cpu_baseline(inp, cfg)
+    return res
+
+
+# --------------------------------------------------------------- prefill ----
+
+def prefill_pairs(perm, idx, counts, blk) -> int:
+    """Attended (query, key) pairs of one head: selected slots with an original position <= the query's."""
+    import numpy as np
+    pos = np.asarray(perm, dtype=np.int64)
+    total = 0
+    for i in range(len(counts)):
+        sel = idx[i, :counts[i]]
+        kp = np.sort(np.concatenate([pos[j * blk:(j + 1) * blk] for j in sel]))
+        total += int(np.searchsorted(kp, pos[i * blk:(i + 1) * blk], side="right").sum())
+    return total
+
+
+def prefill_cpu_baseline(inp, cfg):
+    """The CPU oracle on the full front end plus the attention of sampled query blocks, scaled to T."""
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    nq = cfg.nb
+    sample = list(range(nq // 32, nq, nq // 16))  # 16 evenly spaced query blocks
+    t0 = time.perf_counter()
+    front = O.prefill_front(inp)
+    t_front = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.prefill_step(inp, front=front, blocks=[])
+    t_fixed = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.prefill_step(inp, front=front, blocks=sample)
+    t_sample = time.perf_counter() - t0
+    t_full = t_front + t_fixed + (t_sample - t_fixed) * nq / len(sample)
+    return {"value": cfg.B * cfg.T / t_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"oracle front end (permute, pool, score, select) on all {nq} query blocks ({t_front:.2f} s), "
+                      f"Q/K/V permutation ({t_fixed:.2f} s), and fp64 attention of {len(sample)} evenly spaced "
+                      f"query blocks ({t_sample - t_fixed:.2f} s) scaled to all {nq}"}
+
+
+def bench_prefill(args, cfg):
+    import numpy as np
+    import torch
+
+    import block_sparse_long_int8_amd as S
+    import gen
+
+    t0 = time.time()
+    inp = gen.make(cfg, seed=args.seed)
+    log(f"[bench] generated {cfg.name} in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(0)
+    x = {"q": dev(inp["q"], "bf16"), "k": dev(inp["k"], "bf16"), "v": dev(inp["v"], "bf16"),
+         "qI": dev(inp["qI_tok"]), "kI": dev(inp["kI_tok"]), "w": dev(inp["w"]), "perm": dev(inp["perm"])}
+    spec = S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg)
+    step = S.PrefillStep(spec)
+    step(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], x["perm"])
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident: {sum(t.numel() * t.element_size() for t in x.values()) / 2**30:.2f} GiB")
+
+    stages = ("permute_qkv", "permute_index", "pool_score", "select", "attention", "unpermute_o")
+
+    def run(ev=None):
+        def mark(j):
+            if ev is not None:
+                ev[j].record()
+        mark(0)
+        step.set_perm(x["perm"])
+        step.permute_inputs(x["q"], x["k"], x["v"], x["perm"])
+        mark(1)
+        step.permute_index(x["qI"], x["kI"], x["perm"])
+        mark(2)
+        step.score(x["w"])
+        mark(3)
+        step.select()
+        mark(4)
+        step.attend()
+        mark(5)
+        step.unpermute(x["perm"])
+        mark(6)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    if args.copy_calibration_mib:
+        calibration_copy(args.copy_calibration_mib)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        run(evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / args.steps
+    st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
+    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events")
+
+    idx, counts = step.idx[0].cpu().numpy(), step.count[0].cpu().numpy()
+    pairs = prefill_pairs(inp["perm"], idx, counts, cfg.blk)
+    flop = 4.0 * cfg.d * cfg.Hq * pairs * cfg.B
+    attn_s = st_ms["attention"] * 1e-3
+    achieved = flop / attn_s / 1e12
+    nq = cfg.nb
+    score_ops = 2.0 * cfg.r * cfg.H_idx * (nq * (nq - 1) // 2) * cfg.B
+    score_s = st_ms["pool_score"] * 1e-3
+    el_q, el_kv, el_o = cfg.Hq * cfg.d * 2, cfg.Hkv * cfg.d * 2, cfg.Hq * cfg.d * 4
+    perm_bytes = cfg.B * cfg.T * (el_q + 2 * el_kv) * 2
+    unperm_bytes = cfg.B * cfg.T * el_o * 2
+    traffic = load_traffic(args.traffic_json, source_sha("prefill_attn.hip"))
+    res = {
+        "metric": f"block-sparse prefill tokens/s ({cfg.name}, 1 GPU); attention TFLOP/s vs bf16 MFMA peak",
+        "value": cfg.B * cfg.T / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -199,29 +413,37 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
-                   "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "select": "top-p", "p": cfg.p, "beta": cfg.beta,
-                   "k_min": cfg.k_min, "k_max": cfg.k_max, "n_sink": cfg.n_sink, "n_local": cfg.n_local,
-                   "kv_copies_rotated": args.copies, "seed": args.seed},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "spa_sparse_decode_attn (decode_bf16_kernel + decode_merge_kernel)",
-                     "algorithmic_bytes_per_launch": ab, "avg_launch_ms": attn_avg_s * 1e3},
-        "stages_ms": {"score_select_topp": float(np.mean(select_ms)), "attention": float(np.mean(attn_ms))},
-        "selected_blocks": {"mean": float(counts.mean()), "min": int(counts.min()), "max": int(counts.max())},
-        "step_algorithmic_bytes": ab + index_bytes(cfg),
+                   "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "k": cfg.k, "n_sink": cfg.n_sink,
+                   "seg": cfg.seg, "causal": True, "seed": args.seed},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+                     "kernel": "spa_block_sparse_prefill (prefill attention kernel)",
+                     "algorithmic_flop_per_launch": flop, "attended_pairs_per_head": pairs,
+                     "avg_launch_ms": attn_s * 1e3},
+        "stages_ms": st_ms,
+        "scoring": {"int8_ops": score_ops, "tops": score_ops / score_s / 1e12,
+                    "frac_of_int8_mfma_peak": score_ops / score_s / 1e12 / INT8_MFMA_PEAK_TOPS,
+                    "note": "pool + score launch: two per-token pooling passes and the block-pair scoring"},
+        "permute": {"bytes": perm_bytes, "gbs": perm_bytes / (st_ms["permute_qkv"] * 1e-3) / 1e9,
+                    "unpermute_bytes": unperm_bytes,
+                    "unpermute_gbs": unperm_bytes / (st_ms["unpermute_o"] * 1e-3) / 1e9},
+        "selected_blocks": {"mean": float(counts.mean()), "max": int(counts.max())},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        res["cpu_baseline"] = cpu_baseline(inp, cfg)
+        res["cpu_baseline"] = prefill_cpu_baseline(inp, cfg)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+    cfg = config_of(args.workload)
+    res = bench_prefill(args, cfg) if args.workload.startswith("prefill") else bench_decode(args, cfg)
     print(json.dumps(res), flush=True)
-
-
-def _kernel_sha() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "block_sparse_long_int8_amd", "csrc", "decode_attn.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 if __name__ == "__main__":

@@ -5,17 +5,33 @@
 // segments, with causality enforced on the original positions (§2).  HGA
 // page: the softmax is exact over the selected tokens.
 //
-// One workgroup = one (sequence, 16 query slots of a 64-slot block, 4 query
-// heads of one KV head); one wave = one query head x 16 query slots.  For
-// each selected key block the wave walks two 32-key tiles:
-//   S^T[32 keys, 16 queries] = K . Q^T   (2 x 4 MFMA 16x16x32 bf16)
-//   O^T[128, 16 queries]    += V^T . P^T (8 MFMA 16x16x32 bf16)
-// with the same operand scheme as the decode kernel: K rows feed the A operand
-// directly, V rows are transposed in registers, and S^T's accumulator layout
-// is already the P^T operand layout.  Keys are masked with
-// k_pos <= q_pos (original positions) and t < T.  One register buffer each
-// for K and V: the next tile's K loads start once QK^T has consumed K, its V
-// loads once PV has consumed V, so memory and MFMA work overlap.
+// One workgroup = one (sequence, KV head, query block of 64 slots) and up to
+// four query heads of that KV head: eight waves, wave w owns query head
+// 4*quad + (w & 3) and query slots 32*(w >> 2) .. +31.  The four heads share
+// every key block of the list, so each 64-key block is staged once per
+// workgroup into LDS (direct global->LDS 16-byte loads, 16-byte chunks
+// XOR-swizzled by row so that the MFMA operand reads are free of bank
+// conflicts) and read by all eight waves.  K, V and key positions are
+// double-buffered: tile u+1 streams in while tile u is computed.
+//
+// Per 64-key tile a wave computes, with v_mfma_f32_32x32x16_bf16:
+//   S^T[64 keys, 32 queries] = K . Q^T      (2 x 8 MFMA)
+//   O^T[128, 32 queries]    += V^T . P^T    (4 x 4 MFMA)
+// K rows are the A operand as stored; V^T fragments come from the LDS
+// transpose read (ds_read_b64_tr_b16), whose key order matches the order in
+// which S^T's accumulator registers hold the keys, so P^T is packed straight
+// from S^T.  Two waves share each SIMD, so one wave's softmax (VALU) runs
+// while the other's products (MFMA) do.
+//
+// The running maximum is rescaled lazily: O and the normaliser keep the old
+// reference until a tile's maximum exceeds it by more than 2^8 in the exp2
+// domain, so the O rescale (64 multiplies per lane) runs only on the rare
+// tiles that raise the maximum that much.  The result is the same softmax;
+// only the reference point of the partial sums differs.
+//
+// Keys are masked with k_pos <= q_pos (original positions) and t < T; the
+// masks are skipped for tiles whose largest key position is below the
+// block's smallest query position (every block of an earlier segment).
 #include "spa_internal.h"
 
 namespace spa {
@@ -24,230 +40,268 @@ namespace {
 
 constexpr int D = 128;
 constexpr int BLK = 64;
-constexpr int NT = 1;         // query n-tiles (of 16) per wave: 16 query slots
-constexpr int QW = NT * 16;   // query slots per wave
-constexpr int NSUB = BLK / QW;  // query sub-blocks per 64-slot block
-constexpr int kWaves = 4;     // 4 query heads of one KV head
-constexpr int kTile = 32;
+constexpr int kWaves = 8;
+constexpr int ROWB = D * 2;          // bytes of one K/V row
+constexpr int TILEB = BLK * ROWB;    // bytes of one 64-key K or V tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-// K tile as A operands: lane (row m, group g4) holds 16 bytes of token m per k-step.
-__device__ __forceinline__ void load_k(const uint16_t* __restrict__ kb, int tok0, int nvalid, int lane,
-                                       uint4* kr) {
-  const int m = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int tau = min(16 * mt + m, nvalid - 1);
-    const uint16_t* row = kb + (size_t)(tok0 + tau) * D;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) kr[mt * 4 + j] = *reinterpret_cast<const uint4*>(row + 8 * (4 * j + g4));
-  }
-}
-
-// V tile: the 16 lanes of group g4 read token 16*(i/4) + 4*g4 + i%4 whole.
-__device__ __forceinline__ void load_v(const uint16_t* __restrict__ vb, int tok0, int nvalid, int lane,
-                                       uint4* vr) {
-  const int m = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nvalid - 1);
-    vr[i] = *reinterpret_cast<const uint4*>(vb + (size_t)(tok0 + tau) * D + 8 * m);
-  }
-}
-
-struct State {
-  float m[NT];
-  float l[NT];
-  f32x4 o[8][NT];
+struct Smem {
+  uint8_t k[2][TILEB];
+  uint8_t v[2][TILEB];
+  int32_t pos[2][BLK];
 };
 
-// grid: (Mq * NSUB, Hkv * ceil(G/4), B); block 256 (4 waves).
-__global__ void __launch_bounds__(kWaves * kWave, 2) prefill_kernel(PrefillArgs a) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wv = threadIdx.x / kWave;
-  const int i = blockIdx.x / NSUB;
-  const int qh = blockIdx.x - i * NSUB;  // which 16-slot part of the query block
-  const int G = a.Hq / a.Hkv;
-  const int zg = (G + 3) / 4;
-  const int g = blockIdx.y / zg;
-  const int hg = (blockIdx.y - g * zg) * 4 + wv;
-  const int b = blockIdx.z;
-  if (hg >= G) return;
-  const int h = g * G + hg;
-  const int m = lane & 15, g4 = lane >> 4;
-  const float scale_log2 = a.scale * kLog2e;
-  const int Mq = (a.Tq + BLK - 1) / BLK;
+// byte offset of 16-byte chunk c of row r inside a swizzled tile
+__device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ (r & 15)) << 4); }
 
-  const uint16_t* qb = (const uint16_t*)a.q + ((size_t)b * a.Hq + h) * (size_t)a.Tq * D;
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = min(v, shfl_xor_i(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) v = max(v, shfl_xor_i(v, o));
+  return v;
+}
+
+// Stage key block tok0 (K, V rows and positions) into buffer `slot`.  Wave w
+// moves rows 8w..8w+7 of K and of V: each instruction writes 1 KB (4 rows) at
+// LDS base + 16*lane, so lane l fetches the global chunk that the swizzle
+// places at its slot.  Rows past T re-read row T-1 (masked later).
+__device__ __forceinline__ void stage(Smem& sm, const uint16_t* __restrict__ kb,
+                                      const uint16_t* __restrict__ vb, const int32_t* __restrict__ kpos,
+                                      int tok0, int T, int slot, int w, int lane) {
+  const int cpos = lane & 15;
+#pragma unroll
+  for (int n4 = 0; n4 < 2; ++n4) {
+    const int r0 = 8 * w + 4 * n4;
+    const int r = r0 + (lane >> 4);
+    const int t = min(tok0 + r, T - 1);
+    const size_t off = (size_t)t * D + 8 * (cpos ^ (r & 15));
+    __builtin_amdgcn_global_load_lds(kb + off, (lds_void_t*)(sm.k[slot] + r0 * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + off, (lds_void_t*)(sm.v[slot] + r0 * ROWB), 16, 0, 0);
+  }
+  if (w == 0) {
+    if (kpos)
+      __builtin_amdgcn_global_load_lds(kpos + min(tok0 + lane, T - 1), (lds_void_t*)sm.pos[slot], 4, 0, 0);
+    else
+      sm.pos[slot][lane] = tok0 + lane;
+  }
+}
+
+// grid: (Mq * B * Hkv * ceil(G/4)); block 512 (8 waves).  Workgroups are
+// ordered (query block descending, then sequence/KV head/quad), so that
+// consecutive workgroups -- which the dispatcher spreads over the XCDs --
+// work on different KV heads and the longest lists start first.
+__global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) Smem sm;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  const int G = a.Hq / a.Hkv;
+  const int zq = (G + 3) / 4;
+  const int NG = a.B * a.Hkv * zq;
+  const int Mq = (a.Tq + BLK - 1) / BLK;
+  const int gid = blockIdx.x % NG;
+  const int i = Mq - 1 - (int)(blockIdx.x / NG);
+  const int b = gid / (a.Hkv * zq);
+  const int g = (gid / zq) % a.Hkv;
+  const int hg = (gid % zq) * 4 + (w & 3);
+  const bool active = hg < G;
+  const int h = g * G + min(hg, G - 1);
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int row = i * BLK + 32 * (w >> 2) + l32;  // this lane's query slot (local to the chunk)
+  const bool row_ok = row < a.Tq;
+  const float c2 = a.scale * kLog2e;
+
+  const int32_t* lst = a.idx + ((size_t)b * Mq + i) * a.cap;
+  const int nsel = a.count[(size_t)b * Mq + i];
+
+  // query position; the smallest over the whole query block decides which tiles need masks
+  int qp = -1, qmin = 0x7FFFFFFF;
+  {
+    const int slot = a.q_blk0 * BLK + row;
+    if (row_ok) qp = a.q_pos ? a.q_pos[(size_t)b * a.T + slot] : slot;
+    const int r2 = i * BLK + lane;  // every slot of the block, one per lane
+    if (r2 < a.Tq) {
+      const int s2 = a.q_blk0 * BLK + r2;
+      qmin = a.q_pos ? a.q_pos[(size_t)b * a.T + s2] : s2;
+    }
+    qmin = wave_min_i(qmin);
+  }
+  const bool force_mask = (i + 1) * BLK > a.Tq;
+
+  const size_t qrow0 = ((size_t)b * a.Hq + h) * (size_t)a.Tq;
+  if (nsel <= 0) {
+    if (active && row_ok) {
+      for (int d0 = 64 * hi; d0 < 64 * hi + 64; d0 += 8) {
+        if (a.out_bf16) {
+          *reinterpret_cast<uint4*>((uint16_t*)a.out + (qrow0 + row) * D + d0) = uint4{0u, 0u, 0u, 0u};
+        } else {
+          float* o = (float*)a.out + (qrow0 + row) * D + d0;
+          *reinterpret_cast<float4*>(o) = float4{0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<float4*>(o + 4) = float4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      if (a.lse && hi == 0) a.lse[qrow0 + row] = -INFINITY;
+    }
+    return;
+  }
+
   const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.T * D;
   const uint16_t* kb = (const uint16_t*)a.k + kv_off;
   const uint16_t* vb = (const uint16_t*)a.v + kv_off;
   const int32_t* kpos = a.k_pos ? a.k_pos + (size_t)b * a.T : nullptr;
 
-  bf16x8 qreg[NT][4];
-  int qp[NT];
+  // block list, 64 entries per register chunk (read back with readlane)
+  int chunk = lane < nsel ? lst[lane] : 0;
+  stage(sm, kb, vb, kpos, __builtin_amdgcn_readfirstlane(chunk) * BLK, a.T, 0, w, lane);
+
+  // Q^T fragments (B operand): lane holds query slot row, d = 16ks + 8hi .. +7
+  bf16x8 qf[8];
+  {
+    const uint16_t* qb = (const uint16_t*)a.q + (qrow0 + (row_ok ? row : 0)) * D;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int row = i * BLK + qh * QW + 16 * nt + m;  // local query row of the chunk
-    const int slot = a.q_blk0 * BLK + row;
-    qp[nt] = row < a.Tq ? (a.q_pos ? a.q_pos[(size_t)b * a.T + slot] : slot) : -1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 qv = {0u, 0u, 0u, 0u};
-      if (row < a.Tq) qv = *reinterpret_cast<const uint4*>(qb + (size_t)row * D + 8 * (4 * j + g4));
-      qreg[nt][j] = as_bf16x8(qv);
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = *reinterpret_cast<const uint4*>(qb + 16 * ks + 8 * hi);
+      if (!row_ok) v = uint4{0u, 0u, 0u, 0u};
+      qf[ks] = as_bf16x8(v);
     }
-  }
-  State st;
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    st.m[nt] = -INFINITY;
-    st.l[nt] = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) st.o[jj][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int32_t* lst = a.idx + ((size_t)b * Mq + i) * a.cap;
-  const int nsel = a.count[(size_t)b * Mq + i];
-  const int ntiles = nsel * (BLK / kTile);
-  auto tinfo = [&](int u, int& tok0, int& nv) {
-    const int j = lst[u >> 1];
-    tok0 = j * BLK + (u & 1) * kTile;
-    nv = min(kTile, a.T - tok0);
-  };
-  uint4 kr[8], vr[8];
-  int tok = 0, nv = 0;
-  if (ntiles > 0) {
-    tinfo(0, tok, nv);
-    if (nv > 0) {
-      load_k(kb, tok, nv, lane, kr);
-      load_v(vb, tok, nv, lane, vr);
-    }
-  }
-  for (int u = 0; u < ntiles; ++u) {
-    int tokn = 0, nvn = 0;
-    const bool more = u + 1 < ntiles;
-    if (more) tinfo(u + 1, tokn, nvn);
-    if (nv <= 0) {
-      if (more && nvn > 0) {
-        load_k(kb, tokn, nvn, lane, kr);
-        load_v(vb, tokn, nvn, lane, vr);
-      }
-      tok = tokn;
-      nv = nvn;
-      continue;
-    }
-    // ---- S^T = K . Q^T for both query n-tiles
-    f32x4 s[2][NT];
+  f32x16 o[4];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          s[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[mt * 4 + j]), qreg[nt][j],
-                                                              s[mt][nt], 0, 0, 0);
-      }
-    // key positions of this lane's 8 rows
-    int kp[8];
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
+  float mrun = -INFINITY, lsum = 0.f;
+  const int grp = lane >> 4, s16 = lane & 15;
+
+  for (int u = 0; u < nsel; ++u) {
+    const int slot = u & 1;
+    const int tok0 = __builtin_amdgcn_readlane(chunk, u & 63) * BLK;
+    if (((u + 1) & 63) == 0 && u + 1 < nsel) chunk = u + 1 + lane < nsel ? lst[u + 1 + lane] : 0;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile u have landed
+    __syncthreads();
+    if (u + 1 < nsel)
+      stage(sm, kb, vb, kpos, __builtin_amdgcn_readlane(chunk, (u + 1) & 63) * BLK, a.T, slot ^ 1, w, lane);
+    const int kmax = wave_max_i(tok0 + lane < a.T ? sm.pos[slot][lane] : -0x7FFFFFFF);
+    const bool need_mask = force_mask || tok0 + BLK > a.T || kmax > qmin;
+    if (!active) continue;
+
+    // ---- S^T = K . Q^T
+    f32x16 s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tau = 16 * mt + 4 * g4 + r;
-        kp[mt * 4 + r] = tau < nv ? (kpos ? kpos[tok + tau] : tok + tau) : 0x7FFFFFFF;
-      }
-    // K registers are free: start the next tile's K loads
-    if (more && nvn > 0) load_k(kb, tokn, nvn, lane, kr);
-    // ---- online softmax per query column
-    bf16x8 pb[NT];
-    float corr[NT];
+      for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
+    const uint8_t* kt = sm.k[slot];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x[8];
-      float tmax = -INFINITY;
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(kt + swz(32 * mt + l32, 2 * ks + hi)));
+        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
+      }
+    // ---- mask: this lane holds keys 32mt + 8a + 4hi + r
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float v = kp[mt * 4 + r] <= qp[nt] ? s[mt][nt][r] * scale_log2 : -INFINITY;
-          x[mt * 4 + r] = v;
-          tmax = fmaxf(tmax, v);
+        for (int aa = 0; aa < 4; ++aa) {
+          const int key0 = 32 * mt + 8 * aa + 4 * hi;
+          const int4 kp4 = *reinterpret_cast<const int4*>(&sm.pos[slot][key0]);
+          const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!(tok0 + key0 + r < a.T && kpv[r] <= qp)) s[mt][4 * aa + r] = -INFINITY;
         }
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-      tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-      const float m_new = fmaxf(st.m[nt], tmax);
-      const float base = m_new == -INFINITY ? 0.f : m_new;
-      corr[nt] = exp2f(st.m[nt] - base);
+    }
+    // ---- online softmax (exp2 domain, lazy reference)
+    float tm = -INFINITY;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tm = fmaxf(tm, s[mt][e]);
+    tm = fmaxf(tm, shfl_xor_f(tm, 32));
+    const float tmc = tm * c2;
+    const bool resc = tmc > mrun + kLazy;
+    if (__any((int)resc)) {
+      const float mnew = resc ? tmc : mrun;
+      const float corr = resc ? exp2f(mrun - mnew) : 1.f;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
+      lsum *= corr;
+      mrun = mnew;
+    }
+    const float nb = mrun == -INFINITY ? 0.f : -mrun;
+    bf16x8 pf[4];
+    float ps = 0.f;
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4) {
       float p[8];
-      float psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = exp2f(x[e] - base);
-        psum += p[e];
+        p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb4 >> 1][8 * (kb4 & 1) + e], c2, nb));
+        ps += p[e];
       }
-      st.l[nt] = st.l[nt] * corr[nt] + psum;
-      st.m[nt] = m_new;
-      pb[nt] = as_bf16x8(uint4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                               pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+      pf[kb4] = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                                cvt_pk_bf16(p[6], p[7])});
     }
-    // ---- O^T += V^T . P^T; V^T rows d = 8m + jj come from an in-register transpose
+    lsum += ps;
+    // ---- O^T += V^T . P^T
+    const uint8_t* vt = sm.v[slot];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int wsel = jj >> 1;
-      uint32_t a4[4];
+    for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
-      for (int aa = 0; aa < 4; ++aa) {
-        const uint32_t lo = word_of(vr[2 * aa], wsel);
-        const uint32_t hi = word_of(vr[2 * aa + 1], wsel);
-        a4[aa] = (jj & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+      for (int dt = 0; dt < 4; ++dt) {
+        s16x4 x[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int r = 16 * kb4 + 4 * (grp >> 1) + 8 * t + (s16 >> 2);
+          const int c = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
+          x[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + swz(r, c) + 8 * (s16 & 1)));
+        }
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb4], o[dt], 0, 0, 0);
       }
-      const bf16x8 vt = as_bf16x8(uint4{a4[0], a4[1], a4[2], a4[3]});
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        st.o[jj][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pb[nt], st.o[jj][nt] * corr[nt], 0, 0, 0);
-    }
-    if (more && nvn > 0) load_v(vb, tokn, nvn, lane, vr);
-    tok = tokn;
-    nv = nvn;
   }
+  if (!active || !row_ok) return;
 
-  // epilogue: normalise and store
+  // ---- epilogue: normalise and store; lane holds d = 32dt + 8a + 4hi + r of its query slot
+  const float lt = lsum + shfl_xor_f(lsum, 32);
+  const bool empty = !(lt > 0.f);
+  const float inv = empty ? 0.f : 1.f / lt;
+  const size_t obase = (qrow0 + row) * D + 4 * hi;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float lt = st.l[nt];
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
-    const int row = i * BLK + qh * QW + 16 * nt + m;
-    if (row >= a.Tq) continue;
-    const bool empty = st.m[nt] == -INFINITY || lt <= 0.f;
-    const float inv = empty ? 0.f : 1.f / lt;
-    const size_t obase = (((size_t)b * a.Hq + h) * a.Tq + row) * D + 32 * g4;
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v8[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) v8[jj] = st.o[jj][nt][r] * inv;
-      if (a.out_bf16) {
-        uint4 pk = {pack_bf16x2(v8[0], v8[1]), pack_bf16x2(v8[2], v8[3]), pack_bf16x2(v8[4], v8[5]),
-                    pack_bf16x2(v8[6], v8[7])};
-        *reinterpret_cast<uint4*>((uint16_t*)a.out + obase + 8 * r) = pk;
-      } else {
-        float* o = (float*)a.out + obase + 8 * r;
-        *reinterpret_cast<float4*>(o) = float4{v8[0], v8[1], v8[2], v8[3]};
-        *reinterpret_cast<float4*>(o + 4) = float4{v8[4], v8[5], v8[6], v8[7]};
-      }
+    for (int aa = 0; aa < 4; ++aa) {
+      const float v0 = o[dt][4 * aa] * inv, v1 = o[dt][4 * aa + 1] * inv;
+      const float v2 = o[dt][4 * aa + 2] * inv, v3 = o[dt][4 * aa + 3] * inv;
+      const size_t off = obase + 32 * dt + 8 * aa;
+      if (a.out_bf16)
+        *reinterpret_cast<uint2*>((uint16_t*)a.out + off) = uint2{cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3)};
+      else
+        *reinterpret_cast<float4*>((float*)a.out + off) = float4{v0, v1, v2, v3};
     }
-    if (a.lse && g4 == 0)
-      a.lse[((size_t)b * a.Hq + h) * a.Tq + row] = empty ? -INFINITY : (st.m[nt] + log2f(lt)) * kLn2;
-  }
+  if (a.lse && hi == 0) a.lse[qrow0 + row] = empty ? -INFINITY : (mrun + log2f(lt)) * kLn2;
 }
 
 }  // namespace
@@ -255,8 +309,9 @@ __global__ void __launch_bounds__(kWaves * kWave, 2) prefill_kernel(PrefillArgs 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   const int Mq = (a.Tq + BLK - 1) / BLK;
-  dim3 grid(Mq * NSUB, a.Hkv * ((G + 3) / 4), a.B);
-  prefill_kernel<<<grid, kWaves * kWave, 0, s>>>(a);
+  const long n = (long)Mq * a.B * a.Hkv * ((G + 3) / 4);
+  if (n <= 0) return hipSuccess;
+  prefill_kernel<<<dim3((unsigned)n), kWaves * kWave, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -154,26 +154,57 @@ class PrefillStep:
         self.out = torch.empty_like(self.out_slot)
         self.pos = None
 
-    def front(self, qI_tok, kI_tok, w, perm):
-        """Permute the indexer inputs, pool, score and select."""
+    def set_perm(self, perm):
+        """Positions of the permuted slots (the causal mask uses original positions)."""
         s = self.spec
-        L.spa_segment_permute(qI_tok, perm, s.seg, dim=1, dst=self.qIp)
-        L.spa_segment_permute(kI_tok, perm, s.seg, dim=1, dst=self.kIp)
-        L.spa_index_score(self.qIp, self.kIp, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
-                          ws=self.score_ws)
-        L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
-                          count=self.count)
-        return self.idx, self.count
+        self.pos = perm.reshape(1, -1) if s.B == 1 else perm.reshape(1, -1).expand(s.B, -1).contiguous()
+        return self.pos
 
-    def __call__(self, q, k, v, qI_tok, kI_tok, w, perm):
+    def permute_inputs(self, q, k, v, perm):
+        """Q, K, V into slot order (segment-wise permutation along the token axis)."""
         s = self.spec
-        if self.pos is None or self.pos.data_ptr() == 0 or not torch.equal(self.pos[0], perm):
-            self.pos = perm.reshape(1, -1).expand(s.B, -1).contiguous()
         L.spa_segment_permute(q, perm, s.seg, dim=2, dst=self.qp)
         L.spa_segment_permute(k, perm, s.seg, dim=2, dst=self.kp)
         L.spa_segment_permute(v, perm, s.seg, dim=2, dst=self.vp)
+
+    def permute_index(self, qI_tok, kI_tok, perm):
+        """The per-token indexer vectors into slot order."""
+        s = self.spec
+        L.spa_segment_permute(qI_tok, perm, s.seg, dim=1, dst=self.qIp)
+        L.spa_segment_permute(kI_tok, perm, s.seg, dim=1, dst=self.kIp)
+
+    def score(self, w):
+        """Pool the permuted per-token vectors into blocks and score every (query block, past key block)."""
+        s = self.spec
+        return L.spa_index_score(self.qIp, self.kIp, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
+                                 ws=self.score_ws)
+
+    def select(self):
+        s = self.spec
+        return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
+                                 count=self.count)
+
+    def front(self, qI_tok, kI_tok, w, perm):
+        """Permute the indexer inputs, pool, score and select."""
+        self.permute_index(qI_tok, kI_tok, perm)
+        self.score(w)
+        self.select()
+        return self.idx, self.count
+
+    def attend(self):
+        s = self.spec
+        return L.spa_block_sparse_prefill(self.qp, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
+                                          k_pos=self.pos, out=self.out_slot, lse=self.lse_slot)
+
+    def unpermute(self, perm):
+        """O from slot order back to the original token order."""
+        s = self.spec
+        return L.spa_segment_permute(self.out_slot, perm, s.seg, dim=2, inverse=True, dst=self.out)
+
+    def __call__(self, q, k, v, qI_tok, kI_tok, w, perm):
+        self.set_perm(perm)
+        self.permute_inputs(q, k, v, perm)
         self.front(qI_tok, kI_tok, w, perm)
-        L.spa_block_sparse_prefill(self.qp, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
-                                   k_pos=self.pos, out=self.out_slot, lse=self.lse_slot)
-        L.spa_segment_permute(self.out_slot, perm, s.seg, dim=2, inverse=True, dst=self.out)
+        self.attend()
+        self.unpermute(perm)
         return self.out
