@@ -12,7 +12,9 @@
 // workgroup into LDS (direct global->LDS 16-byte loads, 16-byte chunks
 // XOR-swizzled by row so that the MFMA operand reads are free of bank
 // conflicts) and read by all eight waves.  K, V and key positions are
-// double-buffered: tile u+1 streams in while tile u is computed.
+// double-buffered: tile u+1 streams in while tile u is computed.  The
+// operand fragments of the two products are read from LDS one step ahead of
+// the MFMAs that consume them.
 //
 // Per 64-key tile a wave computes, with v_mfma_f32_32x32x16_bf16:
 //   S^T[64 keys, 32 queries] = K . Q^T      (2 x 8 MFMA)
@@ -30,8 +32,9 @@
 // only the reference point of the partial sums differs.
 //
 // Keys are masked with k_pos <= q_pos (original positions) and t < T; the
-// masks are skipped for tiles whose largest key position is below the
-// block's smallest query position (every block of an earlier segment).
+// masks are skipped for tiles whose key positions all lie below the block's
+// smallest query position (every block of an earlier segment), which one
+// wave vote decides.
 #include "spa_internal.h"
 
 namespace spa {
@@ -60,6 +63,8 @@ struct Smem {
 
 // byte offset of 16-byte chunk c of row r inside a swizzled tile
 __device__ __forceinline__ int swz(int r, int c) { return r * ROWB + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ int vsw(int r) { return 4 * (r & 3) + 2 * ((r >> 1) & 1); }
+__device__ __forceinline__ int swz_v(int r, int c) { return r * ROWB + ((c ^ vsw(r)) << 4); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -73,11 +78,6 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 __device__ __forceinline__ int wave_min_i(int v) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) v = min(v, shfl_xor_i(v, o));
-  return v;
-}
-__device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) v = max(v, shfl_xor_i(v, o));
   return v;
 }
 
@@ -94,9 +94,9 @@ __device__ __forceinline__ void stage(Smem& sm, const uint16_t* __restrict__ kb,
     const int r0 = 8 * w + 4 * n4;
     const int r = r0 + (lane >> 4);
     const int t = min(tok0 + r, T - 1);
-    const size_t off = (size_t)t * D + 8 * (cpos ^ (r & 15));
-    __builtin_amdgcn_global_load_lds(kb + off, (lds_void_t*)(sm.k[slot] + r0 * ROWB), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + off, (lds_void_t*)(sm.v[slot] + r0 * ROWB), 16, 0, 0);
+    const size_t row = (size_t)t * D;
+    __builtin_amdgcn_global_load_lds(kb + row + 8 * (cpos ^ (r & 15)), (lds_void_t*)(sm.k[slot] + r0 * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + row + 8 * (cpos ^ vsw(r)), (lds_void_t*)(sm.v[slot] + r0 * ROWB), 16, 0, 0);
   }
   if (w == 0) {
     if (kpos)
@@ -201,8 +201,8 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     __syncthreads();
     if (u + 1 < nsel)
       stage(sm, kb, vb, kpos, __builtin_amdgcn_readlane(chunk, (u + 1) & 63) * BLK, a.T, slot ^ 1, w, lane);
-    const int kmax = wave_max_i(tok0 + lane < a.T ? sm.pos[slot][lane] : -0x7FFFFFFF);
-    const bool need_mask = force_mask || tok0 + BLK > a.T || kmax > qmin;
+    const bool need_mask =
+        force_mask || tok0 + BLK > a.T || __any((int)(tok0 + lane < a.T && sm.pos[slot][lane] > qmin));
     if (!active) continue;
 
     // ---- S^T = K . Q^T
@@ -212,13 +212,24 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
     const uint8_t* kt = sm.k[slot];
+    bf16x8 kf[8][2];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 kf = as_bf16x8(*reinterpret_cast<const uint4*>(kt + swz(32 * mt + l32, 2 * ks + hi)));
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
-      }
+      for (int mt = 0; mt < 2; ++mt)
+        kf[ks][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(kt + swz(32 * mt + l32, 2 * ks + hi)));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks][mt], qf[ks], s[mt], 0, 0, 0);
+    // reads of d-step ks+1 are issued before the products of d-step ks
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int ks = 0; ks < 7; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     // ---- mask: this lane holds keys 32mt + 8a + 4hi + r
     if (need_mask) {
 #pragma unroll
@@ -267,6 +278,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     lsum += ps;
     // ---- O^T += V^T . P^T
     const uint8_t* vt = sm.v[slot];
+    bf16x8 vf[4][4];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4)
 #pragma unroll
@@ -276,11 +288,22 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
         for (int t = 0; t < 2; ++t) {
           const int r = 16 * kb4 + 4 * (grp >> 1) + 8 * t + (s16 >> 2);
           const int c = 4 * dt + 2 * (grp & 1) + ((s16 & 3) >> 1);
-          x[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + swz(r, c) + 8 * (s16 & 1)));
+          x[t] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + swz_v(r, c) + 8 * (s16 & 1)));
         }
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb4], o[dt], 0, 0, 0);
+        vf[kb4][dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
+#pragma unroll
+    for (int kb4 = 0; kb4 < 4; ++kb4)
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kb4][dt], pf[kb4], o[dt], 0, 0, 0);
+    // fragment reads run two steps ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int j = 0; j < 14; ++j) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
   }
   if (!active || !row_ok) return;
 
