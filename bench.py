@@ -2,8 +2,8 @@
 
 Default workload: one sparse decode step at 128K context.  A step is the
 whole decode hot path of one attention layer over one batch: int8 indexer
-scores and dual top-p selection (one fused launch), then the split sparse
-flash-decode and its log-sum-exp merge.  B = 16 sequences of 131072 tokens,
+scores, dual top-p selection, then the split sparse flash-decode and its
+log-sum-exp merge, replayed as HIP graphs.  B = 16 sequences of 131072 tokens,
 64 query heads over 8 KV heads, d = 128, 64-token blocks, top-p 0.9 over
 softmax(s/8) with K_min 16 / K_max 512 plus 1 sink and 4 local blocks
 (seeded synthetic inputs, planted relevant blocks per sequence drawn from
@@ -60,6 +60,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10 decode, 3 prefill)")
     ap.add_argument("--workload", choices=WORKLOADS, default="decode_128k_topp")
     ap.add_argument("--copies", type=int, default=0, help="input buffer sets to rotate through (0 = auto)")
+    ap.add_argument("--select-path", choices=("fused", "separate"), default="separate",
+                    help="decode: one fused scoring+selection launch, or the scoring kernel then the selection kernel")
+    ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
+                    help="decode: replay each step as a HIP graph (one per input set) or launch it call by call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-json", default=None,
@@ -201,7 +205,7 @@ def bench_decode(args, cfg):
                         r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta,
                         p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
                         local_window_tok=cfg.local_window_tok)
-    step = S.DecodeStep(spec)
+    step = S.DecodeStep(spec, fused=args.select_path == "fused")
     step(base["q"], base["k"], base["v"], base["qI"], base["kI"], base["w"], seq_len, head_mode)
     torch.cuda.synchronize()
     idx, counts = step.idx.cpu().numpy(), step.count.cpu().numpy()
@@ -214,45 +218,79 @@ def bench_decode(args, cfg):
     log(f"[bench] inputs resident: {copies} copies of {per_copy / 2**30:.3f} GiB; "
         f"{(ab + ib) / 1e6:.1f} MB touched per step")
 
+    # HIP graphs: one per input set (a single step) and one chunk of
+    # C = min(copies, steps) consecutive steps on input sets 0 .. C-1, so that
+    # the steps inside a chunk follow each other without a launch boundary.
+    # The timed steps use input set j % copies for step j.
+    use_graph = args.launch == "graph" and copies <= 64
+    step_args = [(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], seq_len, head_mode) for x in sets]
+    chunk_len = min(copies, args.steps)
+    graphs = [step.capture(*a) for a in step_args] if use_graph else None
+    chunk = step.capture_steps(step_args[:chunk_len]) if use_graph else None
+    if use_graph:
+        log(f"[bench] captured {len(graphs)} single-step graphs and a {chunk_len}-step graph")
+
+    def run_steps(n):
+        """Launch n steps on input sets 0, 1, ... (mod copies)."""
+        j = 0
+        while j < n:
+            if use_graph and j % copies == 0 and n - j >= chunk_len:
+                chunk.replay()
+                j += chunk_len
+            elif use_graph:
+                graphs[j % copies].replay()
+                j += 1
+            else:
+                run(j)
+                j += 1
+
     def run(i, ev=None):
         x = sets[i % copies]
         if ev is not None:
             ev[0].record()
-        step.score_select(x["qI"], x["kI"], x["w"], seq_len)
+        if step.fused:
+            step.score_select(x["qI"], x["kI"], x["w"], seq_len)
+        else:
+            step.score(x["qI"], x["kI"], x["w"], seq_len)
+            step.select(seq_len)
         if ev is not None:
             ev[1].record()
         step.attend(x["q"], x["k"], x["v"], seq_len, head_mode)
         if ev is not None:
             ev[2].record()
 
-    for i in range(args.warmup):
-        run(i)
+    run_steps(args.warmup)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
         calibration_copy(args.copy_calibration_mib)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps: launches only, bracketed by one event pair
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for i in range(args.steps):
-        run(args.warmup + i, evs[i])
+    run_steps(args.steps)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
+    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
+    # a second pass of the same steps with events between the stages, for the per-stage breakdown
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(args.warmup + args.steps + i, evs[i])
+    torch.cuda.synchronize()
     sel_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[1].elapsed_time(e[2]) for e in evs]
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
 
     attn_s = float(np.mean(attn_ms)) * 1e-3
     achieved = ab / attn_s / 1e9
     traffic = load_traffic(args.traffic_json, source_sha("decode_attn.hip"))
-    select_name = "score_select_topp" if cfg.select == "topp" else "score_select_topk"
+    select_name = ("score_select_topp" if cfg.select == "topp" else "score_select_topk") + \
+        ("" if step.fused else " (score, then select)")
     res = {
         "metric": DECODE_METRIC if cfg is config_of("decode_128k_topp")
         else f"sparse-decode tokens/s ({cfg.name}, 1 GPU); achieved HBM GB/s vs peak",
@@ -272,13 +310,16 @@ def bench_decode(args, cfg):
                    "beta": cfg.beta, "k_min": cfg.k_min, "k_max": cfg.k_max, "n_sink": cfg.n_sink,
                    "n_local": cfg.n_local, "retrieval_groups": int(sum(1 for m in inp["head_mode"] if m == 0)),
                    "local_sink_tok": cfg.local_sink_tok, "local_window_tok": cfg.local_window_tok,
-                   "input_copies_rotated": copies, "seed": args.seed},
+                   "input_copies_rotated": copies, "seed": args.seed,
+                   "launch": f"hip_graph, {chunk_len} steps per graph" if use_graph else "eager",
+                   "select_path": args.select_path},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "spa_sparse_decode_attn (decode main kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": ab, "avg_launch_ms": attn_s * 1e3},
         "stages_ms": {select_name: float(np.mean(sel_ms)), "attention": float(np.mean(attn_ms))},
-        "step_ms_p10_p50_p90": [pct(step_ms, 10), pct(step_ms, 50), pct(step_ms, 90)],
+        "staged_step_ms_p10_p50_p90": [pct(step_ms, 10), pct(step_ms, 50), pct(step_ms, 90)],
+        "stage_timing": "a second pass of the same steps, launched call by call with events between stages",
         "selected_blocks": {"mean": float(counts.mean()), "min": int(counts.min()), "max": int(counts.max())},
         "step_algorithmic_bytes": ab + ib,
         "step_hbm_gbs": (ab + ib) / (ms_step * 1e-3) / 1e9,
@@ -374,18 +415,22 @@ def bench_prefill(args, cfg):
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
         calibration_copy(args.copy_calibration_mib)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        run(evs[i])
+        run()
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
     ms_step = total_ms / args.steps
-    st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events")
+    # a second pass with events between the stages, for the per-stage breakdown
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
 
     idx, counts = step.idx[0].cpu().numpy(), step.count[0].cpu().numpy()
     pairs = prefill_pairs(inp["perm"], idx, counts, cfg.blk)
@@ -421,6 +466,7 @@ def bench_prefill(args, cfg):
                      "algorithmic_flop_per_launch": flop, "attended_pairs_per_head": pairs,
                      "avg_launch_ms": attn_s * 1e3},
         "stages_ms": st_ms,
+        "stage_timing": "a second pass of the same steps with events between stages",
         "scoring": {"int8_ops": score_ops, "tops": score_ops / score_s / 1e12,
                     "frac_of_int8_mfma_peak": score_ops / score_s / 1e12 / INT8_MFMA_PEAK_TOPS,
                     "note": "pool + score launch: two per-token pooling passes and the block-pair scoring"},

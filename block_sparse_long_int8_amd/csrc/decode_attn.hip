@@ -10,8 +10,9 @@
 //   * an "item" is one (sequence b, KV head g); its tokens are cut into 32-token
 //     tiles (a selected 64-token block is two tiles);
 //   * all items' tiles are laid end to end and split evenly over a persistent
-//     grid of waves, so load balance does not depend on how budgets vary per
-//     sequence (dual top-p gives 21..185 blocks per sequence);
+//     grid of waves (at least 2 tiles per wave for bf16), so load balance does not
+//     depend on how budgets vary per sequence (dual top-p gives 21..185
+//     blocks per sequence);
 //   * a wave writes one partial (unnormalised o, running max m, running sum l)
 //     per item it touched, into slot item + wave; a second kernel merges the
 //     partials of item i (slots i + w for w = first_tile(i)/share ..
@@ -79,6 +80,13 @@ __host__ __device__ inline size_t ws_total(int n_items, int workers, int G, int 
   const size_t slots = (size_t)n_items + workers;
   return kHeader + align256((size_t)(n_items + 1) * sizeof(int)) + align256(slots * G * 2 * sizeof(float)) +
          align256(slots * G * d * sizeof(float));
+}
+
+// Tiles per wave: an even split over the persistent waves, but at least
+// min_share tiles, so that small steps (few sequences) do not scatter into
+// one-tile partials whose merge costs more than the attention itself.
+__device__ __forceinline__ int split_share(int total, int workers, int min_share) {
+  return total > 0 ? max((total + workers - 1) / workers, min_share) : 0;
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -388,7 +396,7 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   __shared__ uint4 qcache[kWPB][kQCache][4][kWave];  // Q operands of a wave's first items
   __shared__ int4 tdesc[kWPB][kWave];                 // descriptors of 64 consecutive tiles
   const int total = build_plan(a, n_items, item_start, scratch);
-  const int share = (total + workers - 1) / workers;
+  const int share = split_share(total, workers, 2);
   const int G = a.Hq / a.Hkv;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, D);
   if (blockIdx.x == 0) {
@@ -569,7 +577,7 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
   __shared__ float p_s[kWPB][16][kTile];
   __shared__ float mnew_s[kWPB][16];
   const int total = build_plan(a, n_items, item_start, scratch);
-  const int share = (total + workers - 1) / workers;
+  const int share = split_share(total, workers, 1);
   const int G = a.Hq / a.Hkv;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, DD);
   if (blockIdx.x == 0) {
@@ -706,7 +714,7 @@ constexpr int kMergeThreads = 1024;
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
   __shared__ float red[kMergeThreads];
   __shared__ float4 acc_s[kMergeThreads];
-  __shared__ float Ms[16];
+  __shared__ float Ms_all[kMergeThreads];
   const int G = a.Hq / a.Hkv;
   const int d = a.d;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
@@ -725,29 +733,25 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const bool active = sub < nsub;
   const int h = pair / per_head;
   const int c4 = pair - h * per_head;
-  // pass 1: head maxima
-  float mx = -INFINITY;
-  if (active)
-    for (int p = sub; p < nparts; p += nsub) mx = fmaxf(mx, ws.part_ml[(((size_t)item + w0 + p) * G + h) * 2]);
-  red[tid] = mx;
-  __syncthreads();
-  if (tid < G) {
-    float m = -INFINITY;
-    for (int t = tid * per_head; t < nsub * pairs; t += pairs)
-      for (int c = 0; c < per_head; ++c) m = fmaxf(m, red[t + c]);
-    Ms[tid] = m;
-  }
-  __syncthreads();
-  // pass 2: rescaled sums of this thread's partials
-  float L = 0.f;
+  // one pass over this thread's partials with a running maximum
+  float M = -INFINITY, L = 0.f;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  const float M = active ? Ms[h] : 0.f;
-  if (active && M != -INFINITY) {
+  if (active) {
 #pragma unroll 4
     for (int p = sub; p < nparts; p += nsub) {
       const size_t slot = (size_t)item + w0 + p;
       const float2 ml = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
       const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
+      if (ml.x == -INFINITY) continue;
+      if (ml.x > M) {
+        const float sc = exp2f(M - ml.x);  // 0 while M is -inf
+        L *= sc;
+        acc.x *= sc;
+        acc.y *= sc;
+        acc.z *= sc;
+        acc.w *= sc;
+        M = ml.x;
+      }
       const float f = exp2f(ml.x - M);
       L += f * ml.y;
       acc.x += f * ow.x;
@@ -756,18 +760,31 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
       acc.w += f * ow.w;
     }
   }
+  Ms_all[tid] = M;
   red[tid] = L;
   acc_s[tid] = acc;
   __syncthreads();
   if (sub != 0) return;
   const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
-  for (int u = 1; u < nsub; ++u) {
-    L += red[u * pairs + pair];
-    const float4 o2 = acc_s[u * pairs + pair];
-    acc.x += o2.x;
-    acc.y += o2.y;
-    acc.z += o2.z;
-    acc.w += o2.w;
+  for (int u = 1; u < nsub; ++u) M = fmaxf(M, Ms_all[u * pairs + pair]);
+  if (M != -INFINITY) {
+    const float f0 = exp2f(Ms_all[pair] - M);
+    L *= f0;
+    acc.x *= f0;
+    acc.y *= f0;
+    acc.z *= f0;
+    acc.w *= f0;
+    for (int u = 1; u < nsub; ++u) {
+      const float mu = Ms_all[u * pairs + pair];
+      if (mu == -INFINITY) continue;
+      const float f = exp2f(mu - M);
+      L += f * red[u * pairs + pair];
+      const float4 o2 = acc_s[u * pairs + pair];
+      acc.x += f * o2.x;
+      acc.y += f * o2.y;
+      acc.z += f * o2.z;
+      acc.w += f * o2.w;
+    }
   }
   float4 o = {0.f, 0.f, 0.f, 0.f};
   float lse_v = -INFINITY;

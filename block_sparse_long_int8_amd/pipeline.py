@@ -1,8 +1,7 @@
 """The two hot paths as sequences of library calls, with buffers preallocated.
 
-DecodeStep:  spa_score_select_decode (scoring and selection in one launch; or
-             spa_index_score -> spa_select_topk | spa_select_topp)
-             -> spa_sparse_decode_attn
+DecodeStep:  spa_index_score -> spa_select_topk | spa_select_topp (or both in
+             one launch: spa_score_select_decode) -> spa_sparse_decode_attn
 PrefillStep: spa_segment_permute (Q, K, V, per-token indexer vectors)
              -> spa_index_score (per-token, pooled) -> spa_select_topk (prefill rows)
              -> spa_block_sparse_prefill -> spa_segment_permute (inverse, on O)
@@ -55,11 +54,15 @@ class DecodeSpec:
 class DecodeStep:
     """One decode step of one attention layer; owns its scratch and output buffers.
 
-    ``fused=True`` scores and selects in one launch (spa_score_select_decode);
-    ``fused=False`` runs spa_index_score then spa_select_*.
+    ``fused=False`` (default) runs spa_index_score (wide, all CUs) then
+    spa_select_* (one workgroup per sequence); ``fused=True`` scores and
+    selects in one launch (spa_score_select_decode), which saves a launch but
+    reads the indexer keys with only one workgroup per sequence.  Replayed as a
+    HIP graph (``capture``), where launches cost nothing, the separate pair is
+    the faster of the two.
     """
 
-    def __init__(self, spec: DecodeSpec, device="cuda", fused: bool = True):
+    def __init__(self, spec: DecodeSpec, device="cuda", fused: bool = False):
         self.spec = s = spec
         self.fused = fused
         dev = torch.device(device)
@@ -105,6 +108,26 @@ class DecodeStep:
             self.score(qI, kI, w, seq_len)
             self.select(seq_len)
         return self.attend(q, k_cache, v_cache, seq_len, head_mode)
+
+    def capture(self, q, k_cache, v_cache, qI, kI, w, seq_len, head_mode=None) -> "torch.cuda.CUDAGraph":
+        """Record one whole step on these tensors as a HIP graph (replay with ``graph.replay()``).
+
+        Every launch of the step goes into the graph; none of them allocates,
+        clears memory or synchronises, so the graph holds kernel nodes only.
+        The graph reads and writes the tensors it was recorded with.
+        """
+        return self.capture_steps([(q, k_cache, v_cache, qI, kI, w, seq_len, head_mode)])
+
+    def capture_steps(self, steps) -> "torch.cuda.CUDAGraph":
+        """Record several consecutive steps (one argument tuple each, in order) as one HIP graph."""
+        for a in steps:
+            self(*a)  # settle lazy state outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for a in steps:
+                self(*a)
+        return g
 
 
 @dataclass

@@ -73,6 +73,38 @@ def test_decode_step_parity(cfg, fused):
     assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
 
 
+@pytest.mark.parametrize("cfg", [gen.SMALL_DECODE_TOPP, gen.SMALL_DECODE_HEADSPLIT], ids=["topp", "headsplit"])
+def test_decode_graph_replay(cfg):
+    """A decode step recorded as a HIP graph gives the eager result on every replay.
+
+    Between replays the test clears the outputs with eager kernels and
+    synchronises; halfway it swaps new query values into the recorded input
+    tensor, so the later replays must follow the new inputs.
+    """
+    print(f"[decode graph replay] {cfg.name}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    args = (t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    step = S.DecodeStep(_spec(cfg))
+    step(*args)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (step.out, step.lse, step.idx, step.count)]
+    g = step.capture(*args)
+    q_new = dev(gen.make(cfg, seed=1)["q"], cfg.dtype)
+    for rep in range(6):
+        if rep == 3:  # new query values in the recorded tensor: recompute the eager reference
+            t["q"].copy_(q_new)
+            step(*args)
+            torch.cuda.synchronize()
+            ref = [x.clone() for x in (step.out, step.lse, step.idx, step.count)]
+        for x in (step.out, step.lse, step.idx, step.count):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((step.out, step.lse, step.idx, step.count), ref):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager step"
+
+
 @pytest.mark.parametrize("cfg", [gen.SMALL_DECODE_TOPK, gen.SMALL_DECODE_TOPP], ids=["topk", "topp"])
 def test_decode_deterministic(cfg):
     inp, t = _decode_inputs(cfg)

@@ -57,13 +57,12 @@ def test_full_decode_parity(S, cfg):
     step.attend(q, k.clone(), v.clone(), dev(inp["seq_len"]), dev(inp["head_mode"]))
     torch.cuda.synchronize()
     assert torch.equal(out0, step.out)
-    # the separate score + select calls give the same scores and selection
-    sep = S.DecodeStep(spec, fused=False)
-    sep.score(dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]))
-    sep.select(dev(inp["seq_len"]))
+    # the fused scoring + selection launch gives the same scores and selection
+    fus = S.DecodeStep(spec, fused=True)
+    fus.score_select(dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), keep_scores=True)
     torch.cuda.synchronize()
-    assert torch.equal(sep.scores, step.scores)
-    assert torch.equal(sep.idx, step.idx) and torch.equal(sep.count, step.count)
+    assert torch.equal(fus.scores, step.scores)
+    assert torch.equal(fus.idx, step.idx) and torch.equal(fus.count, step.count)
 
 
 def test_full_prefill_64k_parity(S):
