@@ -50,6 +50,14 @@ constexpr int kMaxItems = 4096;
 constexpr int kTile = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;  // exp2-domain growth of a running maximum tolerated before O is rescaled
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats to a bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 constexpr size_t kHeader = 256;
 constexpr int kQCache = 2;  // items whose Q a wave keeps in LDS
 constexpr int kOcc = 2;     // bf16 workgroups (4 waves each) resident per CU
@@ -308,22 +316,30 @@ __device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg,
     }
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
   tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-  const float m_new = fmaxf(st.m, tmax);
+  // lazy reference: the running sums keep their reference maximum until a
+  // tile's maximum exceeds it by more than 2^8 (exp2 domain), so O is
+  // rescaled only on the rare tiles that raise it that much
+  const bool resc = tmax > st.m + kLazy;
+  const float m_new = resc ? tmax : st.m;
   // m_new is -inf only if every token seen so far is masked: nothing to add
   const float base = m_new == -INFINITY ? 0.f : m_new;
-  const float corr = exp2f(st.m - base);
+  const float corr = resc ? exp2f(st.m - base) : 1.f;
   float p[8];
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    p[e] = exp2f(x[e] - base);
+    p[e] = __builtin_amdgcn_exp2f(x[e] - base);
     psum += p[e];
   }
   st.l = st.l * corr + psum;
   st.m = m_new;
+  if (__any((int)resc)) {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) st.o[jj] *= corr;
+  }
   // P^T operand: k index 8*g4 + e <-> token 16*(e/4) + 4*g4 + (e%4)
-  const uint4 pu = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                    pack_bf16x2(p[6], p[7])};
+  const uint4 pu = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
+                    cvt_pk_bf16(p[6], p[7])};
   const bf16x8 pb = as_bf16x8(pu);
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
@@ -337,8 +353,7 @@ __device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg,
       a4[aa] = (jj & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
     const uint4 au = {a4[0], a4[1], a4[2], a4[3]};
-    f32x4 acc = st.o[jj] * corr;
-    st.o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(au), pb, acc, 0, 0, 0);
+    st.o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(au), pb, st.o[jj], 0, 0, 0);
   }
 }
 

@@ -27,6 +27,7 @@ namespace spa {
 namespace {
 
 constexpr int kMaxThreads = 1024;
+constexpr int kSortThreads = 512;  // keys per thread: max(2, N / 512)
 constexpr int kMaxWaves = kMaxThreads / kWave;
 constexpr int kMaxBlocks = 4096;
 
@@ -212,15 +213,25 @@ __device__ void bitonic64(unsigned long long (&x)[EPT], int n_sort, unsigned lon
   }
 }
 
-__device__ __forceinline__ int block_max_int(int v, int* scratch) {
-  for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o, kWave));
+// Block-wide maximum of a and of b (one exchange through LDS).
+__device__ __forceinline__ void block_max2_int(int& a, int& b, int* scratch) {
+  for (int o = 1; o < kWave; o <<= 1) {
+    a = max(a, __shfl_xor(a, o, kWave));
+    b = max(b, __shfl_xor(b, o, kWave));
+  }
   const int wid = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) scratch[wid] = v;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    scratch[2 * wid] = a;
+    scratch[2 * wid + 1] = b;
+  }
   __syncthreads();
-  int r = scratch[0];
-  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) r = max(r, scratch[w]);
+  a = scratch[0];
+  b = scratch[1];
+  for (int w = 1; w < (int)(blockDim.x / kWave); ++w) {
+    a = max(a, scratch[2 * w]);
+    b = max(b, scratch[2 * w + 1]);
+  }
   __syncthreads();
-  return r;
 }
 
 // grid: B*M rows; block N / EPT threads; dynamic LDS: N * 8 bytes.
@@ -228,11 +239,12 @@ __device__ __forceinline__ int block_max_int(int v, int* scratch) {
 template <int LOG2N, bool SCORED>
 __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   constexpr int N = 1 << LOG2N;
-  constexpr int EPT = N > 2 * kMaxThreads ? N / kMaxThreads : 2;
+  constexpr int EPT = N > 2 * kSortThreads ? N / kSortThreads : 2;
   extern __shared__ unsigned long long lds64[];
   unsigned* lds32 = reinterpret_cast<unsigned*>(lds64);
   __shared__ unsigned mask[kMaxBlocks / 32];
-  __shared__ int iscratch[kMaxWaves];
+  __shared__ int iscratch[2 * kMaxWaves];
+  __shared__ int kp_s;
   __shared__ float fscratch[kMaxWaves];
   __shared__ int smax_s;
 
@@ -312,11 +324,13 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
     if (a.scores_out)
       for (int j = tid; j < nKb; j += blockDim.x) a.scores_out[(size_t)b * nKb + j] = j < nbv ? s_lds[j] : INT32_MIN;
   } else {
+    // loaded over the whole row, independent of seq_len, so that both global
+    // loads are in flight together; ranks past n_cand are ignored below
     const int32_t* srow = a.scores + (size_t)row * nKb;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int r = tid * EPT + e;
-      sc[e] = r < n_cand ? srow[c0 + r] : 0;
+      sc[e] = c0 + r < nKb ? srow[c0 + r] : 0;
     }
   }
 #pragma unroll
@@ -328,8 +342,10 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
     }
   }
   for (int t = tid; t < kMaxBlocks / 32; t += blockDim.x) mask[t] = 0u;
-  const int smax = block_max_int(lmax, iscratch);
-  const int smin = -block_max_int(lmin == INT32_MIN ? INT32_MAX : -lmin, iscratch);
+  int smax = lmax, nsmin = lmin == INT32_MIN ? INT32_MAX : -lmin;
+  if (tid == 0) kp_s = n_cand;  // ordered before its readers by the barriers below
+  block_max2_int(smax, nsmin, iscratch);
+  const int smin = -nsmin;
   // 32-bit keys when (score - smin) and the inverted index fit side by side
   int ib = 1;
   while ((1 << ib) <= nKb) ++ib;
@@ -386,17 +402,19 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
     }
     float Z;
     float run = block_excl_scan_float(local, fscratch, &Z);
-    // ranks whose normalised cumulative mass is still below p
-    int below = 0;
+    // k_p = 1 + the first rank at which the normalised cumulative mass
+    // reaches p (cumulative mass does not decrease with rank, so this is one
+    // rank up to rounding at thread boundaries; the minimum keeps it
+    // deterministic; no crossing only if rounding keeps the total below p)
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int r = tid * EPT + e;
+      const bool before = run / Z < a.p;
       run += mass[e];
-      below += (r < n_cand && run / Z < a.p) ? 1 : 0;
+      if (r < n_cand && before && !(run / Z < a.p)) atomicMin(&kp_s, r + 1);
     }
-    int n_below;
-    block_excl_scan_int(below, iscratch, &n_below);
-    const int kp = min(n_below + 1, n_cand);
+    __syncthreads();
+    const int kp = min(kp_s, n_cand);
     k_sel = min(n_cand, max(a.k_min, min(kp, a.k_max)));
   }
 
@@ -411,9 +429,33 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   if (tid == 0 && diag >= 0) atomicOr(&mask[diag >> 5], 1u << (diag & 31));
   __syncthreads();
 
-  // ascending output: one 32-block word per thread
+  // ascending output: one 32-block word per lane of wave 0 (rows of up to
+  // 2048 blocks), else one word per thread
   const int nwords = (nKb + 31) >> 5;
   int32_t* out = a.idx + (size_t)row * a.cap;
+  if (nwords <= kWave) {
+    if (tid >= kWave) return;
+    const unsigned m = tid < nwords ? mask[tid] : 0u;
+    const int c = __popc(m);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (tid >= o) incl += y;
+    }
+    const int written = __shfl(incl, kWave - 1, kWave);
+    int pos = incl - c;
+    unsigned mm = m;
+    while (mm) {
+      const int bit = __ffs(mm) - 1;
+      mm &= mm - 1;
+      if (pos < a.cap) out[pos] = (tid << 5) + bit;
+      ++pos;
+    }
+    for (int t = written + tid; t < a.cap; t += kWave) out[t] = -1;
+    if (tid == 0) a.count[row] = min(written, a.cap);
+    return;
+  }
   int written = 0;
   for (int w0 = 0; w0 < nwords; w0 += blockDim.x) {
     const int wdx = w0 + tid;
@@ -442,7 +484,7 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   int log2n = 7;
   while ((1 << log2n) < a.nKb) ++log2n;
   const int n = 1 << log2n;
-  const int ept = n > 2 * kMaxThreads ? n / kMaxThreads : 2;
+  const int ept = n > 2 * kSortThreads ? n / kSortThreads : 2;
   const int threads = n / ept;
   const size_t lds = (size_t)n * sizeof(unsigned long long);
   const int grid = a.B * a.M;
