@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="input buffer sets to rotate through (0 = auto)")
     ap.add_argument("--select-path", choices=("fused", "separate"), default="separate",
                     help="decode: one fused scoring+selection launch, or the scoring kernel then the selection kernel")
+    ap.add_argument("--select-algo", choices=("sort", "hist"), default="sort",
+                    help="selection kernel: bitonic sort of the candidates, or the sort-free radix threshold search")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
                     help="decode: replay each step as a HIP graph (one per input set) or launch it call by call")
     ap.add_argument("--seed", type=int, default=0)
@@ -204,7 +206,7 @@ def bench_decode(args, cfg):
     spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx,
                         r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta,
                         p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
-                        local_window_tok=cfg.local_window_tok)
+                        local_window_tok=cfg.local_window_tok, select_algo=args.select_algo)
     step = S.DecodeStep(spec, fused=args.select_path == "fused")
     step(base["q"], base["k"], base["v"], base["qI"], base["kI"], base["w"], seq_len, head_mode)
     torch.cuda.synchronize()
@@ -312,7 +314,7 @@ def bench_decode(args, cfg):
                    "local_sink_tok": cfg.local_sink_tok, "local_window_tok": cfg.local_window_tok,
                    "input_copies_rotated": copies, "seed": args.seed,
                    "launch": f"hip_graph, {chunk_len} steps per graph" if use_graph else "eager",
-                   "select_path": args.select_path},
+                   "select_path": args.select_path, "select_algo": args.select_algo},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "spa_sparse_decode_attn (decode main kernel + decode_merge_kernel)",
@@ -382,7 +384,7 @@ def bench_prefill(args, cfg):
     x = {"q": dev(inp["q"], "bf16"), "k": dev(inp["k"], "bf16"), "v": dev(inp["v"], "bf16"),
          "qI": dev(inp["qI_tok"]), "kI": dev(inp["kI_tok"]), "w": dev(inp["w"]), "perm": dev(inp["perm"])}
     spec = S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
-                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg)
+                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, select_algo=args.select_algo)
     step = S.PrefillStep(spec)
     step(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], x["perm"])
     torch.cuda.synchronize()
@@ -459,7 +461,7 @@ def bench_prefill(args, cfg):
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "k": cfg.k, "n_sink": cfg.n_sink,
-                   "seg": cfg.seg, "causal": True, "seed": args.seed},
+                   "seg": cfg.seg, "causal": True, "seed": args.seed, "select_algo": args.select_algo},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
                      "kernel": "spa_block_sparse_prefill (prefill attention kernel)",

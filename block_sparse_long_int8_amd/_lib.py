@@ -45,6 +45,9 @@ _SIGS = {
     "spa_index_score_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "spa_select_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "spa_select_topp": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "spa_select_topk_hist": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
+    "spa_select_topp_hist": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f, _f, _i, _i, _vp, _vp, _i, _vp, _sz,
+                                  _vp]),
     "spa_score_select_decode": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _f, _f, _i, _i, _vp,
                                      _vp, _vp, _i, _vp]),
     "spa_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
@@ -175,24 +178,34 @@ def _sel_out(scores, cap, idx, count):
 
 
 def spa_select_topk(scores, blk, n_sink, n_local, k, cap, seq_len=None, prefill=False, q_blk0=0,
-                    idx=None, count=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    idx=None, count=None, algo="sort") -> Tuple[torch.Tensor, torch.Tensor]:
+    """algo "sort" calls spa_select_topk, "hist" spa_select_topk_hist (same result)."""
     _dev(scores, "scores", torch.int32)
     B, M, idx, count = _sel_out(scores, cap, idx, count)
     nKb = scores.shape[-1]
-    st = lib().spa_select_topk(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
-                               k, _ptr(idx), _ptr(count), cap, None, 0, _stream())
-    _check("spa_select_topk", st)
+    name = _sel_name("spa_select_topk", algo)
+    st = getattr(lib(), name)(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
+                              k, _ptr(idx), _ptr(count), cap, None, 0, _stream())
+    _check(name, st)
     return idx, count
 
 
+def _sel_name(base, algo):
+    if algo not in ("sort", "hist"):
+        raise ValueError(f"algo must be 'sort' or 'hist', not {algo!r}")
+    return base if algo == "sort" else base + "_hist"
+
+
 def spa_select_topp(scores, blk, n_sink, n_local, beta, p, k_min, k_max, cap, seq_len=None, prefill=False,
-                    q_blk0=0, idx=None, count=None) -> Tuple[torch.Tensor, torch.Tensor]:
+                    q_blk0=0, idx=None, count=None, algo="sort") -> Tuple[torch.Tensor, torch.Tensor]:
+    """algo "sort" calls spa_select_topp, "hist" spa_select_topp_hist."""
     _dev(scores, "scores", torch.int32)
     B, M, idx, count = _sel_out(scores, cap, idx, count)
     nKb = scores.shape[-1]
-    st = lib().spa_select_topp(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
-                               float(beta), float(p), k_min, k_max, _ptr(idx), _ptr(count), cap, None, 0, _stream())
-    _check("spa_select_topp", st)
+    name = _sel_name("spa_select_topp", algo)
+    st = getattr(lib(), name)(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
+                              float(beta), float(p), k_min, k_max, _ptr(idx), _ptr(count), cap, None, 0, _stream())
+    _check(name, st)
     return idx, count
 
 

@@ -120,7 +120,8 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
                                 int prefill, int mode, int k, float beta, float p, int k_min,
                                 int k_max, int32_t* idx, int32_t* count, int cap, void* stream,
                                 const int8_t* qI = nullptr, const int8_t* kI = nullptr,
-                                const int8_t* w = nullptr, int H = 0, int32_t* scores_out = nullptr) {
+                                const int8_t* w = nullptr, int H = 0, int32_t* scores_out = nullptr,
+                                bool hist = false) {
   REQUIRE(prefill == 0 || prefill == 1, SPA_ERR_INVALID_ARG, "prefill must be 0 or 1 (got %d)", prefill);
   REQUIRE(B >= 0 && M >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG, "negative size");
   REQUIRE(blk >= 1 && n_sink >= 0 && n_local >= 0, SPA_ERR_INVALID_ARG, "need blk >= 1, n_sink >= 0, n_local >= 0");
@@ -167,7 +168,8 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
   a.w = w;
   a.H = H;
   a.scores_out = scores_out;
-  return from_hip(spa::launch_select(a, (hipStream_t)stream), fn);
+  return from_hip(hist ? spa::launch_select_hist(a, (hipStream_t)stream) : spa::launch_select(a, (hipStream_t)stream),
+                  fn);
 }
 
 spa_status spa_score_select_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
@@ -203,6 +205,29 @@ spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_b
   (void)ws_bytes;
   return select_common("spa_select_topp", scores, B, M, nKb, q_blk0, seq_len, blk, n_sink, n_local,
                        prefill, 1, 0, beta, p, k_min, k_max, idx, count, cap, stream);
+}
+
+spa_status spa_select_topk_hist(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                                const int32_t* seq_len, int blk, int n_sink, int n_local,
+                                int prefill, int k, int32_t* idx, int32_t* count, int cap, void* ws,
+                                size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return select_common("spa_select_topk_hist", scores, B, M, nKb, q_blk0, seq_len, blk, n_sink, n_local,
+                       prefill, 0, k, 0.f, 1.f, 0, 0, idx, count, cap, stream, nullptr, nullptr, nullptr, 0,
+                       nullptr, true);
+}
+
+spa_status spa_select_topp_hist(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                                const int32_t* seq_len, int blk, int n_sink, int n_local,
+                                int prefill, float beta, float p, int k_min, int k_max,
+                                int32_t* idx, int32_t* count, int cap, void* ws, size_t ws_bytes,
+                                void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  return select_common("spa_select_topp_hist", scores, B, M, nKb, q_blk0, seq_len, blk, n_sink, n_local,
+                       prefill, 1, 0, beta, p, k_min, k_max, idx, count, cap, stream, nullptr, nullptr, nullptr,
+                       0, nullptr, true);
 }
 
 // ---------------------------------------------------------- decode attention --

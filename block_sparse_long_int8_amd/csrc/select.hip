@@ -255,25 +255,9 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   const int nKb = a.nKb;
 
   // valid blocks, reserved ranges and the candidate range [c0, c1)
-  const int nbv = a.seq_len ? min(nKb, (a.seq_len[b] + a.blk - 1) / a.blk) : nKb;
-  int sink_end, loc0, loc1, diag, c0, c1;
-  if (!a.prefill) {
-    sink_end = min(a.n_sink, nbv);
-    loc0 = max(0, nbv - a.n_local);
-    loc1 = nbv;
-    diag = -1;
-    c0 = a.n_sink;
-    c1 = nbv - a.n_local;
-  } else {
-    const int qa = a.q_blk0 + i;
-    sink_end = min(min(a.n_sink, qa + 1), nKb);
-    loc0 = max(0, qa - a.n_local);
-    loc1 = min(qa, nKb);
-    diag = qa < nKb ? qa : -1;
-    c0 = a.n_sink;
-    c1 = min(min(qa, nbv), qa - a.n_local);
-  }
-  const int n_cand = max(0, c1 - c0);
+  const RowRange rr = row_range(a, b, i);
+  const int nbv = rr.nbv, sink_end = rr.sink_end, loc0 = rr.loc0, loc1 = rr.loc1, diag = rr.diag, c0 = rr.c0;
+  const int n_cand = rr.n_cand;
 
   int sc[EPT];
   int lmax = INT32_MIN, lmin = INT32_MAX;
@@ -397,7 +381,7 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int r = tid * EPT + e;
-      mass[e] = r < n_cand ? expf(a.beta * (float)(rscore[e] - smax)) : 0.f;
+      mass[e] = r < n_cand ? expf(a.beta * (float)((long long)rscore[e] - smax)) : 0.f;
       local += mass[e];
     }
     float Z;

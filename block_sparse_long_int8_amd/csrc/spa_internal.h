@@ -72,8 +72,38 @@ struct SelectArgs {
   int H;
   int32_t* scores_out;  // optional copy of every block's score
 };
-hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);       // bitonic sort of the candidates
+hipError_t launch_select_hist(const SelectArgs& a, hipStream_t s);  // radix threshold search, no sort
 int select_max_blocks();
+
+// Block ranges of selection row (b, i): valid blocks, reserved sink / local /
+// diagonal blocks and the candidate range [c0, c1).
+struct RowRange {
+  int nbv, sink_end, loc0, loc1, diag, c0, c1, n_cand;
+};
+__device__ __forceinline__ RowRange row_range(const SelectArgs& a, int b, int i) {
+  RowRange r;
+  const int nKb = a.nKb;
+  r.nbv = a.seq_len ? min(nKb, (a.seq_len[b] + a.blk - 1) / a.blk) : nKb;
+  if (!a.prefill) {
+    r.sink_end = min(a.n_sink, r.nbv);
+    r.loc0 = max(0, r.nbv - a.n_local);
+    r.loc1 = r.nbv;
+    r.diag = -1;
+    r.c0 = a.n_sink;
+    r.c1 = r.nbv - a.n_local;
+  } else {
+    const int qa = a.q_blk0 + i;
+    r.sink_end = min(min(a.n_sink, qa + 1), nKb);
+    r.loc0 = max(0, qa - a.n_local);
+    r.loc1 = min(qa, nKb);
+    r.diag = qa < nKb ? qa : -1;
+    r.c0 = a.n_sink;
+    r.c1 = min(min(qa, r.nbv), qa - a.n_local);
+  }
+  r.n_cand = max(0, r.c1 - r.c0);
+  return r;
+}
 
 // Decode attention (decode_attn.hip)
 struct DecodeArgs {

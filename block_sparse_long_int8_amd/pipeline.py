@@ -40,6 +40,7 @@ class DecodeSpec:
     local_sink_tok: int = 0
     local_window_tok: int = 0
     out_dtype: torch.dtype = torch.float32
+    select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
 
     @property
     def nb(self) -> int:
@@ -82,9 +83,9 @@ class DecodeStep:
         s = self.spec
         if s.select == "topk":
             return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, seq_len=seq_len,
-                                     idx=self.idx, count=self.count)
+                                     idx=self.idx, count=self.count, algo=s.select_algo)
         return L.spa_select_topp(self.scores, s.blk, s.n_sink, s.n_local, s.beta, s.p, s.k_min, s.k_max, s.cap,
-                                 seq_len=seq_len, idx=self.idx, count=self.count)
+                                 seq_len=seq_len, idx=self.idx, count=self.count, algo=s.select_algo)
 
     def score_select(self, qI, kI, w, seq_len, keep_scores: bool = False):
         """Fused scoring + selection (scores are written only if keep_scores)."""
@@ -145,6 +146,7 @@ class PrefillSpec:
     n_local: int
     seg: int
     out_dtype: torch.dtype = torch.float32
+    select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
 
     @property
     def nb(self) -> int:
@@ -205,7 +207,7 @@ class PrefillStep:
     def select(self):
         s = self.spec
         return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
-                                 count=self.count)
+                                 count=self.count, algo=s.select_algo)
 
     def front(self, qI_tok, kI_tok, w, perm):
         """Permute the indexer inputs, pool, score and select."""

@@ -133,6 +133,32 @@ spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_b
                            int cap, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * spa_select_topk_hist / spa_select_topp_hist -- the same selections without a
+ * sort (arguments, outputs, limits and errors as spa_select_topk /
+ * spa_select_topp).
+ *
+ * RTPurbo page §5 motivates a sort-free threshold for speed.  Rank order is
+ * (score descending, index ascending), so the kept set of size k is every
+ * candidate scoring above the rank-k score plus the lowest-index candidates
+ * scoring equal to it.  Integer scores let a radix search over 256-bin LDS
+ * histograms find that score exactly; top-p accumulates the softmax masses in
+ * fixed point (38 fraction bits per mass, exact sums) and finds the rank at
+ * which the cumulative mass first reaches p times the total.  Top-k lists are
+ * identical to spa_select_topk's; top-p lists can differ from
+ * spa_select_topp's only where a cumulative mass lies within fp32 rounding of
+ * p (the two accumulate in different arithmetic).
+ */
+spa_status spa_select_topk_hist(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                                const int32_t* seq_len, int blk, int n_sink, int n_local,
+                                int prefill, int k, int32_t* idx, int32_t* count, int cap, void* ws,
+                                size_t ws_bytes, void* stream);
+spa_status spa_select_topp_hist(const int32_t* scores, int B, int M, int nKb, int q_blk0,
+                                const int32_t* seq_len, int blk, int n_sink, int n_local,
+                                int prefill, float beta, float p, int k_min, int k_max,
+                                int32_t* idx, int32_t* count, int cap, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
  * spa_score_select_decode -- spa_index_score (decode) and spa_select_topk /
  * spa_select_topp fused into one launch.
  *

@@ -57,8 +57,9 @@ def test_index_score_rejections():
     assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 0) == 0
 
 
-def test_select_rejections():
-    tk = L.spa_select_topk
+@pytest.mark.parametrize("suffix", ["", "_hist"])
+def test_select_rejections(suffix):
+    tk = getattr(L, "spa_select_topk" + suffix)
     # cap smaller than reserved + k
     assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 68, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert b"cap" in L.spa_last_error()
@@ -67,12 +68,14 @@ def test_select_rejections():
     assert tk(_fake(), 1, 1, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tk(_fake(), 1, 1, 5000, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_UNSUPPORTED
     assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, -1, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
-    tp = L.spa_select_topp
+    tp = getattr(L, "spa_select_topp" + suffix)
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 1.5, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 32, 16, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, float("nan"), 0.9, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 16, 512, _fake(3), _fake(4), 516, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(N, 0, 1, 100, 0, N, 64, 1, 4, 0, 0.125, 0.9, 16, 512, N, N, 517, N, 0, N) == S.SPA_OK
+    # null scores with a batch to select
+    assert tk(N, 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
 
 
 def test_decode_attn_rejections():

@@ -46,12 +46,14 @@ def _spec(cfg):
                         local_window_tok=cfg.local_window_tok)
 
 
-@pytest.mark.parametrize("fused", [True, False], ids=["fused", "separate"])
+@pytest.mark.parametrize("path", ["fused", "separate", "separate-hist"])
 @pytest.mark.parametrize("cfg", DECODE_CFGS, ids=[c.name for c in DECODE_CFGS])
-def test_decode_step_parity(cfg, fused):
-    print(f"[decode parity] {cfg.name} fused={fused}", flush=True)
+def test_decode_step_parity(cfg, path):
+    print(f"[decode parity] {cfg.name} {path}", flush=True)
     inp, t = _decode_inputs(cfg)
-    step = S.DecodeStep(_spec(cfg), fused=fused)
+    spec = _spec(cfg)
+    spec.select_algo = "hist" if path.endswith("hist") else "sort"
+    step = S.DecodeStep(spec, fused=path == "fused")
     step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
     torch.cuda.synchronize()
     ref = O.decode_step(inp)
@@ -168,7 +170,8 @@ def test_decode_batch_zero_is_noop():
     assert out.shape == (0, 4, 128)
 
 
-def test_topk_edge_cases():
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+def test_topk_edge_cases(algo):
     # k = 0 keeps only reserved blocks; short sequences keep everything; ties go to the lowest index
     B, nb, blk = 3, 40, 16
     s = np.zeros((B, nb), dtype=np.int32)
@@ -178,30 +181,32 @@ def test_topk_edge_cases():
     sc = dev(s)
     # blocks past the sequence end are never read, whatever they hold
     for k in (0, 2, 5, 100):
-        idx, cnt = S.spa_select_topk(sc, blk, 1, 2, k, 1 + 2 + k, seq_len=dev(L))
+        idx, cnt = S.spa_select_topk(sc, blk, 1, 2, k, 1 + 2 + k, seq_len=dev(L), algo=algo)
         gsel = sel_lists(idx, cnt)
         ref, _ = O.select_decode(s.astype(np.int64), L, blk, 1, 2, "topk", k=k)
         assert gsel == ref, (k, gsel, ref)
 
 
-def test_select_prefill_rows_match_oracle():
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+def test_select_prefill_rows_match_oracle(algo):
     rng = np.random.default_rng(3)
     M, nKb = 70, 70
     s = rng.integers(0, 50, size=(2, M, nKb)).astype(np.int32)   # heavy ties
     for n_sink, n_local, k in ((1, 0, 6), (2, 3, 4), (0, 0, 0)):
         cap = n_sink + n_local + 1 + k
-        idx, cnt = S.spa_select_topk(dev(s), 64, n_sink, n_local, k, cap, prefill=True)
+        idx, cnt = S.spa_select_topk(dev(s), 64, n_sink, n_local, k, cap, prefill=True, algo=algo)
         gsel = sel_lists(idx, cnt)
         ref = O.select_prefill_topk(s.astype(np.int64), n_sink, n_local, k)
         assert gsel == ref
         # a later chunk of rows with q_blk0 > 0
         idx2, cnt2 = S.spa_select_topk(dev(np.ascontiguousarray(s[:, 30:])), 64, n_sink, n_local, k, cap,
-                                       prefill=True, q_blk0=30)
+                                       prefill=True, q_blk0=30, algo=algo)
         ref2 = O.select_prefill_topk(s[:, 30:].astype(np.int64), n_sink, n_local, k, q_blk0=30)
         assert sel_lists(idx2, cnt2) == ref2
 
 
-def test_topp_edge_cases():
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+def test_topp_edge_cases(algo):
     # one-hot -> K_min; p = 1 -> everything up to K_max; equal scores -> lowest indices
     B, nb, blk = 3, 64, 64
     s = np.zeros((B, nb), dtype=np.int32)
@@ -210,11 +215,40 @@ def test_topp_edge_cases():
     L = np.full(B, nb * blk, dtype=np.int32)
     for p, kmin, kmax in ((0.9, 4, 20), (1.0, 0, 64), (0.5, 0, 64)):
         cap = 1 + 4 + kmax
-        idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, 0.125, p, kmin, kmax, cap, seq_len=dev(L))
+        idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, 0.125, p, kmin, kmax, cap, seq_len=dev(L), algo=algo)
         gsel = sel_lists(idx, cnt)
         ref, info = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topp", beta=0.125, p=p, k_min=kmin, k_max=kmax)
         for b in range(B):
             info[b]["reserved"] = O.decode_sets(int(L[b]), blk, 1, 4)[0]
+            check_topp_row(gsel[b], info[b], kmin, kmax, p)
+
+
+@pytest.mark.parametrize("spread", [7, 3000, 2_000_000, 1_500_000_000], ids=["r7", "r3e3", "r2e6", "r1.5e9"])
+def test_select_hist_matches_oracle_across_score_ranges(spread):
+    """The radix threshold search over one to four 8-bit levels picks the oracle's sets.
+
+    Score ranges from 7 (one level, heavy ties) to 1.5e9 (four levels); the
+    rows are ragged and large enough (2048 blocks) for four keys per thread.
+    Top-k must match exactly; top-p by the set rule (the masses are computed
+    with beta scaled so that the softmax stays spread over the range).
+    """
+    rng = np.random.default_rng(spread)
+    B, nb, blk = 6, 2048, 64
+    s = rng.integers(-spread, spread + 1, size=(B, nb)).astype(np.int64)
+    s[1, rng.choice(nb, 40, replace=False)] = spread  # a tied top group
+    s = s.astype(np.int32)
+    L = np.array([nb * blk, nb * blk - 100, 1000 * blk + 7, 300 * blk, 6 * blk, blk], dtype=np.int32)
+    for k in (0, 1, 37, 517):
+        idx, cnt = S.spa_select_topk(dev(s), blk, 1, 4, k, 5 + k, seq_len=dev(L), algo="hist")
+        ref, _ = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topk", k=k)
+        assert sel_lists(idx, cnt) == ref, k
+    beta = 8.0 / spread
+    for p, kmin, kmax in ((0.9, 16, 512), (0.5, 0, 2048), (1.0, 0, 100)):
+        cap = 5 + kmax
+        idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, beta, p, kmin, kmax, cap, seq_len=dev(L), algo="hist")
+        gsel = sel_lists(idx, cnt)
+        ref, info = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topp", beta=beta, p=p, k_min=kmin, k_max=kmax)
+        for b in range(B):
             check_topp_row(gsel[b], info[b], kmin, kmax, p)
 
 

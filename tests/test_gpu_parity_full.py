@@ -57,6 +57,17 @@ def test_full_decode_parity(S, cfg):
     step.attend(q, k.clone(), v.clone(), dev(inp["seq_len"]), dev(inp["head_mode"]))
     torch.cuda.synchronize()
     assert torch.equal(out0, step.out)
+    # the sort-free selection on the same scores
+    if cfg.select == "topk":
+        hidx, hcnt = S.spa_select_topk(step.scores, cfg.blk, cfg.n_sink, cfg.n_local, cfg.k, spec.cap,
+                                       seq_len=dev(inp["seq_len"]), algo="hist")
+        assert sel_lists(hidx, hcnt) == ref["sel"]
+    else:
+        hidx, hcnt = S.spa_select_topp(step.scores, cfg.blk, cfg.n_sink, cfg.n_local, cfg.beta, cfg.p, cfg.k_min,
+                                       cfg.k_max, spec.cap, seq_len=dev(inp["seq_len"]), algo="hist")
+        hsel = sel_lists(hidx, hcnt)
+        for b in range(cfg.B):
+            check_topp_row(hsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
     # the fused scoring + selection launch gives the same scores and selection
     fus = S.DecodeStep(spec, fused=True)
     fus.score_select(dev(inp["qI"]), dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), keep_scores=True)
