@@ -53,6 +53,9 @@ class DecodeConfig:
     local_sink_tok: int = 0
     local_window_tok: int = 0
     seq_lens: Optional[Tuple[int, ...]] = None  # None -> every sequence is full (T)
+    # one selection per KV group from its own indexer heads (H_idx / Hkv each),
+    # with blocks planted per group (SparDA §2, one forecast head per GQA group)
+    per_group: bool = False
 
     @property
     def nb(self) -> int:
@@ -126,6 +129,11 @@ DECODE_64K_HEADSPLIT = DecodeConfig(
     plant_kind="noise", n_plant=(16, 16), plant_mass=0.60, n_retrieval_groups=2,
     local_sink_tok=4, local_window_tok=2048)
 
+DECODE_128K_PERGROUP = DecodeConfig(
+    name="decode_128k_pergroup_bf16", cfg_id=6, B=16, Hq=64, Hkv=8, d=128, T=131072,
+    blk=64, H_idx=8, r=16, dtype="bf16", n_sink=1, n_local=4, select="topk", k=64,
+    plant_kind="copy", n_plant=(8, 32), plant_boost=1.5, per_group=True)
+
 PREFILL_64K = PrefillConfig(
     name="prefill_64k_permuted_bf16", cfg_id=5, B=1, T=65536, Hq=32, Hkv=8, d=128,
     blk=64, H_idx=8, r=16, k=32, n_sink=1, n_local=0, seg=4096)
@@ -149,13 +157,18 @@ SMALL_TINY_RAGGED = replace(
     TINY_DECODE, name="small_tiny_ragged_f32", cfg_id=11, B=2, d=128, Hq=8, Hkv=2,
     seq_lens=(1024, 777))
 
+SMALL_DECODE_PERGROUP = replace(
+    DECODE_32K, name="small_decode_pergroup_bf16", cfg_id=16, B=3, Hq=16, Hkv=4, H_idx=8, T=8192,
+    n_plant=(3, 8), k=10, per_group=True, plant_mass=0.0, plant_boost=1.5, seq_lens=(8192, 5001, 1500))
+
 SMALL_PREFILL = replace(
     PREFILL_64K, name="small_prefill_bf16", cfg_id=15, T=2048, Hq=8, Hkv=2, k=6,
     seg=512)
 
 NAMED = {c.name: c for c in (
     TINY_DECODE, DECODE_32K, DECODE_128K_TOPP, DECODE_64K_HEADSPLIT, PREFILL_64K,
+    DECODE_128K_PERGROUP,
     SMALL_DECODE_TOPK, SMALL_DECODE_TOPP, SMALL_DECODE_HEADSPLIT, SMALL_TINY_RAGGED,
-    SMALL_PREFILL)}
+    SMALL_DECODE_PERGROUP, SMALL_PREFILL)}
 
 BY_ID = {c.cfg_id: c for c in NAMED.values()}

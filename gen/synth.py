@@ -162,7 +162,35 @@ def make_decode_index(cfg: DecodeConfig, seed: int = 0) -> Dict:
     kI = rng_for(seed, cfg.cfg_id, TID_KI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, nb, Hi, r), dtype=np.int8)
     w = rng_for(seed, cfg.cfg_id, TID_W).integers(1, 5, size=(B, Hi), dtype=np.int8)
 
-    # planted blocks, drawn without replacement among the non-reserved blocks
+    # planted blocks, drawn without replacement among the non-reserved blocks;
+    # with per-group selection each KV group gets its own blocks, copied into
+    # its own indexer heads only
+    if cfg.per_group:
+        assert Hi % Hkv == 0, "per-group selection needs H_idx divisible by Hkv"
+        hpg = Hi // Hkv
+        planted_g: List[List[np.ndarray]] = []
+        for b in range(B):
+            nbv = -(-int(seq_len[b]) // blk)
+            cand = np.arange(cfg.n_sink, max(cfg.n_sink, nbv - cfg.n_local))
+            row = []
+            for gq in range(Hkv):
+                g = rng_for(seed, cfg.cfg_id, TID_PLANT, b, gq)
+                lo, hi = cfg.n_plant
+                n = min(int(g.integers(lo, hi + 1)) if hi > lo else lo, len(cand))
+                sel = np.sort(g.choice(cand, n, replace=False)) if n > 0 else np.zeros(0, dtype=np.int64)
+                row.append(sel.astype(np.int32))
+                hs = slice(gq * hpg, (gq + 1) * hpg)
+                if n == 0:
+                    continue
+                if cfg.plant_kind == "copy":
+                    kI[b, sel, hs] = qI[b, hs][None]
+                else:
+                    noise = rng_for(seed, cfg.cfg_id, TID_NOISE, b, gq).integers(-1, 2, size=(n, hpg, r))
+                    kI[b, sel, hs] = np.clip(qI[b, hs][None].astype(np.int16) + noise, -128, 127).astype(np.int8)
+            planted_g.append(row)
+        planted = [np.unique(np.concatenate(row)).astype(np.int32) for row in planted_g]
+        return dict(cfg=cfg, seed=seed, qI=qI, kI=kI, w=w, seq_len=seq_len, head_mode=head_mode,
+                    planted=planted, planted_g=planted_g, ret_groups=ret_groups.astype(np.int32))
     planted: List[np.ndarray] = []
     for b in range(B):
         g = rng_for(seed, cfg.cfg_id, TID_PLANT, b)
@@ -196,11 +224,14 @@ def make_decode(cfg: DecodeConfig, seed: int = 0, threads=None) -> Dict:
     boost = decode_boost(cfg, qf, qbar, ret_groups) if any(len(p) for p in planted) else 0.0
     ret_set = set(int(x) for x in ret_groups)
 
+    planted_g = idx.get("planted_g")
+
     def plant_k(ix, x):
         b, g = ix
-        if g not in ret_set or len(planted[b]) == 0:
+        blocks = planted_g[b][g] if planted_g is not None else planted[b]
+        if g not in ret_set or len(blocks) == 0:
             return
-        rows = (planted[b][:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+        rows = (blocks[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
         rows = rows[rows < T]
         x[rows] += np.float32(boost) * qbar[b, g][None, :]
 

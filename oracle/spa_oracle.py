@@ -21,6 +21,8 @@ What each function follows (page title, section):
   * top-p         -- RTPurbo §3 and SpotAttention §3 (dual top-p): nucleus over
                      the residual distribution (candidates only), stop once the
                      cumulative mass reaches p, floor K_min.
+  * per-group     -- SparDA §2 "Indexador de Pronóstico Compacto": one indexer
+    selection        head (set) per GQA group, each group with its own top-k.
   * attention     -- HGA "Atención Exacta de Token": a standard softmax over
                      exactly the selected tokens; RTPurbo §1 for local heads
                      (sliding window plus sink tokens).
@@ -98,6 +100,30 @@ def score_decode(qI: np.ndarray, kI: np.ndarray, w: np.ndarray, seq_len: np.ndar
         dots = head_dots(qI[b], kI[b, :nbv])              # [nbv, H]
         s = (np.maximum(dots, 0) * w[b].astype(np.int64)[None, :]).sum(axis=1)
         out[b, :nbv] = s
+    assert np.all(np.abs(out[out != INT32_MIN]) < 2 ** 31), "score does not fit int32"
+    return out
+
+
+def score_decode_grouped(qI: np.ndarray, kI: np.ndarray, w: np.ndarray, seq_len: np.ndarray, blk: int,
+                         groups: int) -> np.ndarray:
+    """Per-KV-group decode block scores (SparDA page, "Indexador de Pronóstico
+    Compacto": one forecast head per GQA group instead of one shared selection).
+
+    The H indexer heads are split into ``groups`` equal consecutive sets; group
+    g sums over heads g*H/groups .. (g+1)*H/groups - 1 only:
+    s[b, g, j] = sum_{h in group g} w[b,h] * max(0, qI[b,h,:] . kI[b,j,h,:]).
+    Returns [B, groups, nKb] int64, INT32_MIN past the sequence end.
+    """
+    B, nKb, H = kI.shape[:3]
+    assert H % groups == 0, "indexer heads must split evenly over the groups"
+    hpg = H // groups
+    out = np.full((B, groups, nKb), INT32_MIN, dtype=np.int64)
+    for b in range(B):
+        nbv = min(nKb, -(-int(seq_len[b]) // blk))
+        dots = head_dots(qI[b], kI[b, :nbv])              # [nbv, H]
+        terms = np.maximum(dots, 0) * w[b].astype(np.int64)[None, :]
+        for g in range(groups):
+            out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg].sum(axis=1)
     assert np.all(np.abs(out[out != INT32_MIN]) < 2 ** 31), "score does not fit int32"
     return out
 
@@ -210,6 +236,19 @@ def select_decode(scores, seq_len, blk, n_sink, n_local, mode, k=0, beta=1.0, p=
     return out, info
 
 
+def select_decode_grouped(scores, seq_len, blk, n_sink, n_local, mode, k=0, beta=1.0, p=0.9, k_min=0, k_max=0):
+    """Per-(sequence, KV group) selections: the decode rule applied to each group's scores.
+
+    scores [B, groups, nKb]; returns sel[b][g] (ascending lists) and info[b][g].
+    """
+    B, groups = scores.shape[:2]
+    per = [select_decode(np.ascontiguousarray(scores[:, g]), seq_len, blk, n_sink, n_local, mode, k=k, beta=beta,
+                         p=p, k_min=k_min, k_max=k_max) for g in range(groups)]
+    sel = [[per[g][0][b] for g in range(groups)] for b in range(B)]
+    info = [[per[g][1][b] for g in range(groups)] for b in range(B)]
+    return sel, info
+
+
 def select_prefill_topk(scores, n_sink, n_local, k, q_blk0=0):
     """Per (sequence, query block) selected key-block lists for prefill."""
     B, M = scores.shape[:2]
@@ -248,10 +287,12 @@ def decode_tokens(sel_blocks, seq_len, blk, mode, sink_tok, window_tok) -> np.nd
 
 
 def decode_attention(q, k, v, dtype, seq_len, sel, blk, head_mode=None, sink_tok=0, window_tok=0,
-                     scale=None, heads=None, batches=None):
+                     scale=None, heads=None, batches=None, per_group=False):
     """Sparse decode attention for every (sequence, query head), fp64.
 
     q [B, Hq, d]; k, v [B, Hkv, Tcap, d]; query head h reads KV head h // (Hq/Hkv).
+    sel[b] is the sequence's block list, or with ``per_group`` a list of one
+    block list per KV head (sel[b][g]).
     Returns o [B, Hq, d] and lse [B, Hq] (NaN for rows not computed when
     ``heads``/``batches`` restrict the work).
     """
@@ -267,7 +308,8 @@ def decode_attention(q, k, v, dtype, seq_len, sel, blk, head_mode=None, sink_tok
     for b in (range(B) if batches is None else batches):
         for h in (range(Hq) if heads is None else heads):
             g = h // G
-            toks = decode_tokens(sel[b], seq_len[b], blk, int(head_mode[g]), sink_tok, window_tok)
+            blocks = sel[b][g] if per_group else sel[b]
+            toks = decode_tokens(blocks, seq_len[b], blk, int(head_mode[g]), sink_tok, window_tok)
             K = to_f64(k[b, g, toks], dtype)
             V = to_f64(v[b, g, toks], dtype)
             o[b, h], lse[b, h] = softmax_attend(to_f64(q[b, h], dtype), K, V, scale)
@@ -337,6 +379,17 @@ def segment_permute(x: np.ndarray, perm: np.ndarray, axis: int, inverse: bool = 
 def decode_step(inp: Dict, batches=None, heads=None) -> Dict:
     """Score -> select -> sparse attention for one decode step of a workload dict."""
     cfg = inp["cfg"]
+    if getattr(cfg, "per_group", False):
+        s = score_decode_grouped(inp["qI"], inp["kI"], inp["w"], inp["seq_len"], cfg.blk, cfg.Hkv)
+        if cfg.select == "topk":
+            sel, info = select_decode_grouped(s, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topk", k=cfg.k)
+        else:
+            sel, info = select_decode_grouped(s, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topp",
+                                              beta=cfg.beta, p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max)
+        o, lse = decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], sel, cfg.blk,
+                                  inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok,
+                                  batches=batches, heads=heads, per_group=True)
+        return dict(scores=s, sel=sel, info=info, o=o, lse=lse)
     s = score_decode(inp["qI"], inp["kI"], inp["w"], inp["seq_len"], cfg.blk)
     if cfg.select == "topk":
         sel, info = select_decode(s, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topk", k=cfg.k)

@@ -29,7 +29,7 @@ MUTATIONS = [
     ("scale_dropped", "x = (K @ qv) * scale", "x = (K @ qv)"),
     ("no_normalise", "return (e @ V) / z, float(m + np.log(z))", "return (e @ V), float(m + np.log(z))"),
     ("lse_no_max", "return (e @ V) / z, float(m + np.log(z))", "return (e @ V) / z, float(np.log(z))"),
-    ("gqa_modulo", "            g = h // G\n            toks", "            g = h % Hkv\n            toks"),
+    ("gqa_modulo", "            g = h // G\n            blocks", "            g = h % Hkv\n            blocks"),
     ("prefill_gqa_modulo", "                g = h // G\n                K = to_f64(k[b, g, kslots]",
      "                g = h % Hkv\n                K = to_f64(k[b, g, kslots]"),
     ("causal_strict", "keep = k_pos[kslots] <= pos_u", "keep = k_pos[kslots] < pos_u"),
@@ -44,6 +44,11 @@ MUTATIONS = [
      "    return np.take(x, perm, axis=axis)\n    idx = [slice(None)] * x.ndim"),
     ("bf16_shift", "u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
      "u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(15)"),
+    ("grouped_heads_strided", "out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg].sum(axis=1)",
+     "out[b, g, :nbv] = terms[:, g::groups].sum(axis=1)"),
+    ("grouped_heads_overlap", "out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg].sum(axis=1)",
+     "out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg + 1].sum(axis=1)"),
+    ("per_group_first_list", "blocks = sel[b][g] if per_group else sel[b]", "blocks = sel[b][0] if per_group else sel[b]"),
     ("segment_check_loose", "return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))", "return True"),
 ]
 

@@ -101,6 +101,53 @@ def test_score_prefill_matches_decode_rows_and_mask():
     assert np.array_equal(S2, S[:, 3:])
 
 
+def test_score_grouped_golden():
+    g = gold("score_tiny.json")["grouped"]
+    qI = np.array(g["qI"], dtype=np.int8)[None]
+    kI = np.array(g["kI"], dtype=np.int8)[None]
+    w = np.array(g["w"], dtype=np.int8)[None]
+    for groups in (1, 2, 4):
+        s = O.score_decode_grouped(qI, kI, w, np.array([g["seq_len"]]), g["blk"], groups)
+        assert s[0].tolist() == g[f"expected_groups{groups}"], groups
+    # ragged: the second block lies past a 16-token sequence
+    s = O.score_decode_grouped(qI, kI, w, np.array([16]), g["blk"], 2)
+    assert s[0].tolist() == [[9, O.INT32_MIN], [4, O.INT32_MIN]]
+
+
+def test_score_grouped_partitions_the_shared_score():
+    # the groups partition the indexer heads, so their scores add up to the
+    # shared score, and a single group is the shared score itself
+    rng = np.random.default_rng(14)
+    qI, kI, w = _rand_idx(rng, 3, 21, 8, 16, -128, 127)
+    L = np.array([21 * 32, 400, 33])
+    shared = O.score_decode(qI, kI, w, L, 32)
+    assert np.array_equal(O.score_decode_grouped(qI, kI, w, L, 32, 1)[:, 0], shared)
+    for groups in (2, 4, 8):
+        s = O.score_decode_grouped(qI, kI, w, L, 32, groups)
+        valid = shared != O.INT32_MIN
+        for b in range(3):
+            v = valid[b]
+            assert np.array_equal(s[b][:, v].sum(axis=0), shared[b][v])
+            assert (s[b][:, ~v] == O.INT32_MIN).all()
+
+
+def test_score_grouped_finds_each_groups_planted_blocks():
+    # blocks planted into one group's indexer heads rank first in that group
+    # and carry no signal for the others
+    from gen import SMALL_DECODE_PERGROUP, make_decode_index
+    cfg = SMALL_DECODE_PERGROUP
+    inp = make_decode_index(cfg, seed=0)
+    s = O.score_decode_grouped(inp["qI"], inp["kI"], inp["w"], inp["seq_len"], cfg.blk, cfg.Hkv)
+    sel, _ = O.select_decode_grouped(s, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topk", k=cfg.k)
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            mine = set(int(x) for x in inp["planted_g"][b][g])
+            assert mine and mine <= set(int(x) for x in sel[b][g]), (b, g)
+            others = set().union(*(set(int(x) for x in inp["planted_g"][b][o]) for o in range(cfg.Hkv) if o != g))
+            lo = min(int(s[b, g, j]) for j in mine)
+            assert all(int(s[b, g, j]) < lo for j in others - mine), (b, g)
+
+
 def test_pool_golden():
     g = gold("pool_tiny.json")
     toks = np.array([b["tokens"] for b in g["blocks"]], dtype=np.int8).reshape(1, -1, 1, 1)
@@ -291,6 +338,33 @@ def test_decode_gather_equals_masked_dense_and_set_semantics():
     assert np.allclose(o[0], ref, atol=1e-12)
     o2, _ = O.decode_attention(q, k, v, "f32", np.array([150]), [[9, 0, 4, 3]], blk)
     assert np.allclose(o, o2, atol=1e-13)
+
+
+def test_decode_per_group_lists_route_by_kv_head():
+    # each query head attends over its own KV group's list: equal to masked
+    # dense attention with that group's blocks; identical lists give the
+    # shared-list result
+    rng = np.random.default_rng(15)
+    B, Hq, Hkv, d, T, blk = 2, 6, 3, 16, 160, 16
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    v = rng.standard_normal((B, Hkv, T, d))
+    L = np.array([160, 101])
+    sel = [[[0, 2, 9], [1, 5], [0, 3, 4, 6]], [[6], [0, 1, 2], [2, 4]]]
+    o, lse = O.decode_attention(q, k, v, "f32", L, sel, blk, per_group=True)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            mask = np.full((1, T), -np.inf)
+            for j in sel[b][g]:
+                mask[0, j * blk:min((j + 1) * blk, int(L[b]))] = 0.0
+            ref = _sdpa(q[b, h][None, None], k[b, g][None], v[b, g][None], 1 / 4.0, mask=mask[None])[0, 0]
+            assert np.allclose(o[b, h], ref, atol=1e-12), (b, h)
+    same = [[s0[1]] * Hkv for s0 in sel]
+    o1, l1 = O.decode_attention(q, k, v, "f32", L, same, blk, per_group=True)
+    o2, l2 = O.decode_attention(q, k, v, "f32", L, [s0[1] for s0 in sel], blk)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_kv_permutation_invariance():
