@@ -46,7 +46,8 @@ ROTATE_BYTES = 1 << 30          # bytes one rotation over the copies must touch
 COPY_MEM_LIMIT = 64 << 30       # device bytes all copies together may take
 
 DECODE_METRIC = "sparse-decode tokens/s at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
-WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "tiny_decode", "prefill_64k")
+WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "decode_128k_pergroup", "tiny_decode",
+             "prefill_64k")
 
 
 def log(*a):
@@ -86,7 +87,8 @@ def parse():
 def config_of(name):
     import gen
     return {"decode_128k_topp": gen.DECODE_128K_TOPP, "decode_32k": gen.DECODE_32K,
-            "decode_64k_headsplit": gen.DECODE_64K_HEADSPLIT, "tiny_decode": gen.TINY_DECODE,
+            "decode_64k_headsplit": gen.DECODE_64K_HEADSPLIT, "decode_128k_pergroup": gen.DECODE_128K_PERGROUP,
+            "tiny_decode": gen.TINY_DECODE,
             "prefill_64k": gen.PREFILL_64K}[name]
 
 
@@ -147,20 +149,24 @@ def decode_attn_bytes(cfg, idx, counts, seq_len, head_mode) -> int:
     K and V rows of the tokens each KV group attends (selected blocks clipped
     to the sequence for retrieval groups, sink tokens + window for local
     groups), plus Q, O (fp32), lse (fp32), the block lists and counts.
+    idx/counts hold one list per sequence ([B, cap] / [B]) or, with per-group
+    selection, one per (sequence, KV head) ([B, Hkv, cap] / [B, Hkv]).
     """
     el = 4 if cfg.dtype == "f32" else 2
     row = cfg.d * el
     kv = 0
+    per_group = idx.ndim == 3
     for b in range(cfg.B):
         L = int(seq_len[b])
-        sel_tok = sum(min(cfg.blk, L - int(j) * cfg.blk) for j in idx[b, :counts[b]])
         loc_tok = min(L, cfg.local_sink_tok + cfg.local_window_tok) if cfg.local_window_tok else 0
         for g in range(cfg.Hkv):
+            lst = idx[b, g, :counts[b, g]] if per_group else idx[b, :counts[b]]
+            sel_tok = sum(min(cfg.blk, L - int(j) * cfg.blk) for j in lst)
             kv += 2 * row * (loc_tok if head_mode[g] else sel_tok)
     q = cfg.B * cfg.Hq * cfg.d * el
     o = cfg.B * cfg.Hq * cfg.d * 4
     lse = cfg.B * cfg.Hq * 4
-    lists = int(counts.sum()) * 4 + cfg.B * 4 * 2
+    lists = int(counts.sum()) * 4 + counts.size * 4 + cfg.B * 4
     return kv + q + o + lse + lists
 
 
@@ -206,7 +212,10 @@ def bench_decode(args, cfg):
     spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx,
                         r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta,
                         p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
-                        local_window_tok=cfg.local_window_tok, select_algo=args.select_algo)
+                        local_window_tok=cfg.local_window_tok, select_algo=args.select_algo,
+                        per_group=cfg.per_group)
+    if cfg.per_group and args.select_path == "fused":
+        raise SystemExit("per-group selection has no fused score+select launch; use --select-path separate")
     step = S.DecodeStep(spec, fused=args.select_path == "fused")
     step(base["q"], base["k"], base["v"], base["qI"], base["kI"], base["w"], seq_len, head_mode)
     torch.cuda.synchronize()
@@ -311,6 +320,7 @@ def bench_decode(args, cfg):
                    "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "select": cfg.select, "k": cfg.k, "p": cfg.p,
                    "beta": cfg.beta, "k_min": cfg.k_min, "k_max": cfg.k_max, "n_sink": cfg.n_sink,
                    "n_local": cfg.n_local, "retrieval_groups": int(sum(1 for m in inp["head_mode"] if m == 0)),
+                   "per_group_selection": cfg.per_group,
                    "local_sink_tok": cfg.local_sink_tok, "local_window_tok": cfg.local_window_tok,
                    "input_copies_rotated": copies, "seed": args.seed,
                    "launch": f"hip_graph, {chunk_len} steps per graph" if use_graph else "eager",

@@ -5,11 +5,12 @@ does all the work; this package is its thin ctypes binding plus the two hot
 paths wired as sequences of calls.
 """
 from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORTED, SPA_ERR_WORKSPACE, SPA_F32,
-                   SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, LIB_PATH,
+                   SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, SPA_SCORE_DECODE_GROUPED,
+                   LIB_PATH,
                    SpaError, declared_symbols, lib, spa_block_sparse_prefill, spa_index_score,
                    spa_index_score_workspace_size, spa_score_select_decode, spa_segment_permute, spa_select_topk,
                    spa_select_topp,
-                   spa_sparse_decode_attn, spa_sparse_decode_attn_workspace_size)
+                   spa_sparse_decode_attn, spa_sparse_decode_attn_grouped, spa_sparse_decode_attn_workspace_size)
 from .pipeline import DecodeSpec, DecodeStep, PrefillSpec, PrefillStep
 
 __all__ = [n for n in dir() if not n.startswith("_")]

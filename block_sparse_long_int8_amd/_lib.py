@@ -30,6 +30,7 @@ SPA_BF16 = 1
 SPA_SCORE_DECODE = 0
 SPA_SCORE_PREFILL_POOLED = 1
 SPA_SCORE_PREFILL_TOKENS = 2
+SPA_SCORE_DECODE_GROUPED = 3
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -52,6 +53,8 @@ _SIGS = {
                                      _vp, _vp, _i, _vp]),
     "spa_sparse_decode_attn": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                     _vp, _i, _vp, _vp, _sz, _vp]),
+    "spa_sparse_decode_attn_grouped": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                            _f, _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_sparse_decode_attn_workspace_size": (_sz, [_i, _i, _i, _i]),
     "spa_block_sparse_prefill": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                       _vp, _i, _vp, _vp, _sz, _vp]),
@@ -129,7 +132,10 @@ def spa_index_score_workspace_size(B, H_idx, r, Mq, nKb, mode) -> int:
 
 def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=0, nKb=None, Mq=None,
                     scores=None, ws=None) -> torch.Tensor:
-    """Block scores (int32).  Layouts as in include/spa.h; returns scores."""
+    """Block scores (int32).  Layouts as in include/spa.h; returns scores.
+
+    For SPA_SCORE_DECODE_GROUPED, ``Mq`` is the number of groups (required).
+    """
     _dev(qI, "qI", torch.int8)
     _dev(kI, "kI", torch.int8)
     _dev(w, "w", torch.int8)
@@ -138,6 +144,12 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
         nKb = kI.shape[1]
         Mq = 1
         shape = (B, nKb)
+    elif mode == SPA_SCORE_DECODE_GROUPED:
+        B, H, r = qI.shape
+        nKb = kI.shape[1]
+        if Mq is None:
+            raise ValueError("grouped decode scoring needs Mq (the number of groups)")
+        shape = (B, Mq, nKb)
     else:
         B, _, H, r = qI.shape
         if mode == SPA_SCORE_PREFILL_POOLED:
@@ -238,6 +250,22 @@ def spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d) -> int:
 def spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, idx, count, blk, head_mode=None, local_sink_tok=0,
                            local_window_tok=0, scale=None, out_dtype=torch.float32, out=None, lse=None, ws=None,
                            want_lse=True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One block list per sequence: idx [B, cap], count [B]."""
+    return _decode_attn("spa_sparse_decode_attn", q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
+                        local_sink_tok, local_window_tok, scale, out_dtype, out, lse, ws, want_lse)
+
+
+def spa_sparse_decode_attn_grouped(q, k_cache, v_cache, seq_len, idx, count, blk, head_mode=None,
+                                   local_sink_tok=0, local_window_tok=0, scale=None, out_dtype=torch.float32,
+                                   out=None, lse=None, ws=None,
+                                   want_lse=True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One block list per (sequence, KV head): idx [B, Hkv, cap], count [B, Hkv]."""
+    return _decode_attn("spa_sparse_decode_attn_grouped", q, k_cache, v_cache, seq_len, idx, count, blk,
+                        head_mode, local_sink_tok, local_window_tok, scale, out_dtype, out, lse, ws, want_lse)
+
+
+def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode, local_sink_tok, local_window_tok,
+                 scale, out_dtype, out, lse, ws, want_lse):
     _dev(q, "q")
     _dev(k_cache, "k_cache", q.dtype)
     _dev(v_cache, "v_cache", q.dtype)
@@ -247,6 +275,9 @@ def spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, idx, count, blk, head_m
     B, Hq, d = q.shape
     _, Hkv, Tcap, _ = k_cache.shape
     cap = idx.shape[-1]
+    rows = B * Hkv if name.endswith("_grouped") else B
+    if idx.numel() != rows * cap or count.numel() != rows:
+        raise ValueError(f"{name}: idx must hold {rows} lists of {cap} and count {rows} entries")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -258,11 +289,11 @@ def spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, idx, count, blk, head_m
                          device=q.device)
     if head_mode is not None:
         _dev(head_mode, "head_mode", torch.uint8)
-    st = lib().spa_sparse_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _io_dtype(q), _ptr(seq_len), _ptr(idx),
-                                      _ptr(count), cap, blk, _ptr(head_mode), local_sink_tok, local_window_tok, B, Hq,
-                                      Hkv, d, Tcap, float(scale), _ptr(out), _io_dtype(out), _ptr(lse), _ptr(ws),
-                                      ws.numel(), _stream())
-    _check("spa_sparse_decode_attn", st)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _io_dtype(q), _ptr(seq_len), _ptr(idx),
+                              _ptr(count), cap, blk, _ptr(head_mode), local_sink_tok, local_window_tok, B, Hq, Hkv, d,
+                              Tcap, float(scale), _ptr(out), _io_dtype(out), _ptr(lse), _ptr(ws), ws.numel(),
+                              _stream())
+    _check(name, st)
     return out, lse
 
 

@@ -78,7 +78,8 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
                            int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len, int blk,
                            int mode, int32_t* scores, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "spa_index_score";
-  REQUIRE(mode == SPA_SCORE_DECODE || mode == SPA_SCORE_PREFILL_POOLED || mode == SPA_SCORE_PREFILL_TOKENS,
+  REQUIRE(mode == SPA_SCORE_DECODE || mode == SPA_SCORE_PREFILL_POOLED || mode == SPA_SCORE_PREFILL_TOKENS ||
+              mode == SPA_SCORE_DECODE_GROUPED,
           SPA_ERR_INVALID_ARG, "unknown mode %d", mode);
   REQUIRE(B >= 0 && Mq >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG,
           "negative size (B=%d Mq=%d nKb=%d q_blk0=%d)", B, Mq, nKb, q_blk0);
@@ -86,13 +87,16 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   REQUIRE((long)H_idx * r <= 1024, SPA_ERR_INVALID_ARG, "H_idx*r = %ld exceeds 1024 (int32 scores could overflow)", (long)H_idx * r);
   REQUIRE(blk >= 1, SPA_ERR_INVALID_ARG, "blk must be >= 1 (got %d)", blk);
   if (mode == SPA_SCORE_DECODE) REQUIRE(Mq == 1, SPA_ERR_INVALID_ARG, "decode mode needs Mq == 1 (got %d)", Mq);
+  if (mode == SPA_SCORE_DECODE_GROUPED)
+    REQUIRE(Mq >= 1 && H_idx % Mq == 0, SPA_ERR_INVALID_ARG, "grouped decode needs Mq groups dividing H_idx (Mq=%d H_idx=%d)",
+            Mq, H_idx);
   if (B == 0 || Mq == 0 || nKb == 0) return ok();
   REQUIRE(qI && kI && w && scores, SPA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned16(qI) && aligned16(kI) && aligned16(scores), SPA_ERR_INVALID_ARG, "qI, kI and scores must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  if (mode == SPA_SCORE_DECODE) {
+  if (mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED) {
     REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode mode needs seq_len");
-    return from_hip(spa::launch_score_decode(qI, kI, w, B, H_idx, r, nKb, seq_len, blk, scores, s), fn);
+    return from_hip(spa::launch_score_decode(qI, kI, w, B, H_idx, r, Mq, nKb, seq_len, blk, scores, s), fn);
   }
   REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
   const int8_t* qb = qI;
@@ -125,7 +129,7 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
   REQUIRE(prefill == 0 || prefill == 1, SPA_ERR_INVALID_ARG, "prefill must be 0 or 1 (got %d)", prefill);
   REQUIRE(B >= 0 && M >= 0 && nKb >= 0 && q_blk0 >= 0, SPA_ERR_INVALID_ARG, "negative size");
   REQUIRE(blk >= 1 && n_sink >= 0 && n_local >= 0, SPA_ERR_INVALID_ARG, "need blk >= 1, n_sink >= 0, n_local >= 0");
-  if (!prefill) REQUIRE(M == 1, SPA_ERR_INVALID_ARG, "decode selection needs M == 1 (got %d)", M);
+  if (!prefill && !scores) REQUIRE(M == 1, SPA_ERR_INVALID_ARG, "fused decode selection needs M == 1 (got %d)", M);
   const int budget = mode == 0 ? k : k_max;
   if (mode == 0) {
     REQUIRE(k >= 0, SPA_ERR_INVALID_ARG, "k must be >= 0 (got %d)", k);
@@ -237,13 +241,12 @@ size_t spa_sparse_decode_attn_workspace_size(int B, int Hq, int Hkv, int d) {
   return spa::decode_ws_bytes(B, Hq, Hkv, d, spa::decode_workers());
 }
 
-spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void* v_cache,
-                                  int io_dtype, const int32_t* seq_len, const int32_t* idx,
-                                  const int32_t* count, int cap, int blk, const uint8_t* head_mode,
-                                  int local_sink_tok, int local_window_tok, int B, int Hq, int Hkv,
-                                  int d, int Tcap, float scale, void* out, int out_dtype,
-                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "spa_sparse_decode_attn";
+static spa_status decode_common(const char* fn, int per_group, const void* q, const void* k_cache,
+                                const void* v_cache, int io_dtype, const int32_t* seq_len,
+                                const int32_t* idx, const int32_t* count, int cap, int blk,
+                                const uint8_t* head_mode, int local_sink_tok, int local_window_tok,
+                                int B, int Hq, int Hkv, int d, int Tcap, float scale, void* out,
+                                int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
   REQUIRE(io_dtype == SPA_F32 || io_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown io_dtype %d", io_dtype);
   REQUIRE(out_dtype == SPA_F32 || out_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
   REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && Tcap >= 1, SPA_ERR_INVALID_ARG, "bad sizes (B=%d Hq=%d Hkv=%d d=%d Tcap=%d)", B, Hq, Hkv, d, Tcap);
@@ -274,6 +277,7 @@ spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void
   a.count = count;
   a.cap = cap;
   a.blk = blk;
+  a.per_group = per_group;
   a.head_mode = head_mode;
   a.sink_tok = local_sink_tok;
   a.window_tok = local_window_tok;
@@ -288,6 +292,29 @@ spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void
   a.lse = lse;
   a.ws = ws;
   return from_hip(spa::launch_decode(a, (hipStream_t)stream), fn);
+}
+
+spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                                  int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                  const int32_t* count, int cap, int blk, const uint8_t* head_mode,
+                                  int local_sink_tok, int local_window_tok, int B, int Hq, int Hkv,
+                                  int d, int Tcap, float scale, void* out, int out_dtype,
+                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return decode_common("spa_sparse_decode_attn", 0, q, k_cache, v_cache, io_dtype, seq_len, idx, count,
+                       cap, blk, head_mode, local_sink_tok, local_window_tok, B, Hq, Hkv, d, Tcap, scale,
+                       out, out_dtype, lse, ws, ws_bytes, stream);
+}
+
+spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, const void* v_cache,
+                                          int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                          const int32_t* count, int cap, int blk,
+                                          const uint8_t* head_mode, int local_sink_tok,
+                                          int local_window_tok, int B, int Hq, int Hkv, int d,
+                                          int Tcap, float scale, void* out, int out_dtype, float* lse,
+                                          void* ws, size_t ws_bytes, void* stream) {
+  return decode_common("spa_sparse_decode_attn_grouped", 1, q, k_cache, v_cache, io_dtype, seq_len, idx,
+                       count, cap, blk, head_mode, local_sink_tok, local_window_tok, B, Hq, Hkv, d, Tcap,
+                       scale, out, out_dtype, lse, ws, ws_bytes, stream);
 }
 
 // ----------------------------------------------------------------- prefill --

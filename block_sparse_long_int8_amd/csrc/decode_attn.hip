@@ -103,6 +103,12 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Row of idx / count that lists item (b, g)'s blocks: one list per sequence,
+// or one per (sequence, KV head) with per-group selection.
+__device__ __forceinline__ int list_row(const DecodeArgs& a, int b, int g) {
+  return a.per_group ? b * a.Hkv + g : b;
+}
+
 // Number of 32-token tiles of item (b, g).
 __device__ __forceinline__ int item_tiles(const DecodeArgs& a, int b, int g, int tpb) {
   const int L = a.seq_len[b];
@@ -111,20 +117,20 @@ __device__ __forceinline__ int item_tiles(const DecodeArgs& a, int b, int g, int
     const int wstart = max(ns, L - a.window_tok);
     return (ns + kTile - 1) / kTile + (L - wstart + kTile - 1) / kTile;
   }
-  return a.count[b] * tpb;
+  return a.count[list_row(a, b, g)] * tpb;
 }
 
 // Block indices of a retrieval item, 64 at a time in the lanes of a wave, so
 // a tile's address needs no dependent global load.
 struct IdxWindow {
   int base;  // first block slot held
-  int val;   // lane l holds idx[b, base + l]
+  int val;   // lane l holds the list entry base + l
 };
 
-__device__ __forceinline__ void load_window(const DecodeArgs& a, int b, int base, int cnt, IdxWindow& win) {
+__device__ __forceinline__ void load_window(const DecodeArgs& a, int row, int base, int cnt, IdxWindow& win) {
   const int l = threadIdx.x & (kWave - 1);
   win.base = base;
-  win.val = base + l < cnt ? a.idx[(size_t)b * a.cap + base + l] : 0;
+  win.val = base + l < cnt ? a.idx[(size_t)row * a.cap + base + l] : 0;
 }
 
 // First token and number of valid tokens of tile u of item (b, g).
@@ -143,7 +149,7 @@ __device__ __forceinline__ void tile_info(const DecodeArgs& a, int b, int g, int
     }
   } else {
     const int slot = u / tpb;
-    if (slot - win.base >= kWave) load_window(a, b, slot, cnt, win);
+    if (slot - win.base >= kWave) load_window(a, list_row(a, b, g), slot, cnt, win);
     const int j = __builtin_amdgcn_readlane(win.val, slot - win.base);
     const int sub = u - slot * tpb;
     tok0 = j * a.blk + sub * kTile;
@@ -392,7 +398,7 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item
     } else {
       const int slot = u / tpb;
       const int sub = u - slot * tpb;
-      const int j = a.idx[(size_t)b * a.cap + slot];
+      const int j = a.idx[(size_t)list_row(a, b, g) * a.cap + slot];
       win.tok0 = j * a.blk + sub * kTile;
       win.nvalid = min(min(kTile, a.blk - sub * kTile), L - win.tok0);
     }
@@ -638,9 +644,9 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
     }
     const int L = a.seq_len[b];
     const bool local = a.head_mode && a.head_mode[g];
-    const int cnt = local ? 0 : a.count[b];
+    const int cnt = local ? 0 : a.count[list_row(a, b, g)];
     IdxWindow win;
-    if (!local) load_window(a, b, (t - item_start[item]) / tpb, cnt, win);
+    if (!local) load_window(a, list_row(a, b, g), (t - item_start[item]) / tpb, cnt, win);
     for (int u = t - item_start[item]; u < seg_end - item_start[item]; ++u) {
       int tok0, nvalid;
       tile_info(a, b, g, u, tpb, L, local, cnt, win, tok0, nvalid);

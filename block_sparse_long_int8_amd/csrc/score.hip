@@ -7,7 +7,9 @@
 //
 //  * decode: one lane per (key block, head) for r = 16 (a 16-byte load, four
 //    v_dot4 of 4 MACs each, then a shuffle sum over the block's heads); a
-//    thread-per-block loop handles other r.
+//    thread-per-block loop handles other r.  With per-group selection (SparDA
+//    page, §2 "Indexador de Pronóstico Compacto") the heads split into
+//    consecutive equal groups and each group's sum is a score row of its own.
 //  * prefill: int8 MFMA 32x32x16 -- one MFMA per indexer head covers 32 query
 //    blocks x 32 key blocks with K = r = 16, so no MAC is padding; ReLU and the
 //    head weights are applied per head in the epilogue (the ReLU sits inside
@@ -28,11 +30,12 @@ __device__ __forceinline__ int floor_div_pos(int a, int b) {  // b > 0
 }
 
 // ---------------------------------------------------------------- decode ----
+// scores [B, groups, nKb]; group g sums heads g*H/groups .. (g+1)*H/groups-1.
 // grid: (ceil(nKb / 256), B); block 256.
 __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restrict__ qI,
                                                            const int8_t* __restrict__ kI,
                                                            const int8_t* __restrict__ w, int H,
-                                                           int r, int nKb,
+                                                           int r, int groups, int nKb,
                                                            const int32_t* __restrict__ seq_len,
                                                            int blk, int32_t* __restrict__ scores) {
   __shared__ int q_words[256];  // H*r/4 <= 256
@@ -49,11 +52,12 @@ __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restr
   if (j >= nKb) return;
   const int L = seq_len[b];
   const int nbv = min(nKb, (L + blk - 1) / blk);
-  int32_t* dst = scores + (size_t)b * nKb + j;
+  int32_t* dst = scores + (size_t)b * groups * nKb + j;
   if (j >= nbv) {
-    *dst = INT32_MIN_V;
+    for (int g = 0; g < groups; ++g) dst[(size_t)g * nKb] = INT32_MIN_V;
     return;
   }
+  const int hpg = H / groups;
   const int wpr = r >> 2;  // words per head
   const int8_t* row = kI + ((size_t)b * nKb + j) * HR;
   int total = 0;
@@ -71,6 +75,10 @@ __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restr
           ++h;
           in_head = 0;
           dot = 0;
+          if (h % hpg == 0) {
+            dst[(size_t)(h / hpg - 1) * nKb] = total;
+            total = 0;
+          }
         }
       }
     }
@@ -80,19 +88,23 @@ __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restr
       int dot = 0;
       for (int e = 0; e < wpr; ++e) dot = __builtin_amdgcn_sdot4(q_words[h * wpr + e], roww[h * wpr + e], dot, false);
       total += w_s[h] * max(dot, 0);
+      if ((h + 1) % hpg == 0) {
+        dst[(size_t)(h / hpg) * nKb] = total;
+        total = 0;
+      }
     }
   }
-  *dst = total;
 }
 
 // Fast decode path for r == 16 and a power-of-two H <= 64: one lane per
 // (block, head) loads that head's 16 bytes (the wave reads 1 KB contiguous),
-// four v_dot4 give the head dot, ReLU * w, and H neighbouring lanes sum their
-// heads with xor shuffles.  grid: ceil(B*nKb*H / 256); block 256.
+// four v_dot4 give the head dot, ReLU * w, and each group's 2^log2hpg
+// neighbouring lanes sum their heads with xor shuffles.
+// grid: ceil(B*nKb*H / 256); block 256.
 __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __restrict__ qI,
                                                                const int8_t* __restrict__ kI,
                                                                const int8_t* __restrict__ w, int H,
-                                                               int log2H, int nKb, int B,
+                                                               int log2H, int log2hpg, int nKb, int B,
                                                                const int32_t* __restrict__ seq_len,
                                                                int blk, int32_t* __restrict__ scores) {
   const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -117,8 +129,11 @@ __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __r
       v = (int)w[(size_t)b * H + h] * max(dot, 0);
     }
   }
-  for (int o = 1; o < H; o <<= 1) v += __shfl_xor(v, o, kWave);
-  if (in && h == 0) scores[bj] = valid ? v : INT32_MIN_V;
+  for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
+  if (in && (h & ((1 << log2hpg) - 1)) == 0) {
+    const int groups = H >> log2hpg;
+    scores[((size_t)b * groups + (h >> log2hpg)) * nKb + j] = valid ? v : INT32_MIN_V;
+  }
 }
 
 // --------------------------------------------------------------- pooling ----
@@ -209,18 +224,20 @@ __global__ void __launch_bounds__(64) score_prefill_kernel(const int8_t* __restr
 }  // namespace
 
 hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
-                               int r, int nKb, const int32_t* seq_len, int blk, int32_t* scores,
-                               hipStream_t s) {
+                               int r, int groups, int nKb, const int32_t* seq_len, int blk,
+                               int32_t* scores, hipStream_t s) {
   if (r == 16 && H <= kWave && (H & (H - 1)) == 0) {
-    int log2H = 0;
+    // groups divides a power of two, so the heads per group are one too
+    int log2H = 0, log2hpg = 0;
     while ((1 << log2H) < H) ++log2H;
+    while ((1 << log2hpg) < H / groups) ++log2hpg;
     const long total = (long)B * nKb * H;
-    score_decode_r16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(qI, kI, w, H, log2H, nKb, B,
-                                                                             seq_len, blk, scores);
+    score_decode_r16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(qI, kI, w, H, log2H, log2hpg, nKb,
+                                                                             B, seq_len, blk, scores);
     return hipGetLastError();
   }
   dim3 grid((nKb + 255) / 256, B);
-  score_decode_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, r, nKb, seq_len, blk, scores);
+  score_decode_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, r, groups, nKb, seq_len, blk, scores);
   return hipGetLastError();
 }
 

@@ -43,8 +43,8 @@ struct LaunchStatus {
 
 // Score kernels (score.hip)
 hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
-                               int r, int nKb, const int32_t* seq_len, int blk, int32_t* scores,
-                               hipStream_t s);
+                               int r, int groups, int nKb, const int32_t* seq_len, int blk,
+                               int32_t* scores, hipStream_t s);
 hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok_per_seq, int nblocks,
                               int tok0, int H, int r, int blk, const int32_t* seq_len,
                               int8_t* out, hipStream_t s);
@@ -112,9 +112,10 @@ struct DecodeArgs {
   const void* v;
   int io_bf16;
   const int32_t* seq_len;
-  const int32_t* idx;
-  const int32_t* count;
+  const int32_t* idx;    // [B, cap], or [B, Hkv, cap] when per_group
+  const int32_t* count;  // [B], or [B, Hkv] when per_group
   int cap, blk;
+  int per_group;         // one block list per (sequence, KV head)
   const uint8_t* head_mode;
   int sink_tok, window_tok;
   int B, Hq, Hkv, d, Tcap;

@@ -41,6 +41,7 @@ class DecodeSpec:
     local_window_tok: int = 0
     out_dtype: torch.dtype = torch.float32
     select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
+    per_group: bool = False       # one selection per KV head from its own H_idx/Hkv indexer heads
 
     @property
     def nb(self) -> int:
@@ -61,15 +62,22 @@ class DecodeStep:
     reads the indexer keys with only one workgroup per sequence.  Replayed as a
     HIP graph (``capture``), where launches cost nothing, the separate pair is
     the faster of the two.
+
+    With ``spec.per_group`` every KV head selects its own blocks: grouped
+    scores [B, Hkv, nKb], Hkv selection rows per sequence and
+    spa_sparse_decode_attn_grouped (separate launches only).
     """
 
     def __init__(self, spec: DecodeSpec, device="cuda", fused: bool = False):
         self.spec = s = spec
+        if fused and s.per_group:
+            raise ValueError("the fused score+select launch has no per-group mode")
         self.fused = fused
         dev = torch.device(device)
-        self.scores = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
-        self.idx = torch.empty((s.B, s.cap), dtype=torch.int32, device=dev)
-        self.count = torch.empty((s.B,), dtype=torch.int32, device=dev)
+        rows = (s.B, s.Hkv) if s.per_group else (s.B,)
+        self.scores = torch.empty(rows + (s.nb,), dtype=torch.int32, device=dev)
+        self.idx = torch.empty(rows + (s.cap,), dtype=torch.int32, device=dev)
+        self.count = torch.empty(rows, dtype=torch.int32, device=dev)
         self.out = torch.empty((s.B, s.Hq, s.d), dtype=s.out_dtype, device=dev)
         self.lse = torch.empty((s.B, s.Hq), dtype=torch.float32, device=dev)
         n = L.spa_sparse_decode_attn_workspace_size(s.B, s.Hq, s.Hkv, s.d)
@@ -77,6 +85,9 @@ class DecodeStep:
 
     def score(self, qI, kI, w, seq_len):
         s = self.spec
+        if s.per_group:
+            return L.spa_index_score(qI, kI, w, s.blk, seq_len=seq_len, mode=L.SPA_SCORE_DECODE_GROUPED, Mq=s.Hkv,
+                                     scores=self.scores)
         return L.spa_index_score(qI, kI, w, s.blk, seq_len=seq_len, mode=L.SPA_SCORE_DECODE, scores=self.scores)
 
     def select(self, seq_len):
@@ -97,10 +108,10 @@ class DecodeStep:
 
     def attend(self, q, k_cache, v_cache, seq_len, head_mode=None):
         s = self.spec
-        return L.spa_sparse_decode_attn(q, k_cache, v_cache, seq_len, self.idx, self.count, s.blk,
-                                        head_mode=head_mode, local_sink_tok=s.local_sink_tok,
-                                        local_window_tok=s.local_window_tok, out=self.out, lse=self.lse,
-                                        ws=self.ws)
+        fn = L.spa_sparse_decode_attn_grouped if s.per_group else L.spa_sparse_decode_attn
+        return fn(q, k_cache, v_cache, seq_len, self.idx, self.count, s.blk,
+                  head_mode=head_mode, local_sink_tok=s.local_sink_tok, local_window_tok=s.local_window_tok,
+                  out=self.out, lse=self.lse, ws=self.ws)
 
     def __call__(self, q, k_cache, v_cache, qI, kI, w, seq_len, head_mode=None, keep_scores: bool = False):
         if self.fused:

@@ -3,6 +3,8 @@
  *
  * One decode step of query-dependent block-sparse attention is
  *     spa_index_score -> spa_select_topk | spa_select_topp -> spa_sparse_decode_attn
+ * (with one selection per KV group: spa_index_score (SPA_SCORE_DECODE_GROUPED)
+ * -> spa_select_* with M = Hkv rows per sequence -> spa_sparse_decode_attn_grouped)
  * and one permuted block-sparse prefill is
  *     spa_segment_permute -> spa_index_score (prefill) -> spa_select_topk (prefill)
  *     -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
@@ -48,6 +50,7 @@ typedef int spa_status;
 #define SPA_SCORE_DECODE 0         /* one query row per sequence against its key blocks  */
 #define SPA_SCORE_PREFILL_POOLED 1 /* query blocks x key blocks, block vectors given     */
 #define SPA_SCORE_PREFILL_TOKENS 2 /* as POOLED, per-token vectors pooled by the library */
+#define SPA_SCORE_DECODE_GROUPED 3 /* as DECODE, one score row per group of indexer heads */
 
 /* Human-readable name of a status code (static storage). */
 const char* spa_status_string(spa_status s);
@@ -70,6 +73,11 @@ int spa_version(void);
  * mode SPA_SCORE_DECODE (Mq must be 1):
  *   qI [B, H_idx, r], kI [B, nKb, H_idx, r], w [B, H_idx]  ->  scores [B, nKb].
  *   Blocks j >= ceil(seq_len[b]/blk) get INT32_MIN.  seq_len [B] is required.
+ * mode SPA_SCORE_DECODE_GROUPED (Mq = number of groups, dividing H_idx):
+ *   per-KV-group selection (SparDA page, §2 "Indexador de Pronóstico
+ *   Compacto": one forecast head set per GQA group).  Inputs as DECODE;
+ *   group g sums only heads g*H_idx/Mq .. (g+1)*H_idx/Mq - 1 ->
+ *   scores [B, Mq, nKb], the groups' rows adding up to the DECODE score.
  * mode SPA_SCORE_PREFILL_POOLED:
  *   qI [B, Mq, H_idx, r] are the pooled vectors of query blocks q_blk0..q_blk0+Mq-1,
  *   kI [B, nKb, H_idx, r] the pooled key-block vectors, w [B, Mq, H_idx]
@@ -99,8 +107,10 @@ size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, 
  * and the first min(k, #candidates) are kept.
  *
  * scores [B, M, nKb] int32 (as written by spa_index_score).
- * prefill == 0 (decode, M must be 1): with e = ceil(seq_len[b]/blk) valid blocks,
+ * prefill == 0 (decode): with e = ceil(seq_len[b]/blk) valid blocks,
  *   reserved = {0..n_sink-1} and {e-n_local..e-1}; candidates = the other valid blocks.
+ *   M is 1, or the number of KV groups with per-group scores: the M rows of
+ *   sequence b (row b*M + g) all use seq_len[b].
  * prefill == 1: row i is query block a = q_blk0 + i; reserved = {0..n_sink-1} (those <= a),
  *   {a-n_local..a-1} and the diagonal {a}; candidates = the other blocks j < a.
  *   seq_len may be NULL (then every block below nKb is valid).
@@ -167,7 +177,8 @@ spa_status spa_select_topp_hist(const int32_t* scores, int B, int M, int nKb, in
  * sequence's workgroup computes its blocks' scores from qI [B, H_idx, 16],
  * kI [B, nKb, H_idx, 16] and w [B, H_idx] and selects from them directly, so
  * the scores never travel through HBM.  mode 0 = top-k (uses k), 1 = top-p
- * (uses beta, p, k_min, k_max).  scores_out [B, nKb] may be NULL; when given it
+ * (uses beta, p, k_min, k_max); one row per sequence (no per-group mode).
+ * scores_out [B, nKb] may be NULL; when given it
  * receives every block's score exactly as spa_index_score writes it.
  * Outputs and errors as spa_select_topk / spa_select_topp (decode rows).
  * Supported: r == 16, H_idx a power of two <= 64, nKb <= 4096.
@@ -210,6 +221,25 @@ spa_status spa_sparse_decode_attn(const void* q, const void* k_cache, const void
                                   int d, int Tcap, float scale, void* out, int out_dtype,
                                   float* lse, void* ws, size_t ws_bytes, void* stream);
 size_t spa_sparse_decode_attn_workspace_size(int B, int Hq, int Hkv, int d);
+
+/*
+ * spa_sparse_decode_attn_grouped -- spa_sparse_decode_attn with one block list
+ * per KV head.
+ *
+ * SparDA page, §2 "Indexador de Pronóstico Compacto": each GQA group selects
+ * its own blocks, so the query heads of KV head g attend the tokens of blocks
+ * idx[b, g, 0..count[b, g]-1] (idx [B, Hkv, cap], count [B, Hkv], as
+ * spa_select_* writes them for M = Hkv rows per sequence).  Every other
+ * argument, the outputs, limits, errors and the workspace are those of
+ * spa_sparse_decode_attn.
+ */
+spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, const void* v_cache,
+                                          int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                          const int32_t* count, int cap, int blk,
+                                          const uint8_t* head_mode, int local_sink_tok,
+                                          int local_window_tok, int B, int Hq, int Hkv, int d,
+                                          int Tcap, float scale, void* out, int out_dtype, float* lse,
+                                          void* ws, size_t ws_bytes, void* stream);
 
 /*
  * spa_block_sparse_prefill -- causal attention of a query chunk over selected key blocks.

@@ -51,6 +51,11 @@ def test_index_score_rejections():
     assert f(_fake(), _fake(2), _fake(3), 1, 8, 8, 4, 10, 0, N, 64, 1, _fake(5), N, 0, N) == S.SPA_ERR_UNSUPPORTED
     # per-token prefill without workspace
     assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_WORKSPACE
+    # grouped decode: the groups must divide H_idx
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 3, 10, 0, _fake(4), 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert b"groups" in L.spa_last_error()
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 0, 10, 0, _fake(4), 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     # empty batch is a valid no-op
     assert f(N, N, N, 0, 8, 16, 1, 10, 0, N, 64, 0, N, N, 0, N) == S.SPA_OK
     assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 2) == 2 * 1024 * 128
@@ -63,9 +68,9 @@ def test_select_rejections(suffix):
     # cap smaller than reserved + k
     assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 68, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert b"cap" in L.spa_last_error()
-    # decode rows need M == 1 and seq_len
-    assert tk(_fake(), 1, 2, 100, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    # decode rows need seq_len
     assert tk(_fake(), 1, 1, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tk(_fake(), 1, 8, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tk(_fake(), 1, 1, 5000, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_UNSUPPORTED
     assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, -1, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
     tp = getattr(L, "spa_select_topp" + suffix)
@@ -78,8 +83,9 @@ def test_select_rejections(suffix):
     assert tk(N, 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
 
 
-def test_decode_attn_rejections():
-    f = L.spa_sparse_decode_attn
+@pytest.mark.parametrize("name", ["spa_sparse_decode_attn", "spa_sparse_decode_attn_grouped"])
+def test_decode_attn_rejections(name):
+    f = getattr(L, name)
     args = dict(q=_fake(), k=_fake(2), v=_fake(3), io=S.SPA_BF16, sl=_fake(4), idx=_fake(5), cnt=_fake(6), cap=69,
                 blk=64, hm=N, ns=0, nw=0, B=1, Hq=32, Hkv=8, d=128, T=32768, scale=0.088, out=_fake(7),
                 od=S.SPA_F32, lse=N, ws=_fake(8), wsb=1 << 30, st=N)

@@ -2,6 +2,7 @@
 tails) through the C ABI: scores and top-k bit-exact, top-p by the set rule,
 attention within max|diff| <= 1e-2 and relative L2 <= 2e-3.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -104,6 +105,124 @@ def test_decode_graph_replay(cfg):
         g.replay()
         torch.cuda.synchronize()
         for got, want in zip((step.out, step.lse, step.idx, step.count), ref):
+            assert torch.equal(got, want), f"replay {rep} differs from the eager step"
+
+
+def _pergroup_cfg(select):
+    if select == "topk":
+        return gen.SMALL_DECODE_PERGROUP
+    return dataclasses.replace(gen.SMALL_DECODE_PERGROUP, select="topp", beta=0.05, p=0.9, k_min=2, k_max=24)
+
+
+def _pergroup_check(cfg, inp, step, head_mode=None):
+    """Grouped scores bit-exact, each (sequence, group) list as the oracle's, attention on the GPU lists."""
+    s_ref = O.score_decode_grouped(inp["qI"], inp["kI"], inp["w"], inp["seq_len"], cfg.blk, cfg.Hkv)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), s_ref)
+    if cfg.select == "topk":
+        sel_ref, info = O.select_decode_grouped(s_ref, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topk",
+                                                k=cfg.k)
+    else:
+        sel_ref, info = O.select_decode_grouped(s_ref, inp["seq_len"], cfg.blk, cfg.n_sink, cfg.n_local, "topp",
+                                                beta=cfg.beta, p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max)
+    gsel = sel_lists(step.idx, step.count)           # [b][g]
+    idx_h, cnt_h = step.idx.cpu().numpy(), step.count.cpu().numpy()
+    for b in range(cfg.B):
+        for g in range(cfg.Hkv):
+            assert (idx_h[b, g, cnt_h[b, g]:] == -1).all(), "padding after count must be -1"
+            if cfg.select == "topk":
+                assert gsel[b][g] == sel_ref[b][g], (b, g)
+            else:
+                check_topp_row(gsel[b][g], info[b][g], cfg.k_min, cfg.k_max, cfg.p)
+    hm = inp["head_mode"] if head_mode is None else head_mode
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk, hm,
+                                        cfg.local_sink_tok, cfg.local_window_tok, per_group=True)
+    attn_close(step.out.cpu().numpy(), o_ref)
+    assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
+    return gsel
+
+
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+@pytest.mark.parametrize("select", ["topk", "topp"])
+def test_decode_per_group_parity(select, algo):
+    cfg = _pergroup_cfg(select)
+    print(f"[per-group decode parity] {select} {algo}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    spec = _spec(cfg)
+    spec.per_group = True
+    spec.select_algo = algo
+    step = S.DecodeStep(spec)
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    gsel = _pergroup_check(cfg, inp, step)
+    if select == "topk":
+        # every group finds the blocks planted for it
+        for b in range(cfg.B):
+            for g in range(cfg.Hkv):
+                assert set(inp["planted_g"][b][g].tolist()) <= set(gsel[b][g])
+
+
+def test_decode_per_group_local_heads():
+    # local KV heads ignore their list and read sinks plus the window
+    cfg = dataclasses.replace(gen.SMALL_DECODE_PERGROUP, local_sink_tok=64, local_window_tok=700)
+    inp, t = _decode_inputs(cfg)
+    hm_np = np.array([0, 1, 0, 1], dtype=np.uint8)
+    spec = _spec(cfg)
+    spec.per_group = True
+    step = S.DecodeStep(spec)
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], dev(hm_np))
+    torch.cuda.synchronize()
+    _pergroup_check(cfg, inp, step, head_mode=hm_np)
+
+
+def test_decode_grouped_with_equal_lists_is_the_shared_call():
+    # identical per-group lists: the grouped call splits the work the same way
+    # as the shared-list call and gives bit-identical outputs
+    cfg = gen.SMALL_DECODE_TOPK
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    gidx = step.idx[:, None, :].expand(-1, cfg.Hkv, -1).contiguous()
+    gcnt = step.count[:, None].expand(-1, cfg.Hkv).contiguous()
+    out, lse = S.spa_sparse_decode_attn_grouped(t["q"], t["k"], t["v"], t["seq_len"], gidx, gcnt, cfg.blk,
+                                                head_mode=t["head_mode"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, step.out) and torch.equal(lse, step.lse)
+
+
+@pytest.mark.parametrize("H,r,groups", [(8, 16, 1), (8, 16, 2), (8, 16, 8), (6, 8, 3), (4, 12, 2), (64, 16, 8)])
+def test_scores_decode_grouped(H, r, groups):
+    # both scoring kernels (r = 16 with power-of-two H, and the general loop)
+    rng = np.random.default_rng(H * 100 + r + groups)
+    B, nKb, blk = 3, 300, 32
+    qI = rng.integers(-128, 128, size=(B, H, r), dtype=np.int8)
+    kI = rng.integers(-128, 128, size=(B, nKb, H, r), dtype=np.int8)
+    w = rng.integers(1, 5, size=(B, H), dtype=np.int8)
+    L = np.array([nKb * blk, 4001, 1], dtype=np.int32)
+    got = S.spa_index_score(dev(qI), dev(kI), dev(w), blk, seq_len=dev(L), mode=S.SPA_SCORE_DECODE_GROUPED, Mq=groups)
+    torch.cuda.synchronize()
+    ref = O.score_decode_grouped(qI, kI, w, L, blk, groups)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
+
+
+def test_decode_per_group_graph_replay():
+    cfg = gen.SMALL_DECODE_PERGROUP
+    inp, t = _decode_inputs(cfg)
+    spec = _spec(cfg)
+    spec.per_group = True
+    step = S.DecodeStep(spec)
+    args = (t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    step(*args)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in (step.out, step.lse, step.idx, step.count, step.scores)]
+    g = step.capture(*args)
+    for rep in range(4):
+        for x in (step.out, step.lse, step.idx, step.count, step.scores):
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((step.out, step.lse, step.idx, step.count, step.scores), ref):
             assert torch.equal(got, want), f"replay {rep} differs from the eager step"
 
 

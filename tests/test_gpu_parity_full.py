@@ -1,4 +1,4 @@
-"""GPU parity at the five named workloads' full sizes, in the launch
+"""GPU parity at the named workloads' full sizes, in the launch
 configuration the benchmark uses.  Decode workloads are checked in full
 (the oracle finishes them in seconds); the 64K permuted prefill is checked
 bit-exactly on every score and every selected block list, and on sampled
@@ -74,6 +74,32 @@ def test_full_decode_parity(S, cfg):
     torch.cuda.synchronize()
     assert torch.equal(fus.scores, step.scores)
     assert torch.equal(fus.idx, step.idx) and torch.equal(fus.count, step.count)
+
+
+def test_full_decode_128k_per_group_parity(S):
+    cfg = gen.DECODE_128K_PERGROUP
+    print(f"[full decode parity] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, per_group=True)
+    step = S.DecodeStep(spec)
+    step(dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype), dev(inp["v"], cfg.dtype), dev(inp["qI"]),
+         dev(inp["kI"]), dev(inp["w"]), dev(inp["seq_len"]), dev(inp["head_mode"]))
+    torch.cuda.synchronize()
+    print(f"[full decode parity] {cfg.name}: oracle", flush=True)
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    assert gsel == ref["sel"]
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], per_group=True)
+    ma, rl = attn_close(step.out.cpu().numpy(), o_ref)
+    print(f"[full decode parity] {cfg.name}: max|d| {ma:.2e} rel-L2 {rl:.2e}", flush=True)
+    assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
+    # the sort-free selection on the same grouped scores
+    hidx, hcnt = S.spa_select_topk(step.scores, cfg.blk, cfg.n_sink, cfg.n_local, cfg.k, spec.cap,
+                                   seq_len=dev(inp["seq_len"]), algo="hist")
+    assert sel_lists(hidx, hcnt) == ref["sel"]
 
 
 def test_full_prefill_64k_parity(S):
