@@ -91,6 +91,17 @@ class PrefillConfig:
     idx_lo: int = -128
     idx_hi: int = 127
     dtype: str = "bf16"
+    # heavy-hitter keys (PBS-Attn §3): a fraction of key positions, scattered
+    # uniformly, that every query attends strongly (a shared direction c_g per
+    # KV head: q += hh_q*c, k_hh += hh_k*c) and whose indexer keys copy a
+    # shared indexer direction; 0 = none
+    hh_frac: float = 0.0
+    hh_q: float = 0.7
+    hh_k: float = 0.7
+    # key order: "random" (one uniform permutation per segment) or
+    # "importance" (sorted by the importance of the last query block)
+    perm_kind: str = "random"
+    proxy: int = 64             # proxy queries for the importance (the last block)
 
     @property
     def nb(self) -> int:
@@ -138,6 +149,9 @@ PREFILL_64K = PrefillConfig(
     name="prefill_64k_permuted_bf16", cfg_id=5, B=1, T=65536, Hq=32, Hkv=8, d=128,
     blk=64, H_idx=8, r=16, k=32, n_sink=1, n_local=0, seg=4096)
 
+PREFILL_64K_IMPORTANCE = replace(
+    PREFILL_64K, name="prefill_64k_importance_bf16", cfg_id=7, hh_frac=1 / 64, perm_kind="importance")
+
 # --- small variants: same structure, oracle-friendly sizes, ragged tails ---
 
 SMALL_DECODE_TOPK = replace(
@@ -165,9 +179,13 @@ SMALL_PREFILL = replace(
     PREFILL_64K, name="small_prefill_bf16", cfg_id=15, T=2048, Hq=8, Hkv=2, k=6,
     seg=512)
 
+SMALL_PREFILL_IMPORTANCE = replace(
+    PREFILL_64K_IMPORTANCE, name="small_prefill_importance_bf16", cfg_id=17, T=2048, Hq=8, Hkv=2, k=6,
+    seg=512)
+
 NAMED = {c.name: c for c in (
     TINY_DECODE, DECODE_32K, DECODE_128K_TOPP, DECODE_64K_HEADSPLIT, PREFILL_64K,
-    DECODE_128K_PERGROUP,
+    DECODE_128K_PERGROUP, PREFILL_64K_IMPORTANCE, SMALL_PREFILL_IMPORTANCE,
     SMALL_DECODE_TOPK, SMALL_DECODE_TOPP, SMALL_DECODE_HEADSPLIT, SMALL_TINY_RAGGED,
     SMALL_DECODE_PERGROUP, SMALL_PREFILL)}
 

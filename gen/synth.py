@@ -35,6 +35,7 @@ from .configs import DecodeConfig, PrefillConfig
 
 # tensor ids for the seed sequences
 TID_Q, TID_K, TID_V, TID_QI, TID_KI, TID_W, TID_PLANT, TID_NOISE, TID_GROUPS, TID_PERM = range(1, 11)
+TID_HH, TID_HHDIR, TID_HHIDX = range(11, 14)
 
 
 def rng_for(seed: int, cfg_id: int, tensor_id: int, *chunk: int) -> np.random.Generator:
@@ -242,19 +243,45 @@ def make_decode(cfg: DecodeConfig, seed: int = 0, threads=None) -> Dict:
 
 def make_prefill(cfg: PrefillConfig, seed: int = 0, threads=None) -> Dict:
     B, T, Hq, Hkv, d, blk = cfg.B, cfg.T, cfg.Hq, cfg.Hkv, cfg.d, cfg.blk
-    Hi, r, nb = cfg.H_idx, cfg.r, cfg.nb
-    q = _normal_chunks((B, Hq, T, d), seed, cfg.cfg_id, TID_Q, 2, cfg.dtype, threads)
-    k = _normal_chunks((B, Hkv, T, d), seed, cfg.cfg_id, TID_K, 2, cfg.dtype, threads)
+    Hi, r, nb, G = cfg.H_idx, cfg.r, cfg.nb, cfg.G
+    hh = None
+    q_post = k_post = None
+    if cfg.hh_frac > 0:
+        # heavy hitters: uniform positions per sequence, one shared direction per KV head
+        n_hh = max(1, int(round(cfg.hh_frac * T)))
+        hh = [np.sort(rng_for(seed, cfg.cfg_id, TID_HH, b).choice(T, n_hh, replace=False)) for b in range(B)]
+        c = rng_for(seed, cfg.cfg_id, TID_HHDIR).standard_normal((Hkv, d)).astype(np.float32)
+
+        def q_post(ix, x):
+            x += np.float32(cfg.hh_q) * c[ix[1] // G][None, :]
+
+        def k_post(ix, x):
+            x[hh[ix[0]]] += np.float32(cfg.hh_k) * c[ix[1]][None, :]
+    q = _normal_chunks((B, Hq, T, d), seed, cfg.cfg_id, TID_Q, 2, cfg.dtype, threads, post=q_post)
+    k = _normal_chunks((B, Hkv, T, d), seed, cfg.cfg_id, TID_K, 2, cfg.dtype, threads, post=k_post)
     v = _normal_chunks((B, Hkv, T, d), seed, cfg.cfg_id, TID_V, 2, cfg.dtype, threads)
-    qI_tok = rng_for(seed, cfg.cfg_id, TID_QI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, T, Hi, r), dtype=np.int8)
-    kI_tok = rng_for(seed, cfg.cfg_id, TID_KI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, T, Hi, r), dtype=np.int8)
+    if hh is None:
+        qI_tok = rng_for(seed, cfg.cfg_id, TID_QI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, T, Hi, r),
+                                                            dtype=np.int8)
+        kI_tok = rng_for(seed, cfg.cfg_id, TID_KI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, T, Hi, r),
+                                                            dtype=np.int8)
+    else:
+        # queries share an indexer direction cI (plus half-range noise); heavy-hitter keys copy it
+        cI = rng_for(seed, cfg.cfg_id, TID_HHIDX).integers(-64, 64, size=(Hi, r)).astype(np.int16)
+        qn = rng_for(seed, cfg.cfg_id, TID_QI).integers(-64, 64, size=(B, T, Hi, r)).astype(np.int16)
+        qI_tok = np.clip(qn + cI[None, None], -128, 127).astype(np.int8)
+        kI_tok = rng_for(seed, cfg.cfg_id, TID_KI).integers(cfg.idx_lo, cfg.idx_hi + 1, size=(B, T, Hi, r),
+                                                            dtype=np.int8)
+        for b in range(B):
+            kI_tok[b, hh[b]] = cI.astype(np.int8)[None]
     w = rng_for(seed, cfg.cfg_id, TID_W).integers(1, 5, size=(B, nb, Hi), dtype=np.int8)
     # one independent uniform permutation per segment (PBS-Attn §2)
     perm = np.empty(T, dtype=np.int32)
     for s0 in range(0, T, cfg.seg):
         n = min(cfg.seg, T - s0)
         perm[s0:s0 + n] = s0 + rng_for(seed, cfg.cfg_id, TID_PERM, s0 // cfg.seg).permutation(n)
-    return dict(cfg=cfg, seed=seed, q=q, k=k, v=v, qI_tok=qI_tok, kI_tok=kI_tok, w=w, perm=perm)
+    return dict(cfg=cfg, seed=seed, q=q, k=k, v=v, qI_tok=qI_tok, kI_tok=kI_tok, w=w, perm=perm, hh=hh,
+                seq_len=np.full(B, T, dtype=np.int32))
 
 
 def make(cfg, seed: int = 0, threads=None) -> Dict:

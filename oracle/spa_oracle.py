@@ -29,6 +29,10 @@ What each function follows (page title, section):
   * permutation   -- PBS-Attn §1 (key/value permutation invariance, query
                      equivariance, inverse restores the order) and §2
                      (permutation only inside segments of size S).
+  * importance    -- PBS-Attn §3 "Permutación de Claves Basada en Importancia
+    permutation      Global": the last query block as proxy, mean pooling of
+                     its attention probabilities into one importance per key,
+                     keys sorted by descending importance inside each segment.
 
 Readings where the pages are silent (sentinel values, tie order, pooling
 rounding, reserved counts) are listed at the top of each function.
@@ -360,6 +364,57 @@ def check_segment_perm(perm: np.ndarray, seg: int) -> bool:
     return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))
 
 
+def key_importance(q, k, dtype, seq_len, proxy, scale=None) -> np.ndarray:
+    """Global key importance from a proxy query block (PBS-Attn §3), fp64.
+
+    q [B, Hq, T, d], k [B, Hkv, T, d]; query head h reads KV head h // (Hq/Hkv).
+    Readings: the proxy queries are the last min(proxy, L) tokens before
+    L = seq_len[b], every query head included; each attends causally (keys at
+    positions <= its own) with the softmax of q.k * scale; the importance of key
+    t is the mean of its probability over all (head, proxy query) rows, so the
+    importances of a sequence sum to 1.  Keys at or past L get 0.
+    Returns imp [B, T].
+    """
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    imp = np.zeros((B, T))
+    for b in range(B):
+        L = int(seq_len[b])
+        n = min(proxy, L)
+        u0 = L - n
+        # causal mask of the proxy rows: row i (position u0 + i) sees keys 0 .. u0 + i
+        visible = np.arange(L)[None, :] <= (u0 + np.arange(n))[:, None]
+        for h in range(Hq):
+            x = (to_f64(q[b, h, u0:L], dtype) @ to_f64(k[b, h // G, :L], dtype).T) * scale
+            x = np.where(visible, x, -np.inf)
+            e = np.exp(x - x.max(axis=1, keepdims=True))
+            imp[b, :L] += (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+        imp[b] /= Hq * n
+    return imp
+
+
+def importance_permutation(imp: np.ndarray, seq_len, seg: int) -> np.ndarray:
+    """Segment-wise key order by descending importance (PBS-Attn §3, inside §2's segments).
+
+    perm[b, s*seg + r] is the key at rank r of segment s: the keys below
+    seq_len[b] ordered by importance descending, ties to the lower position;
+    keys at or past seq_len[b] follow in their own order.  Returns [B, T] int64.
+    """
+    B, T = imp.shape
+    perm = np.empty((B, T), dtype=np.int64)
+    for b in range(B):
+        L = int(seq_len[b])
+        for s0 in range(0, T, seg):
+            keys = range(s0, min(s0 + seg, T))
+            valid = sorted((t for t in keys if t < L), key=lambda t: (-imp[b, t], t))
+            tail = [t for t in keys if t >= L]
+            perm[b, s0:s0 + len(keys)] = valid + tail
+    return perm
+
+
 def segment_permute(x: np.ndarray, perm: np.ndarray, axis: int, inverse: bool = False) -> np.ndarray:
     """Forward: dst[t] = src[perm[t]].  Inverse: dst[perm[t]] = src[t].  Along ``axis``."""
     x = np.asarray(x)
@@ -440,6 +495,41 @@ def prefill_step(inp: Dict, front: Dict = None, blocks=None, heads=None) -> Dict
 # --------------------------------------------------------------------------
 # diagnostics (density and attention mass, cf. RTPurbo "Resultados Clave")
 # --------------------------------------------------------------------------
+
+def prefill_block_mass(qp, kp, dtype, q_pos, k_pos, blk, q_blocks, scale=None) -> np.ndarray:
+    """Dense causal attention mass per key block, for chosen query blocks (slot order), fp64.
+
+    qp [Hq, T, d], kp [Hkv, T, d] of one sequence in slot order; q_pos / k_pos
+    the original positions.  For query block i, mass[i, j] is the share of the
+    softmax mass (causal on original positions) that the block's queries put on
+    key block j, averaged over its queries and the query heads.  Used to count
+    the blocks a query block needs for a given coverage (PBS-Attn "Resultados
+    Clave": fewer selected blocks at equal attention coverage).
+    """
+    Hq, T, d = qp.shape
+    G = Hq // kp.shape[0]
+    nb = -(-T // blk)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    out = np.zeros((len(q_blocks), nb))
+    blk_of = np.arange(T) // blk
+    for n, i in enumerate(q_blocks):
+        rows = np.arange(i * blk, min((i + 1) * blk, T))
+        visible = np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[rows][:, None]
+        for h in range(Hq):
+            x = np.where(visible, (to_f64(qp[h, rows], dtype) @ to_f64(kp[h // G], dtype).T) * scale, -np.inf)
+            e = np.exp(x - x.max(axis=1, keepdims=True))
+            p = (e / e.sum(axis=1, keepdims=True)).sum(axis=0)
+            out[n] += np.bincount(blk_of, weights=p, minlength=nb)
+        out[n] /= Hq * len(rows)
+    return out
+
+
+def blocks_for_coverage(mass_row: np.ndarray, coverage: float) -> int:
+    """Fewest key blocks whose mass reaches ``coverage`` (largest blocks first)."""
+    c = np.cumsum(np.sort(np.asarray(mass_row))[::-1])
+    return int(np.searchsorted(c, coverage * c[-1] * (1 - 1e-12)) + 1)
+
 
 def dense_mass(q, k, dtype, seq_len, tokens, heads=None, scale=None) -> np.ndarray:
     """Share of each head's dense softmax mass (over [0, seq_len)) that falls on ``tokens``.

@@ -49,6 +49,12 @@ MUTATIONS = [
     ("grouped_heads_overlap", "out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg].sum(axis=1)",
      "out[b, g, :nbv] = terms[:, g * hpg:(g + 1) * hpg + 1].sum(axis=1)"),
     ("per_group_first_list", "blocks = sel[b][g] if per_group else sel[b]", "blocks = sel[b][0] if per_group else sel[b]"),
+    ("importance_not_causal", "x = np.where(visible, x, -np.inf)\n            e = np.exp(", "x = x\n            e = np.exp("),
+    ("importance_first_block", "        u0 = L - n\n        # causal mask of the proxy", "        u0 = 0\n        # causal mask of the proxy"),
+    ("importance_norm_heads_only", "imp[b] /= Hq * n", "imp[b] /= Hq"),
+    ("importance_gqa_modulo", "to_f64(k[b, h // G, :L], dtype)", "to_f64(k[b, h % Hkv, :L], dtype)"),
+    ("importance_sort_ascending", "key=lambda t: (-imp[b, t], t)", "key=lambda t: (imp[b, t], t)"),
+    ("importance_ties_highest", "key=lambda t: (-imp[b, t], t)", "key=lambda t: (-imp[b, t], -t)"),
     ("segment_check_loose", "return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))", "return True"),
 ]
 

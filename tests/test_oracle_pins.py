@@ -447,6 +447,94 @@ def test_permute_golden_and_inverse():
     assert np.array_equal(x, y)
 
 
+def test_importance_permutation_golden():
+    g = gold("permute_tiny.json")["importance"]
+    perm = O.importance_permutation(np.array([g["imp"]]), np.array([g["seq_len"]]), g["seg"])
+    assert perm[0].tolist() == g["perm"]
+    assert O.check_segment_perm(perm[0], g["seg"])
+
+
+def _importance_inputs(rng, B, Hq, Hkv, T, d):
+    q = rng.standard_normal((B, Hq, T, d))
+    k = rng.standard_normal((B, Hkv, T, d))
+    return q, k
+
+
+def test_key_importance_is_mean_of_sdpa_probabilities():
+    # library special case: attention with V = identity returns the probability rows
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, T, d, proxy = 2, 6, 2, 150, 16, 24
+    q, k = _importance_inputs(rng, B, Hq, Hkv, T, d)
+    L = np.array([150, 97])
+    imp = O.key_importance(q, k, "f32", L, proxy, scale=0.3)
+    G = Hq // Hkv
+    for b in range(B):
+        n = min(proxy, int(L[b]))
+        u0 = int(L[b]) - n
+        mask = np.where(np.arange(L[b])[None, :] <= (u0 + np.arange(n))[:, None], 0.0, -np.inf)
+        P = _sdpa(q[b, :, u0:L[b]], np.repeat(k[b, :, :L[b]], G, axis=0), np.broadcast_to(np.eye(L[b]), (Hq, L[b], L[b])).copy(),
+                  0.3, mask=mask)
+        assert np.allclose(imp[b, :L[b]], P.mean(axis=(0, 1)), atol=1e-14)
+        assert (imp[b, L[b]:] == 0).all()
+        assert abs(imp[b].sum() - 1.0) < 1e-12
+
+
+def test_key_importance_uniform_keys_closed_form():
+    # equal keys: proxy row i (position u0 + i) spreads 1/(u0 + i + 1) over keys 0 .. u0 + i
+    rng = np.random.default_rng(22)
+    T, proxy = 40, 8
+    q = rng.standard_normal((1, 4, T, 8))
+    k = np.broadcast_to(rng.standard_normal(8), (1, 2, T, 8)).copy()
+    imp = O.key_importance(q, k, "f32", np.array([T]), proxy)
+    u0 = T - proxy
+    expect = np.array([sum(1.0 / (u0 + i + 1) for i in range(proxy) if t <= u0 + i) / proxy for t in range(T)])
+    assert np.allclose(imp[0], expect, atol=1e-14)
+
+
+def test_importance_permutation_properties_and_heavy_hitters():
+    from gen import SMALL_PREFILL_IMPORTANCE, make
+    cfg = SMALL_PREFILL_IMPORTANCE
+    inp = make(cfg)
+    imp = O.key_importance(inp["q"], inp["k"], cfg.dtype, inp["seq_len"], cfg.proxy)
+    perm = O.importance_permutation(imp, inp["seq_len"], cfg.seg)
+    assert O.check_segment_perm(perm[0], cfg.seg)
+    for s0 in range(0, cfg.T, cfg.seg):
+        v = imp[0, perm[0, s0:s0 + cfg.seg]]
+        assert (np.diff(v) <= 0).all()
+        # each segment's heavy hitters lead it
+        hh = set(int(t) for t in inp["hh"][0] if s0 <= t < s0 + cfg.seg)
+        assert set(perm[0, s0:s0 + len(hh)].tolist()) == hh
+    # ragged: keys past seq_len stay in place at the segment's end
+    L = np.array([cfg.T - 100])
+    imp2 = O.key_importance(inp["q"], inp["k"], cfg.dtype, L, cfg.proxy)
+    perm2 = O.importance_permutation(imp2, L, cfg.seg)
+    assert perm2[0, L[0]:].tolist() == list(range(L[0], cfg.T))
+    assert O.check_segment_perm(perm2[0], cfg.seg)
+
+
+def test_prefill_block_mass_and_coverage():
+    rng = np.random.default_rng(23)
+    Hq, Hkv, T, d, blk = 4, 2, 96, 8, 16
+    qp = rng.standard_normal((Hq, T, d))
+    kp = rng.standard_normal((Hkv, T, d))
+    pos = np.concatenate([s + rng.permutation(48) for s in (0, 48)])
+    m = O.prefill_block_mass(qp, kp, "f32", pos, pos, blk, [0, 3, 5])
+    assert np.allclose(m.sum(axis=1), 1.0, atol=1e-12)
+    # library: attention onto one-hot block indicators gives the block masses
+    ind = np.zeros((T, T // blk))
+    ind[np.arange(T), np.arange(T) // blk] = 1.0
+    G = Hq // Hkv
+    for n, i in enumerate([0, 3, 5]):
+        rows = np.arange(i * blk, (i + 1) * blk)
+        mask = np.where(pos[None, :] <= pos[rows][:, None], 0.0, -np.inf)
+        P = _sdpa(qp[:, rows], np.repeat(kp, G, axis=0), np.broadcast_to(ind, (Hq, T, T // blk)).copy(),
+                  1 / math.sqrt(d), mask=mask)
+        assert np.allclose(m[n], P.mean(axis=(0, 1)), atol=1e-13)
+    assert O.blocks_for_coverage(np.array([0.5, 0.1, 0.3, 0.1]), 0.8) == 2
+    assert O.blocks_for_coverage(np.array([0.5, 0.1, 0.3, 0.1]), 0.81) == 3
+    assert O.blocks_for_coverage(np.array([0.25, 0.25, 0.25, 0.25]), 1.0) == 4
+
+
 def test_bf16_widening_and_rounding_golden():
     g = gold("bf16_tiny.json")
     for c in g["cases"]:
