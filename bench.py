@@ -47,7 +47,7 @@ COPY_MEM_LIMIT = 64 << 30       # device bytes all copies together may take
 
 DECODE_METRIC = "sparse-decode tokens/s at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
 WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "decode_128k_pergroup", "tiny_decode",
-             "prefill_64k")
+             "prefill_64k", "prefill_64k_importance")
 
 
 def log(*a):
@@ -88,7 +88,7 @@ def config_of(name):
     import gen
     return {"decode_128k_topp": gen.DECODE_128K_TOPP, "decode_32k": gen.DECODE_32K,
             "decode_64k_headsplit": gen.DECODE_64K_HEADSPLIT, "decode_128k_pergroup": gen.DECODE_128K_PERGROUP,
-            "tiny_decode": gen.TINY_DECODE,
+            "tiny_decode": gen.TINY_DECODE, "prefill_64k_importance": gen.PREFILL_64K_IMPORTANCE,
             "prefill_64k": gen.PREFILL_64K}[name]
 
 
@@ -358,6 +358,7 @@ def prefill_pairs(perm, idx, counts, blk) -> int:
 
 def prefill_cpu_baseline(inp, cfg):
     """The CPU oracle on the full front end plus the attention of sampled query blocks, scaled to T."""
+    import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle as O
@@ -365,6 +366,9 @@ def prefill_cpu_baseline(inp, cfg):
     nq = cfg.nb
     sample = list(range(nq // 32, nq, nq // 16))  # 16 evenly spaced query blocks
     t0 = time.perf_counter()
+    if cfg.perm_kind == "importance":
+        imp = O.key_importance(inp["q"], inp["k"], cfg.dtype, inp["seq_len"], cfg.proxy)
+        inp = dict(inp, perm=O.importance_permutation(imp, inp["seq_len"], cfg.seg)[0].astype(np.int32))
     front = O.prefill_front(inp)
     t_front = time.perf_counter() - t0
     t0 = time.perf_counter()
@@ -375,7 +379,8 @@ def prefill_cpu_baseline(inp, cfg):
     t_sample = time.perf_counter() - t0
     t_full = t_front + t_fixed + (t_sample - t_fixed) * nq / len(sample)
     return {"value": cfg.B * cfg.T / t_full, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"oracle front end (permute, pool, score, select) on all {nq} query blocks ({t_front:.2f} s), "
+            "sample": f"oracle front end ({'importance permutation, ' if cfg.perm_kind == 'importance' else ''}"
+                      f"permute, pool, score, select) on all {nq} query blocks ({t_front:.2f} s), "
                       f"Q/K/V permutation ({t_fixed:.2f} s), and fp64 attention of {len(sample)} evenly spaced "
                       f"query blocks ({t_sample - t_fixed:.2f} s) scaled to all {nq}"}
 
@@ -393,33 +398,44 @@ def bench_prefill(args, cfg):
     torch.cuda.set_device(0)
     x = {"q": dev(inp["q"], "bf16"), "k": dev(inp["k"], "bf16"), "v": dev(inp["v"], "bf16"),
          "qI": dev(inp["qI_tok"]), "kI": dev(inp["kI_tok"]), "w": dev(inp["w"]), "perm": dev(inp["perm"])}
+    importance = cfg.perm_kind == "importance"
     spec = S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
-                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, select_algo=args.select_algo)
+                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, select_algo=args.select_algo,
+                         perm_kind="importance" if importance else "given", proxy=cfg.proxy)
     step = S.PrefillStep(spec)
-    step(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], x["perm"])
+    step(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], None if importance else x["perm"])
     torch.cuda.synchronize()
     log(f"[bench] inputs resident: {sum(t.numel() * t.element_size() for t in x.values()) / 2**30:.2f} GiB")
 
-    stages = ("permute_qkv", "permute_index", "pool_score", "select", "attention", "unpermute_o")
+    stages = (("importance_perm",) if importance else ()) + \
+        ("permute_qkv", "permute_index", "pool_score", "select", "attention", "unpermute_o")
 
     def run(ev=None):
-        def mark(j):
+        marks = iter(range(len(stages) + 1))
+
+        def mark():
+            j = next(marks)
             if ev is not None:
                 ev[j].record()
-        mark(0)
-        step.set_perm(x["perm"])
-        step.permute_inputs(x["q"], x["k"], x["v"], x["perm"])
-        mark(1)
-        step.permute_index(x["qI"], x["kI"], x["perm"])
-        mark(2)
+        mark()
+        if importance:
+            perm = step.importance(x["q"], x["k"])
+            mark()
+        else:
+            perm = x["perm"]
+        step.set_perm(perm)
+        step.permute_inputs(x["q"], x["k"], x["v"], perm)
+        mark()
+        step.permute_index(x["qI"], x["kI"], perm)
+        mark()
         step.score(x["w"])
-        mark(3)
+        mark()
         step.select()
-        mark(4)
+        mark()
         step.attend()
-        mark(5)
-        step.unpermute(x["perm"])
-        mark(6)
+        mark()
+        step.unpermute(perm)
+        mark()
 
     for _ in range(args.warmup):
         run()
@@ -438,14 +454,15 @@ def bench_prefill(args, cfg):
     ms_step = total_ms / args.steps
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events")
     # a second pass with events between the stages, for the per-stage breakdown
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
     for i in range(args.steps):
         run(evs[i])
     torch.cuda.synchronize()
     st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
 
     idx, counts = step.idx[0].cpu().numpy(), step.count[0].cpu().numpy()
-    pairs = prefill_pairs(inp["perm"], idx, counts, cfg.blk)
+    used_perm = step.perm[0].cpu().numpy() if importance else inp["perm"]
+    pairs = prefill_pairs(used_perm, idx, counts, cfg.blk)
     flop = 4.0 * cfg.d * cfg.Hq * pairs * cfg.B
     attn_s = st_ms["attention"] * 1e-3
     achieved = flop / attn_s / 1e12
@@ -471,7 +488,9 @@ def bench_prefill(args, cfg):
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "d": cfg.d,
                    "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "k": cfg.k, "n_sink": cfg.n_sink,
-                   "seg": cfg.seg, "causal": True, "seed": args.seed, "select_algo": args.select_algo},
+                   "seg": cfg.seg, "causal": True, "seed": args.seed, "select_algo": args.select_algo,
+                   "permutation": "importance-sorted (last query block as proxy)" if importance
+                   else "uniform random per segment", "heavy_hitter_frac": cfg.hh_frac},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
                      "kernel": "spa_block_sparse_prefill (prefill attention kernel)",
@@ -487,6 +506,15 @@ def bench_prefill(args, cfg):
                     "unpermute_gbs": unperm_bytes / (st_ms["unpermute_o"] * 1e-3) / 1e9},
         "selected_blocks": {"mean": float(counts.mean()), "max": int(counts.max())},
     }
+    if importance:
+        # two passes of S = Q_proxy K^T over every key (4 query heads per wave group), K read twice
+        n_proxy = min(cfg.proxy, cfg.T)
+        imp_flop = 2 * 2.0 * cfg.B * cfg.Hq * n_proxy * cfg.T * cfg.d
+        imp_bytes = 2 * cfg.B * cfg.Hkv * cfg.T * cfg.d * 2
+        t_imp = st_ms["importance_perm"] * 1e-3
+        res["importance"] = {"ms": st_ms["importance_perm"], "flop": imp_flop, "tflops": imp_flop / t_imp / 1e12,
+                             "k_bytes": imp_bytes, "k_gbs": imp_bytes / t_imp / 1e9,
+                             "share_of_step": st_ms["importance_perm"] / sum(st_ms.values())}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         res["cpu_baseline"] = prefill_cpu_baseline(inp, cfg)

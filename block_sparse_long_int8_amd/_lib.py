@@ -59,6 +59,8 @@ _SIGS = {
     "spa_block_sparse_prefill": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                       _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_segment_permute": (_i, [_vp, _vp, _i64, _i, _sz, _vp, _i, _i, _vp]),
+    "spa_importance_permutation": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
+    "spa_importance_permutation_workspace_size": (_sz, [_i, _i, _i]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -338,3 +340,37 @@ def spa_segment_permute(src, perm, seg, dim, inverse=False, dst=None) -> torch.T
                                    _stream())
     _check("spa_segment_permute", st)
     return dst
+
+
+# ------------------------------------------------------ importance permutation --
+
+def spa_importance_permutation_workspace_size(B, Hq, T) -> int:
+    return int(lib().spa_importance_permutation_workspace_size(B, Hq, T))
+
+
+def spa_importance_permutation(q, k, seg, proxy=64, seq_len=None, scale=None, imp=None, perm=None,
+                               ws=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Importance of every key from the last ``proxy`` queries and the segment-wise
+    descending-importance permutation; q [B, Hq, T, d], k [B, Hkv, T, d] bf16.
+    Returns (imp [B, T] fp32, perm [B, T] int32)."""
+    _dev(q, "q", torch.bfloat16)
+    _dev(k, "k", torch.bfloat16)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, T, d):
+        raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
+    if seq_len is not None:
+        _dev(seq_len, "seq_len", torch.int32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if imp is None:
+        imp = torch.empty((B, T), dtype=torch.float32, device=q.device)
+    if perm is None:
+        perm = torch.empty((B, T), dtype=torch.int32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(1, spa_importance_permutation_workspace_size(B, Hq, T)), dtype=torch.uint8,
+                         device=q.device)
+    st = lib().spa_importance_permutation(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, _ptr(seq_len), proxy, float(scale), seg,
+                                          _ptr(imp), _ptr(perm), _ptr(ws), ws.numel(), _stream())
+    _check("spa_importance_permutation", st)
+    return imp, perm

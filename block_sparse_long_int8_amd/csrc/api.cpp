@@ -367,6 +367,38 @@ spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const voi
 
 // ------------------------------------------------------------- permutation --
 
+size_t spa_importance_permutation_workspace_size(int B, int Hq, int T) {
+  if (B <= 0 || Hq <= 0 || T <= 0) return 0;
+  return spa::importance_ws_bytes(B, Hq, T);
+}
+
+spa_status spa_importance_permutation(const void* q, const void* k, int B, int Hq, int Hkv, int T, int d,
+                                      const int32_t* seq_len, int proxy, float scale, int seg, float* imp,
+                                      int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "spa_importance_permutation";
+  REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && T >= 1, SPA_ERR_INVALID_ARG, "bad sizes (B=%d Hq=%d Hkv=%d d=%d T=%d)",
+          B, Hq, Hkv, d, T);
+  REQUIRE(Hq % Hkv == 0, SPA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
+  REQUIRE(std::isfinite(scale) && scale > 0.f, SPA_ERR_INVALID_ARG, "scale must be finite and positive");
+  REQUIRE(seg >= 1, SPA_ERR_INVALID_ARG, "seg must be >= 1 (got %d)", seg);
+  REQUIRE(proxy >= 1, SPA_ERR_INVALID_ARG, "proxy must be >= 1 (got %d)", proxy);
+  REQUIRE(d == 128, SPA_ERR_UNSUPPORTED, "importance supports d == 128 only (got %d)", d);
+  REQUIRE(proxy <= spa::importance_max_proxy(), SPA_ERR_UNSUPPORTED, "proxy %d exceeds %d queries", proxy,
+          spa::importance_max_proxy());
+  REQUIRE(seg <= spa::importance_max_seg(), SPA_ERR_UNSUPPORTED, "seg %d exceeds %d", seg, spa::importance_max_seg());
+  REQUIRE(B <= 65535, SPA_ERR_UNSUPPORTED, "B %d exceeds 65535", B);
+  if (B == 0) return ok();
+  REQUIRE(q && k && imp && perm, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(q) && aligned16(k) && aligned16(imp) && aligned16(perm), SPA_ERR_INVALID_ARG,
+          "tensor pointers must be 16-byte aligned");
+  const size_t need = spa_importance_permutation_workspace_size(B, Hq, T);
+  REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+  REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return from_hip(spa::launch_importance(q, k, B, Hq, Hkv, T, seq_len, proxy, scale, seg, imp, perm, ws,
+                                         (hipStream_t)stream),
+                  fn);
+}
+
 spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
                                const int32_t* perm, int seg, int inverse, void* stream) {
   const char* fn = "spa_segment_permute";

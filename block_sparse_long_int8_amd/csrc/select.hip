@@ -20,6 +20,7 @@
 // prefix whose normalised mass reaches p (clamped to [k_min, k_max]).  A
 // bitmask over block indices then emits the reserved and kept blocks in
 // ascending order with a block-wide prefix count.
+#include "bitonic.h"
 #include "spa_internal.h"
 
 namespace spa {
@@ -85,132 +86,6 @@ __device__ float block_excl_scan_float(float v, float* scratch, float* total) {
   __syncthreads();
   *total = tot;
   return off + (x - v);
-}
-
-__device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m) {
-  const unsigned lo = __shfl_xor((unsigned)v, m, kWave);
-  const unsigned hi = __shfl_xor((unsigned)(v >> 32), m, kWave);
-  return ((unsigned long long)hi << 32) | lo;
-}
-
-// Value of lane (l ^ M) for a compile-time M: DPP lane moves for M <= 8
-// (quad permutes and row / half-row mirrors), a swizzle for 16, a permute for 32.
-template <int M>
-__device__ __forceinline__ unsigned lane_xor(unsigned v) {
-  const int x = (int)v;
-  if constexpr (M == 1) {
-    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
-  } else if constexpr (M == 2) {
-    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-  } else if constexpr (M == 4) {
-    const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);     // half-row mirror: l ^ 7
-    return (unsigned)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);   // quad_perm [3,2,1,0]: ^ 3
-  } else if constexpr (M == 8) {
-    const int r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);     // row mirror: l ^ 15
-    return (unsigned)__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true);  // half-row mirror: ^ 7
-  } else if constexpr (M == 16) {
-    return (unsigned)__builtin_amdgcn_ds_swizzle(x, 0x401F);              // bitmask mode, xor 16
-  } else {
-    return (unsigned)__shfl_xor(x, M, kWave);
-  }
-}
-
-// One compare-exchange stage (k, j) of a descending bitonic sort on 32-bit
-// keys, EPT keys per thread (thread t owns elements t*EPT .. t*EPT+EPT-1).
-template <int EPT, int K, int J>
-__device__ __forceinline__ void stage32(unsigned (&x)[EPT], unsigned* lds, int tid) {
-  if constexpr (J < EPT) {
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      if ((i ^ J) > i) {
-        const int e = tid * EPT + i;
-        const bool desc = (e & K) == 0;
-        const unsigned lo = x[i], hi = x[i ^ J];
-        const unsigned mx = lo > hi ? lo : hi, mn = lo > hi ? hi : lo;
-        x[i] = desc ? mx : mn;
-        x[i ^ J] = desc ? mn : mx;
-      }
-    }
-  } else if constexpr (J < EPT * kWave) {
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const int e = tid * EPT + i;
-      const unsigned p = lane_xor<J / EPT>(x[i]);
-      const bool take_max = ((e & J) == 0) == ((e & K) == 0);
-      x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] > p ? p : x[i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) lds[tid * EPT + i] = x[i];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const int e = tid * EPT + i;
-      const unsigned p = lds[e ^ J];
-      const bool take_max = ((e & J) == 0) == ((e & K) == 0);
-      x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] > p ? p : x[i]);
-    }
-    __syncthreads();
-  }
-}
-
-template <int EPT, int K, int J>
-__device__ __forceinline__ void merge_steps32(unsigned (&x)[EPT], unsigned* lds, int tid) {
-  stage32<EPT, K, J>(x, lds, tid);
-  if constexpr (J > 1) merge_steps32<EPT, K, J / 2>(x, lds, tid);
-}
-
-template <int EPT, int N, int K>
-__device__ __forceinline__ void bitonic32(unsigned (&x)[EPT], unsigned* lds, int tid) {
-  merge_steps32<EPT, K, K / 2>(x, lds, tid);
-  if constexpr (K < N) bitonic32<EPT, N, K * 2>(x, lds, tid);
-}
-
-// Descending bitonic sort of 64-bit keys (fallback when a row's score range
-// does not fit a 32-bit key); same layout, runtime stage loop.
-template <int EPT>
-__device__ void bitonic64(unsigned long long (&x)[EPT], int n_sort, unsigned long long* lds) {
-  const int tid = threadIdx.x;
-  for (int k = 2; k <= n_sort; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      if (j < EPT) {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const int pi = i ^ j;
-          if (pi > i) {
-            const int e = tid * EPT + i;
-            const bool desc = (e & k) == 0;
-            const unsigned long long lo = x[i], hi = x[pi];
-            if (desc ? (lo < hi) : (lo > hi)) {
-              x[i] = hi;
-              x[pi] = lo;
-            }
-          }
-        }
-      } else if (j < EPT * kWave) {
-        const int lm = j / EPT;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const int e = tid * EPT + i;
-          const unsigned long long p = shfl_xor_u64(x[i], lm);
-          const bool take_max = ((e & j) == 0) == ((e & k) == 0);
-          x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] < p ? x[i] : p);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) lds[tid * EPT + i] = x[i];
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-          const int e = tid * EPT + i;
-          const unsigned long long p = lds[e ^ j];
-          const bool take_max = ((e & j) == 0) == ((e & k) == 0);
-          x[i] = take_max ? (x[i] > p ? x[i] : p) : (x[i] < p ? x[i] : p);
-        }
-        __syncthreads();
-      }
-    }
-  }
 }
 
 // Block-wide maximum of a and of b (one exchange through LDS).

@@ -129,6 +129,14 @@ size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers);
 int decode_workers();  // persistent workers (waves) for the current device
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// Key importance and importance-sorted segment permutation (importance.hip)
+size_t importance_ws_bytes(int B, int Hq, int T);
+int importance_max_proxy();
+int importance_max_seg();
+hipError_t launch_importance(const void* q, const void* k, int B, int Hq, int Hkv, int T,
+                             const int32_t* seq_len, int proxy, float scale, int seg, float* imp,
+                             int32_t* perm, void* ws, hipStream_t s);
+
 // Block-sparse prefill (prefill_attn.hip)
 struct PrefillArgs {
   const void* q;

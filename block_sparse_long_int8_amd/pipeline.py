@@ -158,6 +158,8 @@ class PrefillSpec:
     seg: int
     out_dtype: torch.dtype = torch.float32
     select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
+    perm_kind: str = "given"      # "given" (the caller's permutation) | "importance" (computed per call)
+    proxy: int = 64               # proxy queries of the importance permutation
 
     @property
     def nb(self) -> int:
@@ -169,7 +171,12 @@ class PrefillSpec:
 
 
 class PrefillStep:
-    """Permuted block-sparse prefill of one attention layer (one chunk covering T)."""
+    """Permuted block-sparse prefill of one attention layer (one chunk covering T).
+
+    The permutation is the caller's (``perm`` [T], shared by the batch, or
+    [B, T]) or, with ``spec.perm_kind == "importance"``, computed on the device
+    from Q and K by spa_importance_permutation (one per sequence).
+    """
 
     def __init__(self, spec: PrefillSpec, device="cuda"):
         self.spec = s = spec
@@ -189,25 +196,47 @@ class PrefillStep:
         self.lse_slot = torch.empty((s.B, s.Hq, s.T), dtype=torch.float32, device=dev)
         self.out = torch.empty_like(self.out_slot)
         self.pos = None
+        if s.perm_kind == "importance":
+            self.imp = torch.empty((s.B, s.T), dtype=torch.float32, device=dev)
+            self.perm = torch.empty((s.B, s.T), dtype=torch.int32, device=dev)
+            n = L.spa_importance_permutation_workspace_size(s.B, s.Hq, s.T)
+            self.imp_ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
+        elif s.perm_kind != "given":
+            raise ValueError(f"perm_kind must be 'given' or 'importance', not {s.perm_kind!r}")
+
+    def importance(self, q, k):
+        """Importance-sorted segment permutation of each sequence (PBS-Attn §3) into self.perm."""
+        s = self.spec
+        L.spa_importance_permutation(q, k, s.seg, proxy=s.proxy, imp=self.imp, perm=self.perm, ws=self.imp_ws)
+        return self.perm
 
     def set_perm(self, perm):
         """Positions of the permuted slots (the causal mask uses original positions)."""
         s = self.spec
-        self.pos = perm.reshape(1, -1) if s.B == 1 else perm.reshape(1, -1).expand(s.B, -1).contiguous()
+        if perm.dim() == 2:
+            self.pos = perm
+        else:
+            self.pos = perm.reshape(1, -1) if s.B == 1 else perm.reshape(1, -1).expand(s.B, -1).contiguous()
         return self.pos
+
+    def _permute(self, src, perm, dim, dst, inverse=False):
+        s = self.spec
+        if perm.dim() == 1:
+            return L.spa_segment_permute(src, perm, s.seg, dim=dim, inverse=inverse, dst=dst)
+        for b in range(s.B):  # one permutation per sequence
+            L.spa_segment_permute(src[b], perm[b], s.seg, dim=dim - 1, inverse=inverse, dst=dst[b])
+        return dst
 
     def permute_inputs(self, q, k, v, perm):
         """Q, K, V into slot order (segment-wise permutation along the token axis)."""
-        s = self.spec
-        L.spa_segment_permute(q, perm, s.seg, dim=2, dst=self.qp)
-        L.spa_segment_permute(k, perm, s.seg, dim=2, dst=self.kp)
-        L.spa_segment_permute(v, perm, s.seg, dim=2, dst=self.vp)
+        self._permute(q, perm, 2, self.qp)
+        self._permute(k, perm, 2, self.kp)
+        self._permute(v, perm, 2, self.vp)
 
     def permute_index(self, qI_tok, kI_tok, perm):
         """The per-token indexer vectors into slot order."""
-        s = self.spec
-        L.spa_segment_permute(qI_tok, perm, s.seg, dim=1, dst=self.qIp)
-        L.spa_segment_permute(kI_tok, perm, s.seg, dim=1, dst=self.kIp)
+        self._permute(qI_tok, perm, 1, self.qIp)
+        self._permute(kI_tok, perm, 1, self.kIp)
 
     def score(self, w):
         """Pool the permuted per-token vectors into blocks and score every (query block, past key block)."""
@@ -234,10 +263,11 @@ class PrefillStep:
 
     def unpermute(self, perm):
         """O from slot order back to the original token order."""
-        s = self.spec
-        return L.spa_segment_permute(self.out_slot, perm, s.seg, dim=2, inverse=True, dst=self.out)
+        return self._permute(self.out_slot, perm, 2, self.out, inverse=True)
 
-    def __call__(self, q, k, v, qI_tok, kI_tok, w, perm):
+    def __call__(self, q, k, v, qI_tok, kI_tok, w, perm=None):
+        if self.spec.perm_kind == "importance":
+            perm = self.importance(q, k)
         self.set_perm(perm)
         self.permute_inputs(q, k, v, perm)
         self.front(qI_tok, kI_tok, w, perm)

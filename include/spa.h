@@ -6,8 +6,8 @@
  * (with one selection per KV group: spa_index_score (SPA_SCORE_DECODE_GROUPED)
  * -> spa_select_* with M = Hkv rows per sequence -> spa_sparse_decode_attn_grouped)
  * and one permuted block-sparse prefill is
- *     spa_segment_permute -> spa_index_score (prefill) -> spa_select_topk (prefill)
- *     -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
+ *     [spa_importance_permutation ->] spa_segment_permute -> spa_index_score (prefill)
+ *     -> spa_select_topk (prefill) -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer to a dense row-major array with
@@ -264,6 +264,37 @@ spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const voi
                                     int B, int Hq, int Hkv, int d, int T, float scale, void* out,
                                     int out_dtype, float* lse, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/*
+ * spa_importance_permutation -- importance-sorted segment permutation of the keys.
+ *
+ * PBS-Attn page, §3 "Permutación de Claves Basada en Importancia Global": the
+ * last query block is a proxy for all queries; its attention probabilities,
+ * mean-pooled over the proxy queries and all query heads, give one global
+ * importance per key; inside each segment of seg tokens (§2) the keys are
+ * ordered by descending importance, so heavy-hitter keys fill the first
+ * blocks of their segment.
+ *
+ * q [B, Hq, T, d] and k [B, Hkv, T, d] bf16 in natural token order; query head h
+ * reads KV head h / (Hq/Hkv).  With L = seq_len[b] (NULL = T for every
+ * sequence; 1 <= L <= T) the proxy rows are the n = min(proxy, L) queries at
+ * positions L-n .. L-1, each attending keys at positions <= its own with
+ * softmax(scale * q.k).
+ * Outputs: imp [B, T] fp32, the mean probability of each key over the Hq*n
+ * proxy rows (0 for keys at or past L; a sequence's importances sum to 1);
+ * perm [B, T] int32, for segment s the keys s*seg .. below L in order of
+ * importance (descending, equal importances by position), then the keys at or
+ * past L in their own order -- perm[b] maps every segment onto itself and is
+ * the forward permutation of spa_segment_permute.
+ * The order is decided on the fp32 importances as written to imp.
+ * scale > 0 multiplies q.k (normally 1/sqrt(d)).
+ * Supported: d == 128, 1 <= proxy <= 64, 1 <= seg <= 4096.
+ * Workspace: spa_importance_permutation_workspace_size(B, Hq, T) bytes.
+ */
+spa_status spa_importance_permutation(const void* q, const void* k, int B, int Hq, int Hkv, int T, int d,
+                                      const int32_t* seq_len, int proxy, float scale, int seg, float* imp,
+                                      int32_t* perm, void* ws, size_t ws_bytes, void* stream);
+size_t spa_importance_permutation_workspace_size(int B, int Hq, int T);
 
 /*
  * spa_segment_permute -- gather or scatter rows through a segment-wise permutation.

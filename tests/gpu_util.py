@@ -55,3 +55,40 @@ def check_topp_row(gpu_sel, info, k_min, k_max, p, tol=1e-5):
     assert k_min <= lo and hi <= k_max, (kg, ko)
     for t in range(max(0, lo - 1), hi - 1):
         assert abs(cum[t] - p) <= tol, f"rank {t}: cumulative mass {cum[t]!r} not within {tol} of p (gpu {kg}, oracle {ko})"
+
+
+def imp_close(imp_gpu: np.ndarray, imp_ref: np.ndarray, rel=1e-4):
+    """Importance tolerance: |diff| <= rel * |ref| + 1e-12 per key (fp32 softmax over bf16 products)."""
+    g = np.asarray(imp_gpu, dtype=np.float64)
+    r = np.asarray(imp_ref, dtype=np.float64)
+    bad = np.abs(g - r) > rel * np.abs(r) + 1e-12
+    assert not bad.any(), f"{int(bad.sum())} importances out of tolerance, worst at {np.argmax(np.abs(g - r))}"
+
+
+def check_importance_perm(perm_gpu, imp_gpu, imp_ref, seq_len, seg, rel=1e-4):
+    """The GPU permutation of one sequence: every segment maps onto itself; the
+    valid keys are sorted by the GPU's own importances (descending, equal values
+    by position) and the keys past seq_len follow in order; measured with the
+    oracle's importances the order may invert only pairs whose importances agree
+    within the tolerance.  Returns the number of positions that differ from a
+    sort by the oracle's importances."""
+    perm = np.asarray(perm_gpu, dtype=np.int64)
+    T = perm.shape[0]
+    L = int(seq_len)
+    assert np.array_equal(np.sort(perm), np.arange(T)), "not a permutation"
+    assert np.all(perm // seg == np.arange(T) // seg), "permutation leaves its segment"
+    differ = 0
+    for s0 in range(0, T, seg):
+        idx = perm[s0:min(s0 + seg, T)]
+        valid = idx[idx < L]
+        assert np.array_equal(idx[len(valid):], np.arange(max(L, s0), min(s0 + seg, T))), "tail out of order"
+        assert np.all(idx[:len(valid)] < L), "a key past seq_len precedes a valid key"
+        vg = np.asarray(imp_gpu, dtype=np.float64)[valid]
+        assert np.all((vg[:-1] > vg[1:]) | ((vg[:-1] == vg[1:]) & (valid[:-1] < valid[1:]))), "not sorted by imp"
+        vr = np.asarray(imp_ref, dtype=np.float64)[valid]
+        # oracle importances along the GPU order never rise by more than the tolerance
+        run_min = np.minimum.accumulate(vr)
+        assert np.all(vr <= run_min + 2 * rel * np.abs(vr) + 1e-12), "order inverted beyond the tolerance"
+        ref_order = np.array(sorted(valid.tolist(), key=lambda t: (-imp_ref[t], t)))
+        differ += int((ref_order != valid).sum())
+    return differ

@@ -148,3 +148,28 @@ def test_score_select_rejections():
     assert f(*b) == S.SPA_ERR_INVALID_ARG                      # decode rows need seq_len
     b = list(base); b[3] = 0
     assert f(*b) == S.SPA_OK                                   # empty batch
+
+
+def test_importance_permutation_rejections():
+    f = L.spa_importance_permutation
+    base = dict(q=_fake(), k=_fake(2), B=1, Hq=32, Hkv=8, T=4096, d=128, sl=N, proxy=64, scale=0.088, seg=4096,
+                imp=_fake(3), perm=_fake(4), ws=_fake(5), wsb=1 << 30, st=N)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(d=64) == S.SPA_ERR_UNSUPPORTED
+    assert call(proxy=65) == S.SPA_ERR_UNSUPPORTED
+    assert call(proxy=0) == S.SPA_ERR_INVALID_ARG
+    assert call(seg=8192) == S.SPA_ERR_UNSUPPORTED
+    assert call(seg=0) == S.SPA_ERR_INVALID_ARG
+    assert call(Hq=30) == S.SPA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == S.SPA_ERR_INVALID_ARG
+    assert call(scale=-0.5) == S.SPA_ERR_INVALID_ARG
+    assert call(ws=N) == S.SPA_ERR_WORKSPACE
+    assert call(wsb=1024) == S.SPA_ERR_WORKSPACE
+    assert call(perm=N) == S.SPA_ERR_INVALID_ARG
+    assert call(k=ctypes.c_void_p(0x2008)) == S.SPA_ERR_INVALID_ARG
+    assert call(B=0) == S.SPA_OK
+    assert L.spa_importance_permutation_workspace_size(1, 32, 65536) >= 32 * 65536 * 4

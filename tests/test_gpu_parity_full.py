@@ -10,7 +10,7 @@ import torch
 
 import gen
 import oracle as O
-from gpu_util import attn_close, check_topp_row, dev, sel_lists
+from gpu_util import attn_close, check_importance_perm, check_topp_row, dev, imp_close, sel_lists
 
 pytestmark = pytest.mark.gpu
 
@@ -129,4 +129,40 @@ def test_full_prefill_64k_parity(S):
     attn_close(o_slot[:, :, slots], ref["o_slot"][:, :, slots])
     # the inverse permutation puts slot t at original position perm[t]
     o_final = out[:, :, torch.from_numpy(perm[slots]).long().cuda()].cpu().numpy()
+    assert np.array_equal(o_final, o_slot[:, :, slots])
+
+
+def test_full_prefill_64k_importance_parity(S):
+    """The importance-permuted 64K prefill: importances against fp64, the
+    permutation by the near-tie rule, then every score and block list, and
+    sampled attention blocks, downstream of that permutation."""
+    cfg = gen.PREFILL_64K_IMPORTANCE
+    print(f"[full prefill parity] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    step = S.PrefillStep(S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk,
+                                       H_idx=cfg.H_idx, r=cfg.r, k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                                       seg=cfg.seg, perm_kind="importance", proxy=cfg.proxy))
+    out = step(dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"), dev(inp["qI_tok"]),
+               dev(inp["kI_tok"]), dev(inp["w"]))
+    torch.cuda.synchronize()
+    print(f"[full prefill parity] {cfg.name}: oracle importance", flush=True)
+    imp_ref = O.key_importance(inp["q"], inp["k"], cfg.dtype, inp["seq_len"], cfg.proxy)
+    imp_g = step.imp.cpu().numpy()
+    imp_close(imp_g, imp_ref)
+    perm_g = step.perm.cpu().numpy()[0]
+    differ = check_importance_perm(perm_g, imp_g[0], imp_ref[0], cfg.T, cfg.seg)
+    perm_ref = O.importance_permutation(imp_ref, inp["seq_len"], cfg.seg)[0]
+    print(f"[full prefill parity] {cfg.name}: {differ} positions differ from the oracle order", flush=True)
+    use = perm_ref if differ == 0 else perm_g
+    inp2 = dict(inp, perm=use.astype(np.int32))
+    print(f"[full prefill parity] {cfg.name}: oracle front end", flush=True)
+    front = O.prefill_front(inp2)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
+    assert sel_lists(step.idx, step.count) == front["sel"]
+    blocks = [0, 1, 63, 64, 512, 1023]
+    ref = O.prefill_step(inp2, front=front, blocks=blocks)
+    slots = np.concatenate([np.arange(i * cfg.blk, (i + 1) * cfg.blk) for i in blocks])
+    o_slot = step.out_slot.cpu().numpy()
+    attn_close(o_slot[:, :, slots], ref["o_slot"][:, :, slots])
+    o_final = out[:, :, torch.from_numpy(use[slots]).long().cuda()].cpu().numpy()
     assert np.array_equal(o_final, o_slot[:, :, slots])
