@@ -56,6 +56,8 @@ class DecodeConfig:
     # one selection per KV group from its own indexer heads (H_idx / Hkv each),
     # with blocks planted per group (SparDA §2, one forecast head per GQA group)
     per_group: bool = False
+    # selector key cache held as micro-scaled int4 (SpotAttention §4)
+    selector_q4: bool = False
 
     @property
     def nb(self) -> int:
@@ -145,6 +147,8 @@ DECODE_128K_PERGROUP = DecodeConfig(
     blk=64, H_idx=8, r=16, dtype="bf16", n_sink=1, n_local=4, select="topk", k=64,
     plant_kind="copy", n_plant=(8, 32), plant_boost=1.5, per_group=True)
 
+DECODE_128K_TOPP_Q4 = replace(DECODE_128K_TOPP, name="decode_128k_topp_q4_bf16", cfg_id=8, selector_q4=True)
+
 PREFILL_64K = PrefillConfig(
     name="prefill_64k_permuted_bf16", cfg_id=5, B=1, T=65536, Hq=32, Hkv=8, d=128,
     blk=64, H_idx=8, r=16, k=32, n_sink=1, n_local=0, seg=4096)
@@ -175,6 +179,8 @@ SMALL_DECODE_PERGROUP = replace(
     DECODE_32K, name="small_decode_pergroup_bf16", cfg_id=16, B=3, Hq=16, Hkv=4, H_idx=8, T=8192,
     n_plant=(3, 8), k=10, per_group=True, plant_mass=0.0, plant_boost=1.5, seq_lens=(8192, 5001, 1500))
 
+SMALL_DECODE_TOPP_Q4 = replace(SMALL_DECODE_TOPP, name="small_decode_topp_q4_bf16", cfg_id=18, selector_q4=True)
+
 SMALL_PREFILL = replace(
     PREFILL_64K, name="small_prefill_bf16", cfg_id=15, T=2048, Hq=8, Hkv=2, k=6,
     seg=512)
@@ -185,7 +191,8 @@ SMALL_PREFILL_IMPORTANCE = replace(
 
 NAMED = {c.name: c for c in (
     TINY_DECODE, DECODE_32K, DECODE_128K_TOPP, DECODE_64K_HEADSPLIT, PREFILL_64K,
-    DECODE_128K_PERGROUP, PREFILL_64K_IMPORTANCE, SMALL_PREFILL_IMPORTANCE,
+    DECODE_128K_PERGROUP, PREFILL_64K_IMPORTANCE, SMALL_PREFILL_IMPORTANCE, DECODE_128K_TOPP_Q4,
+    SMALL_DECODE_TOPP_Q4,
     SMALL_DECODE_TOPK, SMALL_DECODE_TOPP, SMALL_DECODE_HEADSPLIT, SMALL_TINY_RAGGED,
     SMALL_DECODE_PERGROUP, SMALL_PREFILL)}
 

@@ -29,6 +29,9 @@ What each function follows (page title, section):
   * permutation   -- PBS-Attn §1 (key/value permutation invariance, query
                      equivariance, inverse restores the order) and §2
                      (permutation only inside segments of size S).
+  * int4 selector -- SpotAttention §4 "Cuantización": the selector's key cache
+    keys             in micro-scaled int4 (one scale per r-vector), scored
+                     with the dequantized keys.
   * importance    -- PBS-Attn §3 "Permutación de Claves Basada en Importancia
     permutation      Global": the last query block as proxy, mean pooling of
                      its attention probabilities into one importance per key,
@@ -83,6 +86,42 @@ def pool_blocks(x_tok: np.ndarray, blk: int) -> np.ndarray:
         m = np.floor_divide(2 * s + n, 2 * n)
         out[:, j] = m.astype(np.int8)
     return out
+
+
+def quantize_selector_keys(kI: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Micro-scaled int4 selector keys (SpotAttention §4, quantised selector K cache).
+
+    Readings: one micro-block per r-vector (one key block and indexer head);
+    its scale is a power of two 2^e so that code * 2^e stays an exact integer
+    and the scores stay exact; e is the smallest exponent for which every
+    element's floor(x / 2^e + 1/2) lies in the int4 range [-8, 7], and that
+    value is the element's code.  kI [..., r] int8 -> codes [..., r] int8 in
+    [-8, 7], exps [...] uint8 in [0, 5].
+    """
+    x = np.asarray(kI).astype(np.int64)
+    codes = np.zeros(x.shape, dtype=np.int8)
+    exps = np.full(x.shape[:-1], 255, dtype=np.uint8)
+    todo = np.ones(x.shape[:-1], dtype=bool)
+    for e in range(8):
+        c = np.floor_divide(2 * x + 2 ** e, 2 ** (e + 1))   # floor(x / 2^e + 1/2)
+        ok = todo & (c.min(axis=-1) >= -8) & (c.max(axis=-1) <= 7)
+        codes[ok] = c[ok]
+        exps[ok] = e
+        todo &= ~ok
+    assert not todo.any()
+    return codes, exps
+
+
+def dequantize_selector_keys(codes: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """code * 2^e as exact integers (int16)."""
+    return (codes.astype(np.int16) * (1 << exps.astype(np.int16))[..., None]).astype(np.int16)
+
+
+def pack_int4(codes: np.ndarray) -> np.ndarray:
+    """Storage format: two codes per byte, element 2c in the low nibble and 2c+1 in
+    the high nibble, each as 4-bit two's complement.  [..., r] -> [..., r/2] uint8."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
 
 
 def head_dots(qv: np.ndarray, kv: np.ndarray) -> np.ndarray:
@@ -432,8 +471,14 @@ def segment_permute(x: np.ndarray, perm: np.ndarray, axis: int, inverse: bool = 
 # --------------------------------------------------------------------------
 
 def decode_step(inp: Dict, batches=None, heads=None) -> Dict:
-    """Score -> select -> sparse attention for one decode step of a workload dict."""
+    """Score -> select -> sparse attention for one decode step of a workload dict.
+
+    With an int4 selector cache (cfg.selector_q4) the scores use the
+    dequantised int4 keys in place of the int8 ones.
+    """
     cfg = inp["cfg"]
+    if getattr(cfg, "selector_q4", False):
+        inp = dict(inp, kI=dequantize_selector_keys(*quantize_selector_keys(inp["kI"])))
     if getattr(cfg, "per_group", False):
         s = score_decode_grouped(inp["qI"], inp["kI"], inp["w"], inp["seq_len"], cfg.blk, cfg.Hkv)
         if cfg.select == "topk":

@@ -55,6 +55,9 @@ MUTATIONS = [
     ("importance_gqa_modulo", "to_f64(k[b, h // G, :L], dtype)", "to_f64(k[b, h % Hkv, :L], dtype)"),
     ("importance_sort_ascending", "key=lambda t: (-imp[b, t], t)", "key=lambda t: (imp[b, t], t)"),
     ("importance_ties_highest", "key=lambda t: (-imp[b, t], t)", "key=lambda t: (-imp[b, t], -t)"),
+    ("int4_round_down", "c = np.floor_divide(2 * x + 2 ** e, 2 ** (e + 1))", "c = np.floor_divide(x, 2 ** e)"),
+    ("int4_exponent_from_one", "    for e in range(8):\n        c = np.floor_divide(", "    for e in range(1, 8):\n        c = np.floor_divide("),
+    ("int4_nibbles_swapped", "(c[..., 0::2] | (c[..., 1::2] << 4))", "(c[..., 1::2] | (c[..., 0::2] << 4))"),
     ("segment_check_loose", "return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))", "return True"),
 ]
 

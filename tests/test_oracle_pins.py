@@ -148,6 +148,50 @@ def test_score_grouped_finds_each_groups_planted_blocks():
             assert all(int(s[b, g, j]) < lo for j in others - mine), (b, g)
 
 
+def test_int4_quantization_golden():
+    g = gold("int4_tiny.json")
+    codes, exps = O.quantize_selector_keys(np.array(g["kI"], dtype=np.int8))
+    assert exps.tolist() == g["exps"]
+    assert codes.tolist() == g["codes"]
+    assert O.pack_int4(codes)[0].tolist() == g["packed_row0"]
+
+
+def test_int4_quantization_bounds_minimality_and_packing():
+    rng = np.random.default_rng(31)
+    kI = rng.integers(-128, 128, size=(500, 16), dtype=np.int8)
+    kI[:50] = rng.integers(-8, 8, size=(50, 16))           # already int4: exact
+    kI[50:100] = rng.integers(-30, 31, size=(50, 16))
+    codes, exps = O.quantize_selector_keys(kI)
+    x = kI.astype(np.int64)
+    e = exps.astype(np.int64)[:, None]
+    deq = O.dequantize_selector_keys(codes, exps).astype(np.int64)
+    assert (codes >= -8).all() and (codes <= 7).all()
+    # round to nearest: within half a step, ties upward
+    assert (np.abs(deq - x) * 2 <= (1 << e)).all()
+    assert ((2 * (deq - x) == (1 << e)) | (np.abs(deq - x) * 2 < (1 << e)) | (e == 0)).all()
+    assert (exps[:50] == 0).all() and np.array_equal(deq[:50], x[:50])
+    # minimal: one exponent less overflows the int4 range for some element
+    for i in np.nonzero(exps > 0)[0]:
+        e1 = int(exps[i]) - 1
+        c = [math.floor(v / 2 ** e1 + 0.5) for v in x[i]]
+        assert min(c) < -8 or max(c) > 7
+    # packing: low nibble = even element, high nibble = odd element, 4-bit two's complement
+    p = O.pack_int4(codes).astype(np.int64)
+    lo = ((p & 0xF) ^ 8) - 8
+    hi = ((p >> 4) ^ 8) - 8
+    assert np.array_equal(lo, codes[:, 0::2]) and np.array_equal(hi, codes[:, 1::2])
+
+
+def test_int4_scores_equal_int8_scores_when_keys_fit():
+    # keys already in the int4 range quantise exactly, so the scores are unchanged
+    rng = np.random.default_rng(32)
+    qI, kI, w = _rand_idx(rng, 2, 30, 8, 16, -8, 7)
+    codes, exps = O.quantize_selector_keys(kI)
+    L = np.array([30 * 64, 1000])
+    assert np.array_equal(O.score_decode(qI, O.dequantize_selector_keys(codes, exps), w, L, 64),
+                          O.score_decode(qI, kI, w, L, 64))
+
+
 def test_pool_golden():
     g = gold("pool_tiny.json")
     toks = np.array([b["tokens"] for b in g["blocks"]], dtype=np.int8).reshape(1, -1, 1, 1)

@@ -96,3 +96,17 @@ def test_importance_permutation_needs_fewer_blocks_for_coverage():
                      np.mean([m[n, sel[i]].sum() for n, i in enumerate(qb)]))
     assert res["importance"][0] < 0.95 * res["random"][0], res
     assert res["importance"][1] > res["random"][1] + 0.2, res
+
+
+def test_int4_selector_cache_keeps_the_selection():
+    """SpotAttention §4: the int4 selector cache costs no measurable accuracy.  On
+    the small top-p workload the selections from int4 keys equal those from
+    the int8 keys, sequence by sequence."""
+    import dataclasses
+    import oracle as O
+    cfg = gen.SMALL_DECODE_TOPP_Q4
+    inp = gen.make(cfg)
+    r4 = O.decode_step(inp)
+    r8 = O.decode_step(dict(inp, cfg=dataclasses.replace(cfg, selector_q4=False)))
+    for b in range(cfg.B):
+        assert r4["sel"][b] == r8["sel"][b], b
