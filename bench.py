@@ -46,8 +46,8 @@ ROTATE_BYTES = 1 << 30          # bytes one rotation over the copies must touch
 COPY_MEM_LIMIT = 64 << 30       # device bytes all copies together may take
 
 DECODE_METRIC = "sparse-decode tokens/s at 128K ctx (1 GPU); achieved HBM GB/s vs peak"
-WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "decode_128k_pergroup", "tiny_decode",
-             "prefill_64k", "prefill_64k_importance")
+WORKLOADS = ("decode_128k_topp", "decode_32k", "decode_64k_headsplit", "decode_128k_pergroup", "decode_128k_topp_q4",
+             "tiny_decode", "prefill_64k", "prefill_64k_importance")
 
 
 def log(*a):
@@ -89,6 +89,7 @@ def config_of(name):
     return {"decode_128k_topp": gen.DECODE_128K_TOPP, "decode_32k": gen.DECODE_32K,
             "decode_64k_headsplit": gen.DECODE_64K_HEADSPLIT, "decode_128k_pergroup": gen.DECODE_128K_PERGROUP,
             "tiny_decode": gen.TINY_DECODE, "prefill_64k_importance": gen.PREFILL_64K_IMPORTANCE,
+            "decode_128k_topp_q4": gen.DECODE_128K_TOPP_Q4,
             "prefill_64k": gen.PREFILL_64K}[name]
 
 
@@ -171,9 +172,12 @@ def decode_attn_bytes(cfg, idx, counts, seq_len, head_mode) -> int:
 
 
 def decode_index_bytes(cfg, seq_len) -> int:
-    """Algorithmic bytes of scoring + selection: kI of the valid blocks, qI, w, block lists."""
+    """Algorithmic bytes of scoring + selection: the selector keys of the valid blocks
+    (int8: r bytes per head; int4 cache: r/2 bytes of codes + 1 exponent byte), qI, w,
+    block lists."""
     nbv = sum(-(-int(L) // cfg.blk) for L in seq_len)
-    return nbv * cfg.H_idx * cfg.r + cfg.B * cfg.H_idx * (cfg.r + 1) + cfg.B * 4
+    per_head = cfg.r // 2 + 1 if cfg.selector_q4 else cfg.r
+    return nbv * cfg.H_idx * per_head + cfg.B * cfg.H_idx * (cfg.r + 1) + cfg.B * 4
 
 
 def decode_cpu_baseline(inp, cfg):
@@ -208,16 +212,22 @@ def bench_decode(args, cfg):
     dt = cfg.dtype
     base = {"q": dev(inp["q"], dt), "k": dev(inp["k"], dt), "v": dev(inp["v"], dt), "qI": dev(inp["qI"]),
             "kI": dev(inp["kI"]), "w": dev(inp["w"])}
+    if cfg.selector_q4:
+        # the selector cache is written as int4 when keys enter it (outside the step)
+        base["kq"], base["ke"] = S.spa_quantize_selector_keys(base.pop("kI"))
+
+    def sel_keys(x):
+        return (x["kq"], x["ke"]) if cfg.selector_q4 else x["kI"]
     seq_len, head_mode = dev(inp["seq_len"]), dev(inp["head_mode"])
     spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx,
                         r=cfg.r, n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta,
                         p=cfg.p, k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
                         local_window_tok=cfg.local_window_tok, select_algo=args.select_algo,
-                        per_group=cfg.per_group)
-    if cfg.per_group and args.select_path == "fused":
-        raise SystemExit("per-group selection has no fused score+select launch; use --select-path separate")
+                        per_group=cfg.per_group, selector_q4=cfg.selector_q4)
+    if (cfg.per_group or cfg.selector_q4) and args.select_path == "fused":
+        raise SystemExit("per-group and int4 selection have no fused score+select launch; use --select-path separate")
     step = S.DecodeStep(spec, fused=args.select_path == "fused")
-    step(base["q"], base["k"], base["v"], base["qI"], base["kI"], base["w"], seq_len, head_mode)
+    step(base["q"], base["k"], base["v"], base["qI"], sel_keys(base), base["w"], seq_len, head_mode)
     torch.cuda.synchronize()
     idx, counts = step.idx.cpu().numpy(), step.count.cpu().numpy()
     ab = decode_attn_bytes(cfg, idx, counts, inp["seq_len"], inp["head_mode"])
@@ -234,7 +244,7 @@ def bench_decode(args, cfg):
     # the steps inside a chunk follow each other without a launch boundary.
     # The timed steps use input set j % copies for step j.
     use_graph = args.launch == "graph" and copies <= 64
-    step_args = [(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], seq_len, head_mode) for x in sets]
+    step_args = [(x["q"], x["k"], x["v"], x["qI"], sel_keys(x), x["w"], seq_len, head_mode) for x in sets]
     chunk_len = min(copies, args.steps)
     graphs = [step.capture(*a) for a in step_args] if use_graph else None
     chunk = step.capture_steps(step_args[:chunk_len]) if use_graph else None
@@ -262,7 +272,7 @@ def bench_decode(args, cfg):
         if step.fused:
             step.score_select(x["qI"], x["kI"], x["w"], seq_len)
         else:
-            step.score(x["qI"], x["kI"], x["w"], seq_len)
+            step.score(x["qI"], sel_keys(x), x["w"], seq_len)
             step.select(seq_len)
         if ev is not None:
             ev[1].record()
@@ -321,6 +331,7 @@ def bench_decode(args, cfg):
                    "beta": cfg.beta, "k_min": cfg.k_min, "k_max": cfg.k_max, "n_sink": cfg.n_sink,
                    "n_local": cfg.n_local, "retrieval_groups": int(sum(1 for m in inp["head_mode"] if m == 0)),
                    "per_group_selection": cfg.per_group,
+                   "selector_cache": "int4, one power-of-two scale per 16 keys" if cfg.selector_q4 else "int8",
                    "local_sink_tok": cfg.local_sink_tok, "local_window_tok": cfg.local_window_tok,
                    "input_copies_rotated": copies, "seed": args.seed,
                    "launch": f"hip_graph, {chunk_len} steps per graph" if use_graph else "eager",
@@ -334,6 +345,9 @@ def bench_decode(args, cfg):
         "stage_timing": "a second pass of the same steps, launched call by call with events between stages",
         "selected_blocks": {"mean": float(counts.mean()), "min": int(counts.min()), "max": int(counts.max())},
         "step_algorithmic_bytes": ab + ib,
+        "selector_cache_bytes": {"int8": cfg.B * cfg.nb * cfg.H_idx * cfg.r,
+                                 "int4": cfg.B * cfg.nb * cfg.H_idx * (cfg.r // 2 + 1),
+                                 "held": "int4" if cfg.selector_q4 else "int8"},
         "step_hbm_gbs": (ab + ib) / (ms_step * 1e-3) / 1e9,
     }
     if not args.no_cpu_baseline:

@@ -11,7 +11,8 @@ from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORT
                    spa_index_score_workspace_size, spa_score_select_decode, spa_segment_permute, spa_select_topk,
                    spa_select_topp,
                    spa_sparse_decode_attn, spa_sparse_decode_attn_grouped, spa_sparse_decode_attn_workspace_size,
-                   spa_importance_permutation, spa_importance_permutation_workspace_size)
+                   spa_importance_permutation, spa_importance_permutation_workspace_size, spa_quantize_selector_keys,
+                   spa_index_score_q4)
 from .pipeline import DecodeSpec, DecodeStep, PrefillSpec, PrefillStep
 
 __all__ = [n for n in dir() if not n.startswith("_")]

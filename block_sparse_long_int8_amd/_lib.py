@@ -59,6 +59,8 @@ _SIGS = {
     "spa_block_sparse_prefill": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                       _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_segment_permute": (_i, [_vp, _vp, _i64, _i, _sz, _vp, _i, _i, _vp]),
+    "spa_quantize_selector_keys": (_i, [_vp, _i64, _i, _vp, _vp, _vp]),
+    "spa_index_score_q4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]),
     "spa_importance_permutation": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spa_importance_permutation_workspace_size": (_sz, [_i, _i, _i]),
 }
@@ -176,6 +178,43 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
     st = lib().spa_index_score(_ptr(qI), _ptr(kI), _ptr(w), B, H, r, Mq, nKb, q_blk0, _ptr(seq_len), blk, mode,
                                _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     _check("spa_index_score", st)
+    return scores
+
+
+def spa_quantize_selector_keys(kI, codes=None, exps=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """int8 key vectors [..., 16] -> int4 codes [..., 8] uint8 and exponents [...] uint8."""
+    _dev(kI, "kI", torch.int8)
+    r = kI.shape[-1]
+    lead = tuple(kI.shape[:-1])
+    if codes is None:
+        codes = torch.empty(lead + (r // 2,), dtype=torch.uint8, device=kI.device)
+    if exps is None:
+        exps = torch.empty(lead, dtype=torch.uint8, device=kI.device)
+    st = lib().spa_quantize_selector_keys(_ptr(kI), math.prod(lead), r, _ptr(codes), _ptr(exps), _stream())
+    _check("spa_quantize_selector_keys", st)
+    return codes, exps
+
+
+def spa_index_score_q4(qI, codes, exps, w, blk, seq_len, mode=SPA_SCORE_DECODE, Mq=None, scores=None) -> torch.Tensor:
+    """Decode scores from the int4 selector cache; Mq is the number of groups in grouped mode."""
+    _dev(qI, "qI", torch.int8)
+    _dev(codes, "codes", torch.uint8)
+    _dev(exps, "exps", torch.uint8)
+    _dev(w, "w", torch.int8)
+    _dev(seq_len, "seq_len", torch.int32)
+    B, H, r = qI.shape
+    nKb = codes.shape[1]
+    if codes.shape != (B, nKb, H, r // 2) or exps.shape != (B, nKb, H):
+        raise ValueError("codes must be [B, nKb, H_idx, r/2] and exps [B, nKb, H_idx]")
+    Mq = 1 if mode == SPA_SCORE_DECODE else Mq
+    if Mq is None:
+        raise ValueError("grouped decode scoring needs Mq (the number of groups)")
+    if scores is None:
+        scores = torch.empty((B, nKb) if mode == SPA_SCORE_DECODE else (B, Mq, nKb), dtype=torch.int32,
+                             device=qI.device)
+    st = lib().spa_index_score_q4(_ptr(qI), _ptr(codes), _ptr(exps), _ptr(w), B, H, r, Mq, nKb, _ptr(seq_len), blk,
+                                  mode, _ptr(scores), _stream())
+    _check("spa_index_score_q4", st)
     return scores
 
 

@@ -117,6 +117,41 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   return from_hip(spa::launch_score_prefill(qb, kb, w, B, H_idx, Mq, nKb, q_blk0, seq_len, blk, scores, s), fn);
 }
 
+spa_status spa_quantize_selector_keys(const int8_t* kI, int64_t n_vec, int r, uint8_t* codes, uint8_t* exps,
+                                      void* stream) {
+  const char* fn = "spa_quantize_selector_keys";
+  REQUIRE(n_vec >= 0, SPA_ERR_INVALID_ARG, "negative vector count");
+  REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "int4 selector keys support r == 16 only (got %d)", r);
+  if (n_vec == 0) return ok();
+  REQUIRE(kI && codes && exps, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(kI) && aligned16(codes), SPA_ERR_INVALID_ARG, "kI and codes must be 16-byte aligned");
+  return from_hip(spa::launch_quantize_keys(kI, (long)n_vec, codes, exps, (hipStream_t)stream), fn);
+}
+
+spa_status spa_index_score_q4(const int8_t* qI, const uint8_t* codes, const uint8_t* exps, const int8_t* w, int B,
+                              int H_idx, int r, int Mq, int nKb, const int32_t* seq_len, int blk, int mode,
+                              int32_t* scores, void* stream) {
+  const char* fn = "spa_index_score_q4";
+  REQUIRE(mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED, SPA_ERR_INVALID_ARG,
+          "int4 keys support the decode modes only (got mode %d)", mode);
+  REQUIRE(B >= 0 && Mq >= 0 && nKb >= 0, SPA_ERR_INVALID_ARG, "negative size (B=%d Mq=%d nKb=%d)", B, Mq, nKb);
+  REQUIRE(blk >= 1, SPA_ERR_INVALID_ARG, "blk must be >= 1 (got %d)", blk);
+  REQUIRE(H_idx >= 1, SPA_ERR_INVALID_ARG, "H_idx must be >= 1");
+  if (mode == SPA_SCORE_DECODE) REQUIRE(Mq == 1, SPA_ERR_INVALID_ARG, "decode mode needs Mq == 1 (got %d)", Mq);
+  else
+    REQUIRE(Mq >= 1 && H_idx % Mq == 0, SPA_ERR_INVALID_ARG, "grouped decode needs Mq groups dividing H_idx (Mq=%d H_idx=%d)",
+            Mq, H_idx);
+  REQUIRE(r == 16 && H_idx <= 32 && (H_idx & (H_idx - 1)) == 0, SPA_ERR_UNSUPPORTED,
+          "int4 scoring supports r == 16 and a power-of-two H_idx <= 32 (got r=%d, H_idx=%d)", r, H_idx);
+  if (B == 0 || nKb == 0) return ok();
+  REQUIRE(qI && codes && exps && w && scores && seq_len, SPA_ERR_INVALID_ARG, "null tensor pointer");
+  REQUIRE(aligned16(qI) && aligned16(codes) && aligned16(scores), SPA_ERR_INVALID_ARG,
+          "qI, codes and scores must be 16-byte aligned");
+  return from_hip(spa::launch_score_decode_q4(qI, codes, exps, w, B, H_idx, Mq, nKb, seq_len, blk, scores,
+                                              (hipStream_t)stream),
+                  fn);
+}
+
 // --------------------------------------------------------------- selection --
 
 static spa_status select_common(const char* fn, const int32_t* scores, int B, int M, int nKb,

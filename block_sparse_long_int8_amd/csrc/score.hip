@@ -16,6 +16,9 @@
 //    the head sum, so heads cannot be folded into the K dimension).
 //  * pooling: per-token vectors averaged per block and rounded to
 //    floor(mean + 1/2) (PBS-Attn page, §4: block importance by mean pooling).
+//  * int4 selector cache (SpotAttention page, §4 "Cuantización"): each key
+//    vector is stored as 16 int4 codes plus one power-of-two scale 2^e, so the
+//    dequantised key code * 2^e is an exact integer and so is every score.
 #include "spa_internal.h"
 
 namespace spa {
@@ -136,6 +139,88 @@ __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __r
   }
 }
 
+// ------------------------------------------------------- int4 selector keys --
+// One lane per 16-element key vector: e is the smallest exponent for which the
+// largest and the smallest element (the rounding is monotonic, so they bound
+// every code) give codes floor(x / 2^e + 1/2) in [-8, 7]; the codes are
+// packed two per byte, element 2c in the low nibble.
+__global__ void __launch_bounds__(256) quantize_keys_kernel(const int8_t* __restrict__ kI, long n_vec,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ exps) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_vec) return;
+  const int4 v = *reinterpret_cast<const int4*>(kI + i * 16);
+  const int w[4] = {v.x, v.y, v.z, v.w};
+  int x[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) x[k] = (int)(int8_t)(w[k >> 2] >> (8 * (k & 3)));
+  int vmax = x[0], vmin = x[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    vmax = max(vmax, x[k]);
+    vmin = min(vmin, x[k]);
+  }
+  int e = 0;
+  while (((2 * vmax + (1 << e)) >> (e + 1)) > 7 || ((2 * vmin + (1 << e)) >> (e + 1)) < -8) ++e;
+  uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const uint32_t c = (uint32_t)((2 * x[k] + (1 << e)) >> (e + 1)) & 0xFu;
+    packed[k >> 3] |= c << (4 * (k & 7));
+  }
+  *reinterpret_cast<uint2*>(codes + i * 8) = uint2{packed[0], packed[1]};
+  exps[i] = (uint8_t)e;
+}
+
+// Decode scores from int4 keys, r == 16 and a power-of-two H <= 64: one lane
+// per (block, head) loads its 8 bytes of codes (the wave reads 512 B
+// contiguous) and its exponent.  Shifting each nibble to the top of a byte
+// gives 16 * code as int8, so four v_dot4 against the query bytes regrouped
+// into even and odd elements give 16 * (q . code) exactly; >> 4 and << e
+// give q . (code * 2^e).  ReLU, weight and the group sums as for int8 keys.
+// grid: ceil(B*nKb*H / 256); block 256.
+__global__ void __launch_bounds__(256) score_decode_q4_kernel(const int8_t* __restrict__ qI,
+                                                              const uint8_t* __restrict__ codes,
+                                                              const uint8_t* __restrict__ exps,
+                                                              const int8_t* __restrict__ w, int H,
+                                                              int log2H, int log2hpg, int nKb, int B,
+                                                              const int32_t* __restrict__ seq_len,
+                                                              int blk, int32_t* __restrict__ scores) {
+  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long total = (long)B * nKb * H;
+  const bool in = t < total;
+  const long bj = in ? (t >> log2H) : 0;
+  const int h = (int)(t & (H - 1));
+  const int b = (int)(bj / nKb);
+  const int j = (int)(bj - (long)b * nKb);
+  int v = 0;
+  bool valid = false;
+  if (in) {
+    const int L = seq_len[b];
+    valid = j < min(nKb, (L + blk - 1) / blk);
+    if (valid) {
+      const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)t * 8);
+      const int e = exps[t];
+      const int4 q = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+      // even / odd elements of each 8-element half of the query
+      const int qe0 = (int)__builtin_amdgcn_perm((unsigned)q.y, (unsigned)q.x, 0x06040200u);
+      const int qo0 = (int)__builtin_amdgcn_perm((unsigned)q.y, (unsigned)q.x, 0x07050301u);
+      const int qe1 = (int)__builtin_amdgcn_perm((unsigned)q.w, (unsigned)q.z, 0x06040200u);
+      const int qo1 = (int)__builtin_amdgcn_perm((unsigned)q.w, (unsigned)q.z, 0x07050301u);
+      int dot = __builtin_amdgcn_sdot4(qe0, (int)((c.x << 4) & 0xF0F0F0F0u), 0, false);
+      dot = __builtin_amdgcn_sdot4(qo0, (int)(c.x & 0xF0F0F0F0u), dot, false);
+      dot = __builtin_amdgcn_sdot4(qe1, (int)((c.y << 4) & 0xF0F0F0F0u), dot, false);
+      dot = __builtin_amdgcn_sdot4(qo1, (int)(c.y & 0xF0F0F0F0u), dot, false);
+      v = (int)w[(size_t)b * H + h] * max((dot >> 4) << (e & 7), 0);
+    }
+  }
+  for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
+  if (in && (h & ((1 << log2hpg) - 1)) == 0) {
+    const int groups = H >> log2hpg;
+    scores[((size_t)b * groups + (h >> log2hpg)) * nKb + j] = valid ? v : INT32_MIN_V;
+  }
+}
+
 // --------------------------------------------------------------- pooling ----
 // x_tok [B, n_tok, H*r] int8 whose token 0 is absolute token tok0; block jb of
 // the output covers absolute tokens [tok0 + jb*blk, +blk) below seq_len.
@@ -238,6 +323,23 @@ hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t*
   }
   dim3 grid((nKb + 255) / 256, B);
   score_decode_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, r, groups, nKb, seq_len, blk, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_keys(const int8_t* kI, long n_vec, uint8_t* codes, uint8_t* exps, hipStream_t s) {
+  quantize_keys_kernel<<<(unsigned)((n_vec + 255) / 256), 256, 0, s>>>(kI, n_vec, codes, exps);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_decode_q4(const int8_t* qI, const uint8_t* codes, const uint8_t* exps, const int8_t* w,
+                                  int B, int H, int groups, int nKb, const int32_t* seq_len, int blk,
+                                  int32_t* scores, hipStream_t s) {
+  int log2H = 0, log2hpg = 0;
+  while ((1 << log2H) < H) ++log2H;
+  while ((1 << log2hpg) < H / groups) ++log2hpg;
+  const long total = (long)B * nKb * H;
+  score_decode_q4_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(qI, codes, exps, w, H, log2H, log2hpg, nKb,
+                                                                          B, seq_len, blk, scores);
   return hipGetLastError();
 }
 

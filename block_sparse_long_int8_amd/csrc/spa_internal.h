@@ -45,6 +45,10 @@ struct LaunchStatus {
 hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
                                int r, int groups, int nKb, const int32_t* seq_len, int blk,
                                int32_t* scores, hipStream_t s);
+hipError_t launch_quantize_keys(const int8_t* kI, long n_vec, uint8_t* codes, uint8_t* exps, hipStream_t s);
+hipError_t launch_score_decode_q4(const int8_t* qI, const uint8_t* codes, const uint8_t* exps, const int8_t* w,
+                                  int B, int H, int groups, int nKb, const int32_t* seq_len, int blk,
+                                  int32_t* scores, hipStream_t s);
 hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok_per_seq, int nblocks,
                               int tok0, int H, int r, int blk, const int32_t* seq_len,
                               int8_t* out, hipStream_t s);

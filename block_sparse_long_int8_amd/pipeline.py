@@ -42,6 +42,7 @@ class DecodeSpec:
     out_dtype: torch.dtype = torch.float32
     select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
     per_group: bool = False       # one selection per KV head from its own H_idx/Hkv indexer heads
+    selector_q4: bool = False     # selector keys held as int4 codes + exponents (a (codes, exps) pair for kI)
 
     @property
     def nb(self) -> int:
@@ -70,8 +71,8 @@ class DecodeStep:
 
     def __init__(self, spec: DecodeSpec, device="cuda", fused: bool = False):
         self.spec = s = spec
-        if fused and s.per_group:
-            raise ValueError("the fused score+select launch has no per-group mode")
+        if fused and (s.per_group or s.selector_q4):
+            raise ValueError("the fused score+select launch has no per-group or int4 mode")
         self.fused = fused
         dev = torch.device(device)
         rows = (s.B, s.Hkv) if s.per_group else (s.B,)
@@ -83,8 +84,18 @@ class DecodeStep:
         n = L.spa_sparse_decode_attn_workspace_size(s.B, s.Hq, s.Hkv, s.d)
         self.ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
 
+    @staticmethod
+    def quantize_selector(kI):
+        """int8 selector keys [B, nKb, H_idx, 16] -> the int4 cache (codes, exps) that ``kI`` takes with selector_q4."""
+        return L.spa_quantize_selector_keys(kI)
+
     def score(self, qI, kI, w, seq_len):
         s = self.spec
+        if s.selector_q4:
+            codes, exps = kI
+            mode = L.SPA_SCORE_DECODE_GROUPED if s.per_group else L.SPA_SCORE_DECODE
+            return L.spa_index_score_q4(qI, codes, exps, w, s.blk, seq_len, mode=mode, Mq=s.Hkv if s.per_group else 1,
+                                        scores=self.scores)
         if s.per_group:
             return L.spa_index_score(qI, kI, w, s.blk, seq_len=seq_len, mode=L.SPA_SCORE_DECODE_GROUPED, Mq=s.Hkv,
                                      scores=self.scores)

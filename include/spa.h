@@ -98,6 +98,36 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
 size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, int mode);
 
 /*
+ * spa_quantize_selector_keys / spa_index_score_q4 -- the selector key cache in
+ * micro-scaled int4.
+ *
+ * SpotAttention page, §4 "Cuantización": the selector's key cache, separate
+ * from the attention K/V cache, can be held in micro-scaled int4, cutting its
+ * footprint without touching the attention path.  Here each r = 16 key vector
+ * (one key block and indexer head) is one micro-block: codes c in [-8, 7] and
+ * one power-of-two scale 2^e, e the smallest exponent for which every element
+ * x gives floor(x / 2^e + 1/2) within [-8, 7] (that value is its code).  The
+ * dequantised key c * 2^e is an exact integer, so scores stay exact int32.
+ *
+ * spa_quantize_selector_keys: kI [n_vec, 16] int8 (any leading layout, e.g.
+ *   [B, nKb, H_idx, 16]) -> codes [n_vec, 8] uint8 (element 2i in the low
+ *   nibble of byte i, 2i+1 in the high nibble, 4-bit two's complement) and
+ *   exps [n_vec] uint8 (0..5).  Run when keys enter the cache.
+ * spa_index_score_q4: spa_index_score's decode modes (SPA_SCORE_DECODE with
+ *   Mq == 1, SPA_SCORE_DECODE_GROUPED with Mq groups) on the int4 cache:
+ *   qI [B, H_idx, 16], codes [B, nKb, H_idx, 8], exps [B, nKb, H_idx] (as written
+ *   above; exps are trusted to be those values), w [B, H_idx], seq_len [B]
+ *   -> scores [B, Mq, nKb] with the dequantised keys in place of kI.
+ * Supported: r == 16; scoring needs a power-of-two H_idx <= 32 (so no score can
+ * overflow int32).  No workspace.
+ */
+spa_status spa_quantize_selector_keys(const int8_t* kI, int64_t n_vec, int r, uint8_t* codes, uint8_t* exps,
+                                      void* stream);
+spa_status spa_index_score_q4(const int8_t* qI, const uint8_t* codes, const uint8_t* exps, const int8_t* w, int B,
+                              int H_idx, int r, int Mq, int nKb, const int32_t* seq_len, int blk, int mode,
+                              int32_t* scores, void* stream);
+
+/*
  * spa_select_topk -- static top-k block selection with reserved blocks.
  *
  * RTPurbo page §3 (fixed top-k budget) with the reserved blocks of the

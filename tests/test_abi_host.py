@@ -173,3 +173,27 @@ def test_importance_permutation_rejections():
     assert call(k=ctypes.c_void_p(0x2008)) == S.SPA_ERR_INVALID_ARG
     assert call(B=0) == S.SPA_OK
     assert L.spa_importance_permutation_workspace_size(1, 32, 65536) >= 32 * 65536 * 4
+
+
+def test_int4_selector_rejections():
+    q = L.spa_quantize_selector_keys
+    assert q(_fake(), 10, 8, _fake(2), _fake(3), N) == S.SPA_ERR_UNSUPPORTED
+    assert q(_fake(), -1, 16, _fake(2), _fake(3), N) == S.SPA_ERR_INVALID_ARG
+    assert q(N, 10, 16, _fake(2), _fake(3), N) == S.SPA_ERR_INVALID_ARG
+    assert q(N, 0, 16, N, N, N) == S.SPA_OK
+    f = L.spa_index_score_q4
+    base = [_fake(), _fake(2), _fake(3), _fake(4), 1, 8, 16, 1, 100, _fake(5), 64, 0, _fake(6), N]
+    b = list(base); b[11] = 1                     # prefill modes are not supported
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[5] = 64                     # H_idx above 32 could overflow
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED
+    b = list(base); b[5] = 6
+    assert f(*b) == S.SPA_ERR_UNSUPPORTED
+    b = list(base); b[7] = 2                      # decode mode needs Mq == 1
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[11] = 3; b[7] = 3           # groups must divide H_idx
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[9] = N                      # seq_len is required
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
+    b = list(base); b[4] = 0
+    assert f(*b) == S.SPA_OK

@@ -108,6 +108,70 @@ def test_decode_graph_replay(cfg):
             assert torch.equal(got, want), f"replay {rep} differs from the eager step"
 
 
+@pytest.mark.parametrize("lo,hi", [(-128, 127), (-8, 7), (-30, 30), (-128, -100)], ids=["full", "int4", "mid", "neg"])
+def test_quantize_selector_keys_bitexact(lo, hi):
+    rng = np.random.default_rng(hi - lo)
+    kI = rng.integers(lo, hi + 1, size=(3, 257, 8, 16), dtype=np.int8)
+    codes, exps = S.spa_quantize_selector_keys(dev(kI))
+    torch.cuda.synchronize()
+    c_ref, e_ref = O.quantize_selector_keys(kI)
+    assert np.array_equal(exps.cpu().numpy(), e_ref)
+    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(c_ref))
+
+
+@pytest.mark.parametrize("H,groups", [(8, 1), (8, 2), (8, 8), (32, 4), (1, 1)])
+def test_scores_decode_q4(H, groups):
+    rng = np.random.default_rng(100 * H + groups)
+    B, nKb, blk = 3, 300, 32
+    qI = rng.integers(-128, 128, size=(B, H, 16), dtype=np.int8)
+    kI = rng.integers(-128, 128, size=(B, nKb, H, 16), dtype=np.int8)
+    w = rng.integers(1, 5, size=(B, H), dtype=np.int8)
+    L = np.array([nKb * blk, 4001, 1], dtype=np.int32)
+    codes, exps = S.spa_quantize_selector_keys(dev(kI))
+    mode = S.SPA_SCORE_DECODE if groups == 1 else S.SPA_SCORE_DECODE_GROUPED
+    got = S.spa_index_score_q4(dev(qI), codes, exps, dev(w), blk, dev(L), mode=mode, Mq=groups)
+    torch.cuda.synchronize()
+    kq = O.dequantize_selector_keys(*O.quantize_selector_keys(kI))
+    ref = O.score_decode(qI, kq, w, L, blk) if groups == 1 else O.score_decode_grouped(qI, kq, w, L, blk, groups)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+def test_decode_q4_step_parity(algo):
+    cfg = gen.SMALL_DECODE_TOPP_Q4
+    print(f"[int4 decode parity] {cfg.name} {algo}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    spec = _spec(cfg)
+    spec.selector_q4 = True
+    spec.select_algo = algo
+    step = S.DecodeStep(spec)
+    kq = step.quantize_selector(t["kI"])
+    step(t["q"], t["k"], t["v"], t["qI"], kq, t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    for b in range(cfg.B):
+        check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok)
+    attn_close(step.out.cpu().numpy(), o_ref)
+
+
+def test_decode_q4_per_group_scores():
+    cfg = dataclasses.replace(gen.SMALL_DECODE_PERGROUP, selector_q4=True)
+    inp, t = _decode_inputs(cfg)
+    spec = _spec(cfg)
+    spec.per_group = True
+    spec.selector_q4 = True
+    step = S.DecodeStep(spec)
+    step(t["q"], t["k"], t["v"], t["qI"], step.quantize_selector(t["kI"]), t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    assert sel_lists(step.idx, step.count) == ref["sel"]
+
+
 def _pergroup_cfg(select):
     if select == "topk":
         return gen.SMALL_DECODE_PERGROUP

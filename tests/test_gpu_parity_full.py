@@ -102,6 +102,34 @@ def test_full_decode_128k_per_group_parity(S):
     assert sel_lists(hidx, hcnt) == ref["sel"]
 
 
+def test_full_decode_128k_q4_parity(S):
+    """The 128K top-p step with the int4 selector cache: quantisation and scores
+    bit-exact, selection by the top-p rule, attention on the GPU's lists."""
+    cfg = gen.DECODE_128K_TOPP_Q4
+    print(f"[full decode parity] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta, p=cfg.p,
+                        k_min=cfg.k_min, k_max=cfg.k_max, selector_q4=True)
+    step = S.DecodeStep(spec)
+    codes, exps = step.quantize_selector(dev(inp["kI"]))
+    step(dev(inp["q"], cfg.dtype), dev(inp["k"], cfg.dtype), dev(inp["v"], cfg.dtype), dev(inp["qI"]),
+         (codes, exps), dev(inp["w"]), dev(inp["seq_len"]), dev(inp["head_mode"]))
+    torch.cuda.synchronize()
+    print(f"[full decode parity] {cfg.name}: oracle", flush=True)
+    c_ref, e_ref = O.quantize_selector_keys(inp["kI"])
+    assert np.array_equal(exps.cpu().numpy(), e_ref)
+    assert np.array_equal(codes.cpu().numpy(), O.pack_int4(c_ref))
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    for b in range(cfg.B):
+        check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, _ = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                  inp["head_mode"])
+    attn_close(step.out.cpu().numpy(), o_ref)
+
+
 def test_full_prefill_64k_parity(S):
     cfg = gen.PREFILL_64K
     print(f"[full prefill parity] {cfg.name}: generating", flush=True)
