@@ -824,6 +824,127 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
 }
 
+// Heads per workgroup of the split merge: (item, group of kMergeGH heads) per
+// workgroup of 256 threads, so the merge spreads over more compute units; thread
+// (sub, pair) loads its partials eight at a time before combining them, so the
+// loads are in flight together.
+#ifndef SPA_MERGE_GH
+#define SPA_MERGE_GH 2
+#endif
+constexpr int kMergeGH = SPA_MERGE_GH > 0 ? SPA_MERGE_GH : 1;
+constexpr bool kMergeSplit = SPA_MERGE_GH > 0;  // 0 selects the one-workgroup-per-item merge
+constexpr int kMerge2Threads = 256;
+
+__global__ void __launch_bounds__(kMerge2Threads) decode_merge2_kernel(DecodeArgs a, int n_items, int workers) {
+  __shared__ float Ms_all[kMerge2Threads];
+  __shared__ float red[kMerge2Threads];
+  __shared__ float4 acc_s[kMerge2Threads];
+  const int G = a.Hq / a.Hkv;
+  const int d = a.d;
+  const int hgroups = (G + kMergeGH - 1) / kMergeGH;
+  const int item = blockIdx.x / hgroups;
+  const int hg = blockIdx.x - item * hgroups;
+  WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
+  const int share = ws.hdr[1];
+  const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
+  if (s1 <= s0 || share <= 0) return;
+  const int w0 = s0 / share;
+  const int nparts = (s1 - 1) / share - w0 + 1;
+  const int per_head = d / 4;
+  const int pairs = kMergeGH * per_head;  // <= 256 (kMergeGH * d <= 1024)
+  const int nsub = kMerge2Threads / pairs;
+  const int tid = threadIdx.x;
+  const int sub = tid / pairs;
+  const int pair = tid - sub * pairs;
+  const int hl = pair / per_head;
+  const int h = hg * kMergeGH + hl;
+  const int c4 = pair - hl * per_head;
+  const bool active = sub < nsub && h < G;
+  float M = -INFINITY, L = 0.f;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (active) {
+    for (int p0 = sub; p0 < nparts; p0 += 8 * nsub) {
+      float2 ml[8];
+      float4 ow[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = p0 + e * nsub;
+        if (p < nparts) {
+          const size_t slot = (size_t)item + w0 + p;
+          ml[e] = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
+          ow[e] = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
+        } else {
+          ml[e] = float2{-INFINITY, 0.f};
+          ow[e] = float4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      float Mc = M;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Mc = fmaxf(Mc, ml[e].x);
+      if (Mc != -INFINITY) {
+        const float sc = exp2f(M - Mc);  // 0 while M is -inf
+        L *= sc;
+        acc.x *= sc;
+        acc.y *= sc;
+        acc.z *= sc;
+        acc.w *= sc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if (ml[e].x == -INFINITY) continue;
+          const float f = exp2f(ml[e].x - Mc);
+          L += f * ml[e].y;
+          acc.x += f * ow[e].x;
+          acc.y += f * ow[e].y;
+          acc.z += f * ow[e].z;
+          acc.w += f * ow[e].w;
+        }
+        M = Mc;
+      }
+    }
+  }
+  Ms_all[tid] = M;
+  red[tid] = L;
+  acc_s[tid] = acc;
+  __syncthreads();
+  if (sub != 0 || !active) return;
+  const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
+  for (int u = 1; u < nsub; ++u) M = fmaxf(M, Ms_all[u * pairs + pair]);
+  if (M != -INFINITY) {
+    const float f0 = exp2f(Ms_all[pair] - M);
+    L *= f0;
+    acc.x *= f0;
+    acc.y *= f0;
+    acc.z *= f0;
+    acc.w *= f0;
+    for (int u = 1; u < nsub; ++u) {
+      const float mu = Ms_all[u * pairs + pair];
+      if (mu == -INFINITY) continue;
+      const float f = exp2f(mu - M);
+      L += f * red[u * pairs + pair];
+      const float4 o2 = acc_s[u * pairs + pair];
+      acc.x += f * o2.x;
+      acc.y += f * o2.y;
+      acc.z += f * o2.z;
+      acc.w += f * o2.w;
+    }
+  }
+  float4 o = {0.f, 0.f, 0.f, 0.f};
+  float lse_v = -INFINITY;
+  if (M != -INFINITY && L > 0.f) {
+    const float inv = 1.f / L;
+    o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+    lse_v = (M + log2f(L)) * kLn2;
+  }
+  const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
+  if (a.out_bf16) {
+    const uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
+  } else {
+    *reinterpret_cast<float4*>((float*)a.out + orow) = o;
+  }
+  if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
+}
+
 int g_workers = 0;
 
 }  // namespace
@@ -858,7 +979,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_merge_kernel<<<n_items, kMergeThreads, 0, s>>>(a, n_items, workers);
+  if (!kMergeSplit) {
+    decode_merge_kernel<<<n_items, kMergeThreads, 0, s>>>(a, n_items, workers);
+  } else {
+    const int G = a.Hq / a.Hkv;
+    decode_merge2_kernel<<<n_items * ((G + kMergeGH - 1) / kMergeGH), kMerge2Threads, 0, s>>>(a, n_items, workers);
+  }
   return hipGetLastError();
 }
 

@@ -120,17 +120,18 @@ __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __r
   int v = 0;
   bool valid = false;
   if (in) {
+    // every (block, head) below nKb is addressable: the loads go out together
+    // with seq_len's, and the sequence end only masks the result
+    const int4 kv = *reinterpret_cast<const int4*>(kI + (size_t)t * 16);
+    const int4 qv = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+    const int wt = w[(size_t)b * H + h];
     const int L = seq_len[b];
     valid = j < min(nKb, (L + blk - 1) / blk);
-    if (valid) {
-      const int4 kv = *reinterpret_cast<const int4*>(kI + (size_t)t * 16);
-      const int4 qv = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
-      int dot = __builtin_amdgcn_sdot4(qv.x, kv.x, 0, false);
-      dot = __builtin_amdgcn_sdot4(qv.y, kv.y, dot, false);
-      dot = __builtin_amdgcn_sdot4(qv.z, kv.z, dot, false);
-      dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
-      v = (int)w[(size_t)b * H + h] * max(dot, 0);
-    }
+    int dot = __builtin_amdgcn_sdot4(qv.x, kv.x, 0, false);
+    dot = __builtin_amdgcn_sdot4(qv.y, kv.y, dot, false);
+    dot = __builtin_amdgcn_sdot4(qv.z, kv.z, dot, false);
+    dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
+    v = valid ? wt * max(dot, 0) : 0;
   }
   for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
   if (in && (h & ((1 << log2hpg) - 1)) == 0) {
@@ -196,12 +197,13 @@ __global__ void __launch_bounds__(256) score_decode_q4_kernel(const int8_t* __re
   int v = 0;
   bool valid = false;
   if (in) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)t * 8);
+    const int e = exps[t];
+    const int4 q = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+    const int wt = w[(size_t)b * H + h];
     const int L = seq_len[b];
     valid = j < min(nKb, (L + blk - 1) / blk);
-    if (valid) {
-      const uint2 c = *reinterpret_cast<const uint2*>(codes + (size_t)t * 8);
-      const int e = exps[t];
-      const int4 q = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+    {
       // even / odd elements of each 8-element half of the query
       const int qe0 = (int)__builtin_amdgcn_perm((unsigned)q.y, (unsigned)q.x, 0x06040200u);
       const int qo0 = (int)__builtin_amdgcn_perm((unsigned)q.y, (unsigned)q.x, 0x07050301u);
@@ -211,7 +213,7 @@ __global__ void __launch_bounds__(256) score_decode_q4_kernel(const int8_t* __re
       dot = __builtin_amdgcn_sdot4(qo0, (int)(c.x & 0xF0F0F0F0u), dot, false);
       dot = __builtin_amdgcn_sdot4(qe1, (int)((c.y << 4) & 0xF0F0F0F0u), dot, false);
       dot = __builtin_amdgcn_sdot4(qo1, (int)(c.y & 0xF0F0F0F0u), dot, false);
-      v = (int)w[(size_t)b * H + h] * max((dot >> 4) << (e & 7), 0);
+      v = valid ? wt * max((dot >> 4) << (e & 7), 0) : 0;
     }
   }
   for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
