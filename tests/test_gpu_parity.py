@@ -354,6 +354,90 @@ def test_decode_batch_zero_is_noop():
 
 
 @pytest.mark.parametrize("algo", ["sort", "hist"])
+@pytest.mark.parametrize("mode", ["topk", "topp"])
+def test_select_at_maximum_blocks(mode, algo):
+    # nKb at the selection limit (4096 blocks): the largest sort / histogram shapes
+    rng = np.random.default_rng(17)
+    nKb, blk = 4096, 16
+    B = 3
+    s = rng.integers(-3000, 3000, size=(B, nKb)).astype(np.int32)
+    s[0, rng.choice(nKb, 40, replace=False)] = 9000            # a clear top set
+    s[2, :] = 5                                                  # all tied
+    L = np.array([nKb * blk, nKb * blk - 7, 2000 * blk + 3], dtype=np.int32)
+    if mode == "topk":
+        idx, cnt = S.spa_select_topk(dev(s), blk, 1, 4, 300, 305, seq_len=dev(L), algo=algo)
+        ref, _ = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topk", k=300)
+        assert sel_lists(idx, cnt) == ref
+    else:
+        idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, 0.01, 0.9, 16, 1024, 1029, seq_len=dev(L), algo=algo)
+        _, info = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topp", beta=0.01, p=0.9, k_min=16, k_max=1024)
+        gsel = sel_lists(idx, cnt)
+        for b in range(B):
+            check_topp_row(gsel[b], info[b], 16, 1024, 0.9)
+
+
+DECODE_EDGE = [
+    ("G16", dict(Hq=32, Hkv=2)),
+    ("f32_d128", dict(dtype="f32", d=128, Hq=8, Hkv=2)),
+    ("blk32", dict(blk=32, k=20)),
+    ("blk128", dict(blk=128, k=6, n_plant=(3, 3))),
+]
+
+
+@pytest.mark.parametrize("name,over", DECODE_EDGE, ids=[e[0] for e in DECODE_EDGE])
+def test_decode_edge_shapes(name, over):
+    cfg = dataclasses.replace(gen.SMALL_DECODE_TOPK, name=f"edge_{name}", **over)
+    print(f"[decode edge] {name}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    assert gsel == ref["sel"]
+    attn_close(step.out.cpu().numpy(), ref["o"])
+
+
+def test_decode_at_maximum_items():
+    # B * Hkv = 4096 (sequence, KV head) items, the limit of the decode plan
+    cfg = dataclasses.replace(gen.TINY_DECODE, name="edge_items", B=512, Hq=8, Hkv=8, T=128, blk=16, k=2, n_plant=(1, 1),
+                              seq_lens=tuple(int(x) for x in np.random.default_rng(3).integers(1, 129, size=512)))
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert sel_lists(step.idx, step.count) == ref["sel"]
+    attn_close(step.out.cpu().numpy(), ref["o"])
+
+
+def test_prefill_long_block_lists():
+    # lists of more than 64 blocks: the kernel reloads its register copy of the list
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, T, d = 1, 4, 1, 150 * 64, 128
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, T, d), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, d), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, d), dtype=np.float32))
+    nb = T // 64
+    idx = np.full((1, nb, nb), -1, dtype=np.int32)
+    cnt = np.zeros((1, nb), dtype=np.int32)
+    for i in range(nb):
+        # odd rows: every block up to the diagonal; even rows: every other block and the diagonal
+        sel = sorted(set(range(0, i + 1, 1 if i % 2 else 2)) | {i})
+        idx[0, i, :len(sel)] = sel
+        cnt[0, i] = len(sel)
+    out, _ = S.spa_block_sparse_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(idx), dev(cnt), 64)
+    torch.cuda.synchronize()
+    pos = np.arange(T)
+    blocks = [63, 64, 65, 128, 129, 149]
+    ref, _ = O.prefill_attention(q, k, v, "bf16", pos, pos, [[idx[0, i, :cnt[0, i]].tolist() for i in range(nb)]], 64,
+                                 blocks=blocks)
+    rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in blocks])
+    attn_close(out.cpu().numpy()[:, :, rows], ref[:, :, rows])
+
+
+@pytest.mark.parametrize("algo", ["sort", "hist"])
 def test_topk_edge_cases(algo):
     # k = 0 keeps only reserved blocks; short sequences keep everything; ties go to the lowest index
     B, nb, blk = 3, 40, 16
