@@ -726,119 +726,20 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 }
 
 // ----------------------------------------------------------------- merge ----
-// One workgroup of 1024 threads per item.  Thread (sub, pair) owns one float4
-// of one head (pair) and every nsub-th partial (sub): pass 1 finds the head
-// maxima, pass 2 rescales and sums its partials, and the nsub sums are added
-// in LDS.  Items with no tile were written by workgroup 0 of the main kernel.
-constexpr int kMergeThreads = 1024;
+// One workgroup of 256 threads per (item, pair of query heads), so the merge
+// spreads over all compute units (one workgroup per item, 1024 threads, took
+// 60 % longer).  Thread (sub, pair) owns one float4 of one head and every
+// nsub-th partial; it loads its partials eight at a time before combining
+// them, so those loads are in flight together, and the nsub sums are added by
+// log-sum-exp in LDS.  Items with no tile were written by workgroup 0 of the
+// main kernel.
+constexpr int kMergeGH = 2;  // query heads per workgroup
+constexpr int kMergeThreads = 256;
 
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
+  __shared__ float Ms_all[kMergeThreads];
   __shared__ float red[kMergeThreads];
   __shared__ float4 acc_s[kMergeThreads];
-  __shared__ float Ms_all[kMergeThreads];
-  const int G = a.Hq / a.Hkv;
-  const int d = a.d;
-  WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
-  const int item = blockIdx.x;
-  const int share = ws.hdr[1];
-  const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
-  if (s1 <= s0 || share <= 0) return;
-  const int w0 = s0 / share;
-  const int nparts = (s1 - 1) / share - w0 + 1;
-  const int per_head = d / 4;
-  const int pairs = G * per_head;            // <= 1024 (G * d <= 4096)
-  const int nsub = kMergeThreads / pairs;
-  const int tid = threadIdx.x;
-  const int sub = tid / pairs;
-  const int pair = tid - sub * pairs;
-  const bool active = sub < nsub;
-  const int h = pair / per_head;
-  const int c4 = pair - h * per_head;
-  // one pass over this thread's partials with a running maximum
-  float M = -INFINITY, L = 0.f;
-  float4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (active) {
-#pragma unroll 4
-    for (int p = sub; p < nparts; p += nsub) {
-      const size_t slot = (size_t)item + w0 + p;
-      const float2 ml = *reinterpret_cast<const float2*>(ws.part_ml + (slot * G + h) * 2);
-      const float4 ow = *reinterpret_cast<const float4*>(ws.part_o + (slot * G + h) * d + 4 * c4);
-      if (ml.x == -INFINITY) continue;
-      if (ml.x > M) {
-        const float sc = exp2f(M - ml.x);  // 0 while M is -inf
-        L *= sc;
-        acc.x *= sc;
-        acc.y *= sc;
-        acc.z *= sc;
-        acc.w *= sc;
-        M = ml.x;
-      }
-      const float f = exp2f(ml.x - M);
-      L += f * ml.y;
-      acc.x += f * ow.x;
-      acc.y += f * ow.y;
-      acc.z += f * ow.z;
-      acc.w += f * ow.w;
-    }
-  }
-  Ms_all[tid] = M;
-  red[tid] = L;
-  acc_s[tid] = acc;
-  __syncthreads();
-  if (sub != 0) return;
-  const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
-  for (int u = 1; u < nsub; ++u) M = fmaxf(M, Ms_all[u * pairs + pair]);
-  if (M != -INFINITY) {
-    const float f0 = exp2f(Ms_all[pair] - M);
-    L *= f0;
-    acc.x *= f0;
-    acc.y *= f0;
-    acc.z *= f0;
-    acc.w *= f0;
-    for (int u = 1; u < nsub; ++u) {
-      const float mu = Ms_all[u * pairs + pair];
-      if (mu == -INFINITY) continue;
-      const float f = exp2f(mu - M);
-      L += f * red[u * pairs + pair];
-      const float4 o2 = acc_s[u * pairs + pair];
-      acc.x += f * o2.x;
-      acc.y += f * o2.y;
-      acc.z += f * o2.z;
-      acc.w += f * o2.w;
-    }
-  }
-  float4 o = {0.f, 0.f, 0.f, 0.f};
-  float lse_v = -INFINITY;
-  if (M != -INFINITY && L > 0.f) {
-    const float inv = 1.f / L;
-    o = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
-    lse_v = (M + log2f(L)) * kLn2;
-  }
-  const size_t orow = ((size_t)b * a.Hq + g * G + h) * d + 4 * c4;
-  if (a.out_bf16) {
-    const uint2 pk = {pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w)};
-    *reinterpret_cast<uint2*>((uint16_t*)a.out + orow) = pk;
-  } else {
-    *reinterpret_cast<float4*>((float*)a.out + orow) = o;
-  }
-  if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
-}
-
-// Heads per workgroup of the split merge: (item, group of kMergeGH heads) per
-// workgroup of 256 threads, so the merge spreads over more compute units; thread
-// (sub, pair) loads its partials eight at a time before combining them, so the
-// loads are in flight together.
-#ifndef SPA_MERGE_GH
-#define SPA_MERGE_GH 2
-#endif
-constexpr int kMergeGH = SPA_MERGE_GH > 0 ? SPA_MERGE_GH : 1;
-constexpr bool kMergeSplit = SPA_MERGE_GH > 0;  // 0 selects the one-workgroup-per-item merge
-constexpr int kMerge2Threads = 256;
-
-__global__ void __launch_bounds__(kMerge2Threads) decode_merge2_kernel(DecodeArgs a, int n_items, int workers) {
-  __shared__ float Ms_all[kMerge2Threads];
-  __shared__ float red[kMerge2Threads];
-  __shared__ float4 acc_s[kMerge2Threads];
   const int G = a.Hq / a.Hkv;
   const int d = a.d;
   const int hgroups = (G + kMergeGH - 1) / kMergeGH;
@@ -852,7 +753,7 @@ __global__ void __launch_bounds__(kMerge2Threads) decode_merge2_kernel(DecodeArg
   const int nparts = (s1 - 1) / share - w0 + 1;
   const int per_head = d / 4;
   const int pairs = kMergeGH * per_head;  // <= 256 (kMergeGH * d <= 1024)
-  const int nsub = kMerge2Threads / pairs;
+  const int nsub = kMergeThreads / pairs;
   const int tid = threadIdx.x;
   const int sub = tid / pairs;
   const int pair = tid - sub * pairs;
@@ -979,12 +880,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (!kMergeSplit) {
-    decode_merge_kernel<<<n_items, kMergeThreads, 0, s>>>(a, n_items, workers);
-  } else {
-    const int G = a.Hq / a.Hkv;
-    decode_merge2_kernel<<<n_items * ((G + kMergeGH - 1) / kMergeGH), kMerge2Threads, 0, s>>>(a, n_items, workers);
-  }
+  const int G = a.Hq / a.Hkv;
+  decode_merge_kernel<<<n_items * ((G + kMergeGH - 1) / kMergeGH), kMergeThreads, 0, s>>>(a, n_items, workers);
   return hipGetLastError();
 }
 

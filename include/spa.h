@@ -4,7 +4,10 @@
  * One decode step of query-dependent block-sparse attention is
  *     spa_index_score -> spa_select_topk | spa_select_topp -> spa_sparse_decode_attn
  * (with one selection per KV group: spa_index_score (SPA_SCORE_DECODE_GROUPED)
- * -> spa_select_* with M = Hkv rows per sequence -> spa_sparse_decode_attn_grouped)
+ * -> spa_select_* with M = Hkv rows per sequence -> spa_sparse_decode_attn_grouped;
+ * with the int4 selector cache, spa_index_score_q4 in place of spa_index_score,
+ * the cache written by spa_quantize_selector_keys when keys enter it; the
+ * spa_select_*_hist variants select without sorting)
  * and one permuted block-sparse prefill is
  *     [spa_importance_permutation ->] spa_segment_permute -> spa_index_score (prefill)
  *     -> spa_select_topk (prefill) -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
