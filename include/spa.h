@@ -24,8 +24,10 @@
  *     Values inside device arrays (idx, count, perm, positions, seq_len) are
  *     trusted: they must satisfy the stated ranges.
  *   - Pointers to bf16/fp32/int tensors must be 16-byte aligned.
- *   - No global mutable state: calls on different streams may run concurrently
- *     as long as their workspaces do not overlap.
+ *   - The only process-wide state is a cache of the GPU's compute-unit count,
+ *     taken on first use (it sets the decode work split and so the decode
+ *     workspace size; size and call on the same device).  Calls on different
+ *     streams may run concurrently as long as their workspaces do not overlap.
  *   - bf16 is passed as its 16-bit pattern (uint16 storage).
  */
 #ifndef SPA_H_
