@@ -4,6 +4,7 @@
 // contract of each entry point.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -173,8 +174,10 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
     REQUIRE(std::isfinite(beta) && beta >= 0.f, SPA_ERR_INVALID_ARG, "need finite beta >= 0 (got %g)", (double)beta);
     REQUIRE(k_min >= 0 && k_min <= k_max, SPA_ERR_INVALID_ARG, "need 0 <= k_min <= k_max (got %d, %d)", k_min, k_max);
   }
-  const long need_cap = (long)n_sink + n_local + budget + (prefill ? 1 : 0);
-  REQUIRE(cap >= 1 && (long)cap >= need_cap, SPA_ERR_INVALID_ARG, "cap %d < reserved + budget = %ld", cap, need_cap);
+  // a row lists distinct blocks below nKb: reserved + budget, at most nKb of them
+  const long need_cap = std::min((long)nKb, (long)n_sink + n_local + budget + (prefill ? 1 : 0));
+  REQUIRE(cap >= 1 && (long)cap >= need_cap, SPA_ERR_INVALID_ARG, "cap %d < min(nKb, reserved + budget) = %ld", cap,
+          need_cap);
   REQUIRE(nKb <= spa::select_max_blocks(), SPA_ERR_UNSUPPORTED, "nKb %d exceeds %d", nKb, spa::select_max_blocks());
   if (B == 0 || M == 0) return ok();
   REQUIRE((scores || (qI && kI && w)) && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");

@@ -151,7 +151,8 @@ spa_status spa_index_score_q4(const int8_t* qI, const uint8_t* codes, const uint
  *   seq_len may be NULL (then every block below nKb is valid).
  * Output: idx [B, M, cap] int32, ascending block indices of reserved + chosen,
  *   padded with -1; count [B, M] int32 = number of valid entries.
- * Errors: SPA_ERR_INVALID_ARG if cap < n_sink + n_local + k (+1 in prefill).
+ * Errors: SPA_ERR_INVALID_ARG if cap < min(nKb, n_sink + n_local + k (+1 in
+ *   prefill)): no list is longer than that.
  * Supported: nKb <= 4096.  No workspace needed (ws may be NULL).
  */
 spa_status spa_select_topk(const int32_t* scores, int B, int M, int nKb, int q_blk0,
@@ -169,8 +170,8 @@ spa_status spa_select_topk(const int32_t* scores, int B, int M, int nKb, int q_b
  * prefix length is clamped to [k_min, k_max] (k_min is the floor of the
  * SpotAttention page, k_max a cap on the workspace of the attention step) and
  * to the number of candidates.  Masses are computed in fp32 on the device.
- * Arguments and outputs as spa_select_topk; cap >= n_sink + n_local + k_max
- * (+1 in prefill).  0 < p <= 1, beta >= 0, 0 <= k_min <= k_max.
+ * Arguments and outputs as spa_select_topk; cap >= min(nKb, n_sink + n_local +
+ * k_max (+1 in prefill)).  0 < p <= 1, beta >= 0, 0 <= k_min <= k_max.
  */
 spa_status spa_select_topp(const int32_t* scores, int B, int M, int nKb, int q_blk0,
                            const int32_t* seq_len, int blk, int n_sink, int n_local, int prefill,

@@ -68,6 +68,9 @@ def test_select_rejections(suffix):
     # cap smaller than reserved + k
     assert tk(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 68, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert b"cap" in L.spa_last_error()
+    # ... but no row lists more than nKb blocks: with 50 blocks, cap 50 is enough (B = 0: validated, nothing launched)
+    assert tk(_fake(), 0, 1, 50, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 49, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tk(_fake(), 0, 1, 50, 0, _fake(2), 64, 1, 4, 0, 64, _fake(3), _fake(4), 50, N, 0, N) == S.SPA_OK
     # decode rows need seq_len
     assert tk(_fake(), 1, 1, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tk(_fake(), 1, 8, 100, 0, N, 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG
@@ -77,7 +80,7 @@ def test_select_rejections(suffix):
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 1.5, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 32, 16, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, float("nan"), 0.9, 16, 512, _fake(3), _fake(4), 517, N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert tp(_fake(), 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 16, 512, _fake(3), _fake(4), 516, N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert tp(_fake(), 1, 1, 1000, 0, _fake(2), 64, 1, 4, 0, 0.125, 0.9, 16, 512, _fake(3), _fake(4), 516, N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert tp(N, 0, 1, 100, 0, N, 64, 1, 4, 0, 0.125, 0.9, 16, 512, N, N, 517, N, 0, N) == S.SPA_OK
     # null scores with a batch to select
     assert tk(N, 1, 1, 100, 0, _fake(2), 64, 1, 4, 0, 8, _fake(3), _fake(4), 13, N, 0, N) == S.SPA_ERR_INVALID_ARG

@@ -1,0 +1,144 @@
+"""Seeded random sweep of decode-step shapes against the CPU oracle.
+
+Each case draws one configuration that the named workloads do not cover
+together: block size, GQA ratio, indexer heads, reserved blocks, top-k or dual
+top-p budgets, ragged sequence lengths, local-window heads, fp32 or bf16, and
+the selection path (separate sorted, separate sort-free, or fused).  The
+parity bars are the suite's: scores and top-k lists bit-exact, top-p lists by
+the set rule, attention within max |diff| <= 1e-2 and relative L2 <= 2e-3.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle as O
+from gpu_util import attn_close, check_topp_row, dev, sel_lists
+
+pytestmark = pytest.mark.gpu
+
+S = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global S
+    import block_sparse_long_int8_amd as mod
+    mod.lib()
+    S = mod
+    yield
+
+
+PATHS = ("separate", "fused", "separate-hist")
+
+
+def _draw(seed: int):
+    """One decode configuration and selection path, from a seeded generator."""
+    g = np.random.default_rng(1000 + seed)
+    f32 = g.random() < 0.25
+    d = int(g.choice([64, 128])) if f32 else 128
+    blk = int(g.choice([16, 32, 64, 128]))
+    Hkv = int(g.choice([1, 2, 4]))
+    G = int(g.choice([1, 2, 3, 4, 8, 16] if Hkv == 1 else [1, 2, 3, 4, 8]))
+    B = int(g.integers(1, 6))
+    nb = int(g.integers(6, 81))
+    T = nb * blk
+    H_idx = int(g.choice([1, 2, 4, 8]))
+    n_sink = int(g.integers(0, 3))
+    n_local = int(g.integers(0, 5))
+    kw = {}
+    if g.random() < 0.5:
+        kw.update(select="topk", k=int(g.integers(0, nb + 1)))
+    else:
+        k_min = int(g.integers(0, 9))
+        kw.update(select="topp", p=float(g.choice([0.5, 0.8, 0.95])), beta=float(g.choice([0.125, 0.5, 1.0])),
+                  k_min=k_min, k_max=int(g.integers(max(k_min, 1), nb + 1)))
+    seq_lens = tuple(int(x) for x in g.integers(1, T + 1, size=B))
+    n_ret = None
+    if Hkv > 1 and g.random() < 0.5:
+        n_ret = int(g.integers(0, Hkv + 1))
+        kw.update(local_sink_tok=int(g.integers(0, 2 * blk)), local_window_tok=int(g.integers(0, 8 * blk)))
+    cfg = dataclasses.replace(
+        gen.DECODE_128K_TOPP, name=f"random_decode_{seed}", cfg_id=200 + seed, B=B, Hq=G * Hkv, Hkv=Hkv, d=d, T=T,
+        blk=blk, H_idx=H_idx, r=16, dtype="f32" if f32 else "bf16", n_sink=n_sink, n_local=n_local,
+        plant_kind="copy", n_plant=(0, min(6, nb)), plant_boost=1.5, plant_mass=0.0, n_retrieval_groups=n_ret,
+        seq_lens=seq_lens, **kw)
+    return cfg, PATHS[seed % len(PATHS)]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_sweep(seed):
+    cfg, path = _draw(seed)
+    print(f"[random decode] seed {seed} {path}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} T={cfg.T} blk={cfg.blk} "
+          f"H_idx={cfg.H_idx} {cfg.select} k={cfg.k} p={cfg.p} beta={cfg.beta} kmin={cfg.k_min} kmax={cfg.k_max} "
+          f"sink={cfg.n_sink} local={cfg.n_local} ret={cfg.n_retrieval_groups} lens={cfg.seq_lens} {cfg.dtype}",
+          flush=True)
+    inp = gen.make(cfg)
+    t = dict(q=dev(inp["q"], cfg.dtype), k=dev(inp["k"], cfg.dtype), v=dev(inp["v"], cfg.dtype),
+             qI=dev(inp["qI"]), kI=dev(inp["kI"]), w=dev(inp["w"]), seq_len=dev(inp["seq_len"]),
+             head_mode=dev(inp["head_mode"]))
+    spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta, p=cfg.p,
+                        k_min=cfg.k_min, k_max=cfg.k_max, local_sink_tok=cfg.local_sink_tok,
+                        local_window_tok=cfg.local_window_tok,
+                        select_algo="hist" if path.endswith("hist") else "sort")
+    step = S.DecodeStep(spec, fused=path == "fused")
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    idx_h = step.idx.cpu().numpy()
+    for b in range(cfg.B):
+        assert (idx_h[b, len(gsel[b]):] == -1).all(), "padding after count must be -1"
+    if cfg.select == "topk":
+        assert gsel == ref["sel"]
+    else:
+        for b in range(cfg.B):
+            check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok)
+    attn_close(step.out.cpu().numpy(), o_ref)
+    lse = step.lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert (np.isfinite(lse) == fin).all()
+    assert np.allclose(lse[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
+
+
+def _draw_prefill(seed: int):
+    """One permuted block-sparse prefill configuration, from a seeded generator."""
+    g = np.random.default_rng(2000 + seed)
+    Hkv = int(g.choice([1, 2]))
+    G = int(g.choice([1, 2, 3, 4, 5, 8]))
+    T = 64 * int(g.integers(4, 41))  # whole 64-token blocks, as the per-token indexer inputs must be
+    seg = int(g.choice([64, 128, 192, 256, 512, T]))
+    return dataclasses.replace(
+        gen.SMALL_PREFILL, name=f"random_prefill_{seed}", cfg_id=300 + seed, B=int(g.integers(1, 3)), T=T,
+        Hq=G * Hkv, Hkv=Hkv, H_idx=int(g.choice([1, 2, 4, 8])), k=int(g.integers(0, 13)),
+        n_sink=int(g.integers(0, 3)), n_local=int(g.integers(0, 3)), seg=seg)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_prefill_random_sweep(seed):
+    cfg = _draw_prefill(seed)
+    print(f"[random prefill] seed {seed}: B={cfg.B} T={cfg.T} Hq={cfg.Hq} Hkv={cfg.Hkv} H_idx={cfg.H_idx} k={cfg.k} "
+          f"sink={cfg.n_sink} local={cfg.n_local} seg={cfg.seg}", flush=True)
+    inp = gen.make(cfg)
+    t = dict(q=dev(inp["q"], "bf16"), k=dev(inp["k"], "bf16"), v=dev(inp["v"], "bf16"), qI=dev(inp["qI_tok"]),
+             kI=dev(inp["kI_tok"]), w=dev(inp["w"]), perm=dev(inp["perm"]))
+    step = S.PrefillStep(S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk,
+                                       H_idx=cfg.H_idx, r=cfg.r, k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local,
+                                       seg=cfg.seg))
+    out = step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
+    torch.cuda.synchronize()
+    front = O.prefill_front(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
+    assert sel_lists(step.idx, step.count) == front["sel"]
+    ref = O.prefill_step(inp, front=front)
+    attn_close(out.cpu().numpy(), ref["o"])
+    lse = step.lse_slot.cpu().numpy()
+    fin = np.isfinite(ref["lse_slot"])
+    assert (np.isfinite(lse) == fin).all()
+    assert np.allclose(lse[fin], ref["lse_slot"][fin], atol=1e-4, rtol=1e-5)
