@@ -68,7 +68,7 @@ def _draw(seed: int):
     return cfg, PATHS[seed % len(PATHS)]
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_decode_random_sweep(seed):
     cfg, path = _draw(seed)
     print(f"[random decode] seed {seed} {path}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} T={cfg.T} blk={cfg.blk} "
@@ -120,7 +120,7 @@ def _draw_prefill(seed: int):
         n_sink=int(g.integers(0, 3)), n_local=int(g.integers(0, 3)), seg=seg)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_prefill_random_sweep(seed):
     cfg = _draw_prefill(seed)
     print(f"[random prefill] seed {seed}: B={cfg.B} T={cfg.T} Hq={cfg.Hq} Hkv={cfg.Hkv} H_idx={cfg.H_idx} k={cfg.k} "
@@ -142,3 +142,60 @@ def test_prefill_random_sweep(seed):
     fin = np.isfinite(ref["lse_slot"])
     assert (np.isfinite(lse) == fin).all()
     assert np.allclose(lse[fin], ref["lse_slot"][fin], atol=1e-4, rtol=1e-5)
+
+
+def _draw_variant(seed: int):
+    """A decode configuration with per-KV-group selection and/or the int4 selector cache."""
+    g = np.random.default_rng(3000 + seed)
+    per_group = bool(seed % 3 != 1)
+    q4 = bool(seed % 3 != 0)
+    base, _ = _draw(500 + seed)
+    Hkv = int(g.choice([1, 2, 4, 8]))
+    hpg = int(g.choice([1, 2, 4])) if per_group else 1
+    H_idx = min(32, Hkv * hpg) if per_group else int(g.choice([1, 2, 4, 8, 16, 32]))
+    G = int(g.choice([1, 2, 4]))
+    cfg = dataclasses.replace(base, name=f"random_variant_{seed}", cfg_id=400 + seed, Hkv=Hkv, Hq=G * Hkv, H_idx=H_idx,
+                              per_group=per_group, selector_q4=q4, n_retrieval_groups=None, local_sink_tok=0,
+                              local_window_tok=0)
+    return cfg, ("separate-hist" if seed % 2 else "separate")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_decode_variant_random_sweep(seed):
+    cfg, path = _draw_variant(seed)
+    print(f"[random decode variant] seed {seed} {path}: per_group={cfg.per_group} q4={cfg.selector_q4} B={cfg.B} "
+          f"Hq={cfg.Hq} Hkv={cfg.Hkv} H_idx={cfg.H_idx} T={cfg.T} blk={cfg.blk} {cfg.select} k={cfg.k} p={cfg.p} "
+          f"kmin={cfg.k_min} kmax={cfg.k_max} sink={cfg.n_sink} local={cfg.n_local} lens={cfg.seq_lens} {cfg.dtype}",
+          flush=True)
+    inp = gen.make(cfg)
+    t = dict(q=dev(inp["q"], cfg.dtype), k=dev(inp["k"], cfg.dtype), v=dev(inp["v"], cfg.dtype),
+             qI=dev(inp["qI"]), kI=dev(inp["kI"]), w=dev(inp["w"]), seq_len=dev(inp["seq_len"]),
+             head_mode=dev(inp["head_mode"]))
+    spec = S.DecodeSpec(B=cfg.B, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, Tcap=cfg.T, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                        n_sink=cfg.n_sink, n_local=cfg.n_local, select=cfg.select, k=cfg.k, beta=cfg.beta, p=cfg.p,
+                        k_min=cfg.k_min, k_max=cfg.k_max, per_group=cfg.per_group, selector_q4=cfg.selector_q4,
+                        select_algo="hist" if path.endswith("hist") else "sort")
+    step = S.DecodeStep(spec)
+    kI = step.quantize_selector(t["kI"]) if cfg.selector_q4 else t["kI"]
+    step(t["q"], t["k"], t["v"], t["qI"], kI, t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    rows = [(b, None) for b in range(cfg.B)] if not cfg.per_group else \
+        [(b, g) for b in range(cfg.B) for g in range(cfg.Hkv)]
+    for b, g in rows:
+        mine = gsel[b] if g is None else gsel[b][g]
+        theirs = ref["sel"][b] if g is None else ref["sel"][b][g]
+        info = ref["info"][b] if g is None else ref["info"][b][g]
+        if cfg.select == "topk":
+            assert mine == theirs, (b, g)
+        else:
+            check_topp_row(mine, info, cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], 0, 0, per_group=cfg.per_group)
+    attn_close(step.out.cpu().numpy(), o_ref)
+    lse = step.lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert (np.isfinite(lse) == fin).all()
+    assert np.allclose(lse[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
