@@ -1,4 +1,4 @@
-"""Seeded random sweep of decode-step shapes against the CPU oracle.
+"""Seeded random sweeps of decode, prefill and importance-permutation shapes against the CPU oracle.
 
 Each case draws one configuration that the named workloads do not cover
 together: block size, GQA ratio, indexer heads, reserved blocks, top-k or dual
@@ -15,7 +15,7 @@ import torch
 
 import gen
 import oracle as O
-from gpu_util import attn_close, check_topp_row, dev, sel_lists
+from gpu_util import attn_close, check_importance_perm, check_topp_row, dev, imp_close, sel_lists
 
 pytestmark = pytest.mark.gpu
 
@@ -199,3 +199,29 @@ def test_decode_variant_random_sweep(seed):
     fin = np.isfinite(lse_ref)
     assert (np.isfinite(lse) == fin).all()
     assert np.allclose(lse[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_importance_permutation_random_sweep(seed):
+    g = np.random.default_rng(4000 + seed)
+    B = int(g.integers(1, 4))
+    Hkv = int(g.choice([1, 2, 4]))
+    Hq = Hkv * int(g.choice([1, 2, 3, 4]))
+    T = int(g.integers(64, 3001))
+    seg = int(g.choice([64, 100, 256, 1000, 4096]))
+    proxy = int(g.integers(1, 65))
+    lens = tuple(int(x) for x in g.integers(1, T + 1, size=B)) if g.random() < 0.5 else None
+    print(f"[random importance] seed {seed}: B={B} Hq={Hq} Hkv={Hkv} T={T} seg={seg} proxy={proxy} lens={lens}",
+          flush=True)
+    q = gen.f32_to_bf16_bits(g.standard_normal((B, Hq, T, 128), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(g.standard_normal((B, Hkv, T, 128), dtype=np.float32))
+    L = np.array(lens if lens else [T] * B, dtype=np.int32)
+    imp, perm = S.spa_importance_permutation(dev(q, "bf16"), dev(k, "bf16"), seg, proxy=proxy,
+                                             seq_len=None if lens is None else dev(L))
+    torch.cuda.synchronize()
+    ref = O.key_importance(q, k, "bf16", L, proxy)
+    imp_h, perm_h = imp.cpu().numpy(), perm.cpu().numpy()
+    imp_close(imp_h, ref)
+    for b in range(B):
+        assert abs(float(imp_h[b].astype(np.float64).sum()) - 1.0) < 1e-4
+        check_importance_perm(perm_h[b], imp_h[b], ref[b], L[b], seg)
