@@ -225,3 +225,56 @@ def test_importance_permutation_random_sweep(seed):
     for b in range(B):
         assert abs(float(imp_h[b].astype(np.float64).sum()) - 1.0) < 1e-4
         check_importance_perm(perm_h[b], imp_h[b], ref[b], L[b], seg)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_scores_random_sweep(seed):
+    """Decode scores for random indexer shapes (any rank r that is a multiple of 4, any head count): both kernels."""
+    g = np.random.default_rng(5000 + seed)
+    H = int(g.integers(1, 17))
+    r = 4 * int(g.integers(1, 9))
+    if H * r > 1024:
+        r = 4 * max(1, 1024 // (4 * H))
+    groups = int(g.choice([d for d in range(1, H + 1) if H % d == 0]))
+    B, nKb, blk = int(g.integers(1, 5)), int(g.integers(1, 700)), int(g.choice([16, 32, 64, 128]))
+    lo = int(g.choice([-128, -8]))
+    qI = g.integers(lo, -lo, size=(B, H, r), dtype=np.int8)
+    kI = g.integers(lo, -lo, size=(B, nKb, H, r), dtype=np.int8)
+    w = g.integers(1, 5, size=(B, H), dtype=np.int8)
+    L = g.integers(1, nKb * blk + 1, size=B).astype(np.int32)
+    print(f"[random scores] seed {seed}: B={B} H={H} r={r} groups={groups} nKb={nKb} blk={blk}", flush=True)
+    got = S.spa_index_score(dev(qI), dev(kI), dev(w), blk, seq_len=dev(L), mode=S.SPA_SCORE_DECODE_GROUPED, Mq=groups)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), O.score_decode_grouped(qI, kI, w, L, blk, groups))
+    got1 = S.spa_index_score(dev(qI), dev(kI), dev(w), blk, seq_len=dev(L))
+    torch.cuda.synchronize()
+    assert np.array_equal(got1.cpu().numpy().astype(np.int64), O.score_decode(qI, kI, w, L, blk))
+
+
+@pytest.mark.parametrize("algo", ["sort", "hist"])
+@pytest.mark.parametrize("seed", range(8))
+def test_select_ties_random_sweep(seed, algo):
+    """Selection on heavily tied scores (a few distinct values): top-k lists exact, top-p by the set rule."""
+    g = np.random.default_rng(6000 + seed)
+    B, nb, blk = int(g.integers(1, 5)), int(g.integers(8, 2049)), 64
+    levels = int(g.choice([1, 2, 3, 5, 17]))
+    s = (g.integers(0, levels, size=(B, nb)) * int(g.choice([1, 100, 40000]))).astype(np.int32)
+    L = g.integers(1, nb * blk + 1, size=B).astype(np.int32)
+    n_sink, n_local = int(g.integers(0, 3)), int(g.integers(0, 5))
+    k = int(g.integers(0, nb + 1))
+    print(f"[random ties] seed {seed} {algo}: B={B} nb={nb} levels={levels} k={k} sink={n_sink} local={n_local}",
+          flush=True)
+    idx, cnt = S.spa_select_topk(dev(s), blk, n_sink, n_local, k, max(1, min(nb, n_sink + n_local + k)),
+                                 seq_len=dev(L), algo=algo)
+    ref, _ = O.select_decode(s.astype(np.int64), L, blk, n_sink, n_local, "topk", k=k)
+    assert sel_lists(idx, cnt) == ref
+    k_min = int(g.integers(0, 9))
+    k_max = int(g.integers(max(1, k_min), nb + 1))
+    p, beta = float(g.choice([0.3, 0.9, 1.0])), float(g.choice([0.0, 0.01, 0.125]))
+    idx, cnt = S.spa_select_topp(dev(s), blk, n_sink, n_local, beta, p, k_min, k_max,
+                                 max(1, min(nb, n_sink + n_local + k_max)), seq_len=dev(L), algo=algo)
+    gsel = sel_lists(idx, cnt)
+    _, info = O.select_decode(s.astype(np.int64), L, blk, n_sink, n_local, "topp", beta=beta, p=p, k_min=k_min,
+                              k_max=k_max)
+    for b in range(B):
+        check_topp_row(gsel[b], info[b], k_min, k_max, p)
