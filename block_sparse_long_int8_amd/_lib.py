@@ -31,6 +31,8 @@ SPA_SCORE_DECODE = 0
 SPA_SCORE_PREFILL_POOLED = 1
 SPA_SCORE_PREFILL_TOKENS = 2
 SPA_SCORE_DECODE_GROUPED = 3
+SPA_ORDER_SLOT = 0
+SPA_ORDER_ORIGINAL = 1
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -57,7 +59,7 @@ _SIGS = {
                                             _f, _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_sparse_decode_attn_workspace_size": (_sz, [_i, _i, _i, _i]),
     "spa_block_sparse_prefill": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
-                                      _vp, _i, _vp, _vp, _sz, _vp]),
+                                      _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "spa_segment_permute": (_i, [_vp, _vp, _i64, _i, _sz, _vp, _i, _i, _vp]),
     "spa_quantize_selector_keys": (_i, [_vp, _i64, _i, _vp, _vp, _vp]),
     "spa_index_score_q4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]),
@@ -341,25 +343,39 @@ def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
 # ----------------------------------------------------------------- prefill --
 
 def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q_blk0=0, scale=None,
-                             out_dtype=torch.float32, out=None, lse=None,
-                             want_lse=True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                             out_dtype=torch.float32, out=None, lse=None, want_lse=True, order="slot",
+                             Tq=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``order="slot"``: q, out [B, Hq, Tq, d] hold the chunk's slots.  ``order="original"``:
+    q, out [B, Hq, T, d] (and lse [B, Hq, T]) in original token order, rows q_pos[b, slot];
+    Tq (the chunk length) defaults to T - q_blk0*blk."""
     _dev(q, "q", torch.bfloat16)
     _dev(k, "k", torch.bfloat16)
     _dev(v, "v", torch.bfloat16)
     _dev(idx, "idx", torch.int32)
     _dev(count, "count", torch.int32)
-    B, Hq, Tq, d = q.shape
+    if order not in ("slot", "original"):
+        raise ValueError(f"order must be 'slot' or 'original', not {order!r}")
+    B, Hq, Tr, d = q.shape
     _, Hkv, T, _ = k.shape
+    if order == "slot":
+        Tq = Tr if Tq is None else Tq
+        if Tq != Tr:
+            raise ValueError("in slot order q holds exactly the chunk's Tq rows")
+    else:
+        if Tr != T:
+            raise ValueError("in original order q holds the whole sequence (T rows)")
+        Tq = T - q_blk0 * blk if Tq is None else Tq
     cap = idx.shape[-1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((B, Hq, Tq, d), dtype=out_dtype, device=q.device)
+        out = torch.empty((B, Hq, Tr, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
-        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, Tr), dtype=torch.float32, device=q.device)
     st = lib().spa_block_sparse_prefill(_ptr(q), q_blk0, Tq, _ptr(k), _ptr(v), _ptr(q_pos), _ptr(k_pos), _ptr(idx),
                                         _ptr(count), cap, blk, B, Hq, Hkv, d, T, float(scale), _ptr(out),
-                                        _io_dtype(out), _ptr(lse), None, 0, _stream())
+                                        _io_dtype(out), _ptr(lse), SPA_ORDER_ORIGINAL if order == "original"
+                                        else SPA_ORDER_SLOT, None, 0, _stream())
     _check("spa_block_sparse_prefill", st)
     return out, lse
 

@@ -147,19 +147,24 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   }
   const bool force_mask = (i + 1) * BLK > a.Tq;
 
-  const size_t qrow0 = ((size_t)b * a.Hq + h) * (size_t)a.Tq;
+  // this lane's row of q, out and lse: its slot in the chunk, or in original
+  // order its query's position (q rows read and O rows written where they
+  // belong, which makes the permutation of Q and the inverse permutation of O
+  // unnecessary)
+  const size_t qrow0 = a.orig_order ? (((size_t)b * a.Hq + h) * (size_t)a.T + (row_ok ? qp : 0))
+                                    : (((size_t)b * a.Hq + h) * (size_t)a.Tq + (row_ok ? row : 0));
   if (nsel <= 0) {
     if (active && row_ok) {
       for (int d0 = 64 * hi; d0 < 64 * hi + 64; d0 += 8) {
         if (a.out_bf16) {
-          *reinterpret_cast<uint4*>((uint16_t*)a.out + (qrow0 + row) * D + d0) = uint4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<uint4*>((uint16_t*)a.out + qrow0 * D + d0) = uint4{0u, 0u, 0u, 0u};
         } else {
-          float* o = (float*)a.out + (qrow0 + row) * D + d0;
+          float* o = (float*)a.out + qrow0 * D + d0;
           *reinterpret_cast<float4*>(o) = float4{0.f, 0.f, 0.f, 0.f};
           *reinterpret_cast<float4*>(o + 4) = float4{0.f, 0.f, 0.f, 0.f};
         }
       }
-      if (a.lse && hi == 0) a.lse[qrow0 + row] = -INFINITY;
+      if (a.lse && hi == 0) a.lse[qrow0] = -INFINITY;
     }
     return;
   }
@@ -176,7 +181,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   // Q^T fragments (B operand): lane holds query slot row, d = 16ks + 8hi .. +7
   bf16x8 qf[8];
   {
-    const uint16_t* qb = (const uint16_t*)a.q + (qrow0 + (row_ok ? row : 0)) * D;
+    const uint16_t* qb = (const uint16_t*)a.q + qrow0 * D;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       uint4 v = *reinterpret_cast<const uint4*>(qb + 16 * ks + 8 * hi);
@@ -311,7 +316,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   const float lt = lsum + shfl_xor_f(lsum, 32);
   const bool empty = !(lt > 0.f);
   const float inv = empty ? 0.f : 1.f / lt;
-  const size_t obase = (qrow0 + row) * D + 4 * hi;
+  const size_t obase = qrow0 * D + 4 * hi;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -324,7 +329,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
       else
         *reinterpret_cast<float4*>((float*)a.out + off) = float4{v0, v1, v2, v3};
     }
-  if (a.lse && hi == 0) a.lse[qrow0 + row] = empty ? -INFINITY : (mrun + log2f(lt)) * kLn2;
+  if (a.lse && hi == 0) a.lse[qrow0] = empty ? -INFINITY : (mrun + log2f(lt)) * kLn2;
 }
 
 }  // namespace

@@ -156,6 +156,7 @@ struct PrefillArgs {
   void* out;
   int out_bf16;
   float* lse;
+  int orig_order;  // q, out, lse indexed by original position q_pos[b, slot] ([.., T, ..]) instead of slot
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

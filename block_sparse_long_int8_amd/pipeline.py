@@ -2,9 +2,10 @@
 
 DecodeStep:  spa_index_score -> spa_select_topk | spa_select_topp (or both in
              one launch: spa_score_select_decode) -> spa_sparse_decode_attn
-PrefillStep: spa_segment_permute (Q, K, V, per-token indexer vectors)
+PrefillStep: spa_segment_permute (K, V, per-token indexer vectors)
              -> spa_index_score (per-token, pooled) -> spa_select_topk (prefill rows)
-             -> spa_block_sparse_prefill -> spa_segment_permute (inverse, on O)
+             -> spa_block_sparse_prefill (original order: Q read and O written at
+                each query's original position, so neither is permuted)
 
 Only marshalling lives here; every step runs in the HIP library.
 """
@@ -186,14 +187,16 @@ class PrefillStep:
 
     The permutation is the caller's (``perm`` [T], shared by the batch, or
     [B, T]) or, with ``spec.perm_kind == "importance"``, computed on the device
-    from Q and K by spa_importance_permutation (one per sequence).
+    from Q and K by spa_importance_permutation (one per sequence).  K, V and
+    the indexer vectors are permuted into slot order; the attention reads Q
+    and writes O (``out``) and the log-sum-exp (``lse``) in the original token
+    order.
     """
 
     def __init__(self, spec: PrefillSpec, device="cuda"):
         self.spec = s = spec
         dev = torch.device(device)
         bf = torch.bfloat16
-        self.qp = torch.empty((s.B, s.Hq, s.T, s.d), dtype=bf, device=dev)
         self.kp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
         self.vp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
         self.qIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
@@ -203,9 +206,8 @@ class PrefillStep:
         self.count = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
         n = L.spa_index_score_workspace_size(s.B, s.H_idx, s.r, s.nb, s.nb, L.SPA_SCORE_PREFILL_TOKENS)
         self.score_ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
-        self.out_slot = torch.empty((s.B, s.Hq, s.T, s.d), dtype=s.out_dtype, device=dev)
-        self.lse_slot = torch.empty((s.B, s.Hq, s.T), dtype=torch.float32, device=dev)
-        self.out = torch.empty_like(self.out_slot)
+        self.out = torch.empty((s.B, s.Hq, s.T, s.d), dtype=s.out_dtype, device=dev)
+        self.lse = torch.empty((s.B, s.Hq, s.T), dtype=torch.float32, device=dev)
         self.pos = None
         if s.perm_kind == "importance":
             self.imp = torch.empty((s.B, s.T), dtype=torch.float32, device=dev)
@@ -238,9 +240,8 @@ class PrefillStep:
             L.spa_segment_permute(src[b], perm[b], s.seg, dim=dim - 1, inverse=inverse, dst=dst[b])
         return dst
 
-    def permute_inputs(self, q, k, v, perm):
-        """Q, K, V into slot order (segment-wise permutation along the token axis)."""
-        self._permute(q, perm, 2, self.qp)
+    def permute_kv(self, k, v, perm):
+        """K and V into slot order (segment-wise permutation along the token axis)."""
         self._permute(k, perm, 2, self.kp)
         self._permute(v, perm, 2, self.vp)
 
@@ -267,21 +268,17 @@ class PrefillStep:
         self.select()
         return self.idx, self.count
 
-    def attend(self):
+    def attend(self, q):
+        """Attention of every query (q and out in original order) over its block's selected key blocks."""
         s = self.spec
-        return L.spa_block_sparse_prefill(self.qp, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
-                                          k_pos=self.pos, out=self.out_slot, lse=self.lse_slot)
-
-    def unpermute(self, perm):
-        """O from slot order back to the original token order."""
-        return self._permute(self.out_slot, perm, 2, self.out, inverse=True)
+        return L.spa_block_sparse_prefill(q, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
+                                          k_pos=self.pos, out=self.out, lse=self.lse, order="original")
 
     def __call__(self, q, k, v, qI_tok, kI_tok, w, perm=None):
         if self.spec.perm_kind == "importance":
             perm = self.importance(q, k)
         self.set_perm(perm)
-        self.permute_inputs(q, k, v, perm)
+        self.permute_kv(k, v, perm)
         self.front(qI_tok, kI_tok, w, perm)
-        self.attend()
-        self.unpermute(perm)
+        self.attend(q)
         return self.out

@@ -51,6 +51,10 @@ typedef int spa_status;
 #define SPA_F32 0
 #define SPA_BF16 1
 
+/* row order of the query, output and lse tensors of spa_block_sparse_prefill */
+#define SPA_ORDER_SLOT 0     /* the chunk's slots, in slot (permuted) order        */
+#define SPA_ORDER_ORIGINAL 1 /* the whole sequence, in original token order        */
+
 /* spa_index_score modes */
 #define SPA_SCORE_DECODE 0         /* one query row per sequence against its key blocks  */
 #define SPA_SCORE_PREFILL_POOLED 1 /* query blocks x key blocks, block vectors given     */
@@ -285,20 +289,28 @@ spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, co
  * permuted inside segments with causality kept on the original positions
  * (§2); HGA page: exact softmax over the selected tokens.
  *
- * q [B, Hq, Tq, d] holds query slots q_blk0*blk .. q_blk0*blk+Tq-1 (slot order);
- * k, v [B, Hkv, T, d].  q_pos, k_pos [B, T] int32 give each slot's original
+ * The chunk is query slots q_blk0*blk .. q_blk0*blk+Tq-1; k, v [B, Hkv, T, d]
+ * are in slot order.  q_pos, k_pos [B, T] int32 give each slot's original
  * position (NULL = identity).  Query slot u in block a = q_blk0 + i attends the
  * key slots t of blocks idx[b, i, 0..count[b,i]-1] (idx [B, Mq, cap], Mq =
  * ceil(Tq/blk), count [B, Mq]) with t < T and k_pos[t] <= q_pos[u].
- * out [B, Hq, Tq, d] (SPA_F32 or SPA_BF16); lse [B, Hq, Tq] fp32 (may be NULL).
- * A query with no visible key gets out = 0 and lse = -inf.
+ * order selects where query rows are read and written:
+ *   SPA_ORDER_SLOT:     q [B, Hq, Tq, d], out [B, Hq, Tq, d], lse [B, Hq, Tq],
+ *                       row u - q_blk0*blk for slot u;
+ *   SPA_ORDER_ORIGINAL: q [B, Hq, T, d], out [B, Hq, T, d], lse [B, Hq, T] in
+ *                       the original token order, row q_pos[b, u] for slot u
+ *                       (only the chunk's rows are read and written).  This
+ *                       spares the caller the permutation of Q and the
+ *                       inverse permutation of O (PBS-Attn §2).
+ * out is SPA_F32 or SPA_BF16; lse fp32 (may be NULL).  A query with no visible
+ * key gets out = 0 and lse = -inf.
  * Supported: bf16 inputs, d == 128, blk == 64, Hq % Hkv == 0.  No workspace.
  */
 spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const void* k,
                                     const void* v, const int32_t* q_pos, const int32_t* k_pos,
                                     const int32_t* idx, const int32_t* count, int cap, int blk,
                                     int B, int Hq, int Hkv, int d, int T, float scale, void* out,
-                                    int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                    int out_dtype, float* lse, int order, void* ws, size_t ws_bytes,
                                     void* stream);
 
 /*

@@ -115,7 +115,9 @@ def test_decode_attn_rejections(name):
 def test_prefill_and_permute_rejections():
     f = L.spa_block_sparse_prefill
     base = [_fake(), 0, 4096, _fake(2), _fake(3), N, N, _fake(4), _fake(5), 34, 64, 1, 32, 8, 128, 4096, 0.088,
-            _fake(6), S.SPA_F32, N, N, 0, N]
+            _fake(6), S.SPA_F32, N, S.SPA_ORDER_SLOT, N, 0, N]
+    b = list(base); b[20] = 2
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # unknown row order
     b = list(base); b[10] = 32
     assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # blk must be 64
     b = list(base); b[14] = 64

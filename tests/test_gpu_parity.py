@@ -594,7 +594,7 @@ def test_prefill_pipeline_parity():
     assert sel_lists(step.idx, step.count) == front["sel"]
     ref = O.prefill_step(inp, front=front)
     attn_close(out.cpu().numpy(), ref["o"])
-    assert np.allclose(step.lse_slot.cpu().numpy(), ref["lse_slot"], atol=1e-4, rtol=1e-5)
+    assert np.allclose(step.lse.cpu().numpy(), ref["lse"], atol=1e-4, rtol=1e-5)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,T,seg,proxy,lens", [
@@ -651,22 +651,31 @@ def test_importance_prefill_pipeline_parity():
 
 
 def test_prefill_chunked_equals_one_shot_bitwise():
+    # chunks of 512 query slots, in original order (rows perm[slot] of q / out / lse) and in slot order,
+    # give exactly the rows of the one-shot call
     cfg = gen.SMALL_PREFILL
     inp, t = _prefill_inputs(cfg)
     step = S.PrefillStep(_pspec(cfg))
     step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
     torch.cuda.synchronize()
-    full = step.out_slot.clone()
+    full, full_lse = step.out.clone(), step.lse.clone()
     blk, T = cfg.blk, cfg.T
+    perm = inp["perm"]
     for c0 in range(0, T, 512):
         b0 = c0 // blk
-        qc = step.qp[:, :, c0:c0 + 512].contiguous()
         idx = step.idx[:, b0:b0 + 512 // blk].contiguous()
         cnt = step.count[:, b0:b0 + 512 // blk].contiguous()
-        oc, _ = S.spa_block_sparse_prefill(qc, step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
-                                           q_blk0=b0)
+        rows = torch.from_numpy(perm[c0:c0 + 512].astype(np.int64)).cuda()
+        oc, lc = S.spa_block_sparse_prefill(t["q"], step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
+                                            q_blk0=b0, Tq=512, order="original")
+        qs = t["q"][:, :, rows].contiguous()  # the chunk's queries in slot order
+        os_, ls_ = S.spa_block_sparse_prefill(qs, step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
+                                              q_blk0=b0)
         torch.cuda.synchronize()
-        assert torch.equal(oc, full[:, :, c0:c0 + 512])
+        assert torch.equal(oc[:, :, rows], full[:, :, rows])
+        assert torch.equal(lc[:, :, rows], full_lse[:, :, rows])
+        assert torch.equal(os_, full[:, :, rows])
+        assert torch.equal(ls_, full_lse[:, :, rows])
 
 
 def test_prefill_all_blocks_equals_dense_causal():

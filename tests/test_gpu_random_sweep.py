@@ -138,10 +138,10 @@ def test_prefill_random_sweep(seed):
     assert sel_lists(step.idx, step.count) == front["sel"]
     ref = O.prefill_step(inp, front=front)
     attn_close(out.cpu().numpy(), ref["o"])
-    lse = step.lse_slot.cpu().numpy()
-    fin = np.isfinite(ref["lse_slot"])
+    lse = step.lse.cpu().numpy()
+    fin = np.isfinite(ref["lse"])
     assert (np.isfinite(lse) == fin).all()
-    assert np.allclose(lse[fin], ref["lse_slot"][fin], atol=1e-4, rtol=1e-5)
+    assert np.allclose(lse[fin], ref["lse"][fin], atol=1e-4, rtol=1e-5)
 
 
 def _draw_variant(seed: int):
