@@ -3,7 +3,10 @@
 // PBS-Attn page: block-sparse attention computes only the key blocks of a
 // precomputed list ("Declaración del Problema"); tokens may be permuted inside
 // segments, with causality enforced on the original positions (§2).  HGA
-// page: the softmax is exact over the selected tokens.
+// page: the softmax is exact over the selected tokens.  K and V come in slot
+// (permuted) order; query rows are read, and output rows written, either in
+// the chunk's slot order or at each query's original position, which takes
+// the permutation of Q and the inverse permutation of O off the pipeline.
 //
 // One workgroup = one (sequence, KV head, query block of 64 slots) and up to
 // four query heads of that KV head: eight waves, wave w owns query head
