@@ -278,3 +278,57 @@ def test_select_ties_random_sweep(seed, algo):
                               k_max=k_max)
     for b in range(B):
         check_topp_row(gsel[b], info[b], k_min, k_max, p)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_segment_permute_random_sweep(seed):
+    """Segment permutation and its inverse on random row sizes (16-byte, 4-byte and byte paths), lengths and segments."""
+    g = np.random.default_rng(7000 + seed)
+    T = int(g.integers(1, 5001))
+    seg = int(g.integers(1, T + 1)) if g.random() < 0.7 else int(g.choice([64, 4096]))
+    perm = np.concatenate([s0 + g.permutation(min(seg, T - s0)) for s0 in range(0, T, seg)]).astype(np.int32)
+    dt = (np.int8, np.int16, np.float32)[int(g.integers(3))]
+    tails = ((128,), (8, 16), (3,), (5, 7), (1,), (33,))
+    tail = tails[int(g.integers(len(tails)))]
+    outer = tuple(int(x) for x in g.integers(1, 4, size=int(g.integers(0, 3))))
+    shape = outer + (T,) + tail
+    x = g.integers(-100, 100, size=shape).astype(dt)
+    dim = len(outer)
+    print(f"[random permute] seed {seed}: shape={shape} dtype={np.dtype(dt).name} seg={seg}", flush=True)
+    y = S.spa_segment_permute(dev(x), dev(perm), seg, dim)
+    z = S.spa_segment_permute(y, dev(perm), seg, dim, inverse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), O.segment_permute(x, perm, dim))
+    assert np.array_equal(z.cpu().numpy(), x)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_scores_prefill_random_sweep(seed):
+    """Prefill block-pair scores from pooled block vectors (a chunk of query blocks at q_blk0) and from per-token
+    vectors with ragged sequence lengths."""
+    g = np.random.default_rng(8000 + seed)
+    B, H, blk = int(g.integers(1, 4)), int(g.integers(1, 17)), 64
+    nKb = int(g.integers(1, 120))
+    q_blk0 = int(g.integers(0, nKb))
+    M = int(g.integers(1, nKb - q_blk0 + 1))
+    lo = int(g.choice([-128, -8]))
+    qIb = g.integers(lo, -lo, size=(B, M, H, 16), dtype=np.int8)
+    kIb = g.integers(lo, -lo, size=(B, nKb, H, 16), dtype=np.int8)
+    w = g.integers(1, 5, size=(B, M, H), dtype=np.int8)
+    print(f"[random prefill scores] seed {seed}: B={B} H={H} nKb={nKb} q_blk0={q_blk0} M={M}", flush=True)
+    got = S.spa_index_score(dev(qIb), dev(kIb), dev(w), blk, mode=S.SPA_SCORE_PREFILL_POOLED, q_blk0=q_blk0)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), O.score_prefill(qIb, kIb, w, q_blk0=q_blk0))
+    # per-token vectors of whole blocks, pooled by the library; ragged lengths pool the tokens each block has
+    T = nKb * blk
+    x = g.integers(lo, -lo, size=(B, T, H, 16), dtype=np.int8)
+    wt = g.integers(1, 5, size=(B, nKb, H), dtype=np.int8)
+    L = g.integers(1, T + 1, size=B).astype(np.int32)
+    s = S.spa_index_score(dev(x), dev(x), dev(wt), blk, seq_len=dev(L), mode=S.SPA_SCORE_PREFILL_TOKENS)
+    torch.cuda.synchronize()
+    sh = s.cpu().numpy()
+    for b in range(B):
+        pooled = O.pool_blocks(x[b:b + 1, :L[b]], blk)
+        nb = pooled.shape[1]
+        ref = O.score_prefill(pooled, pooled, wt[b:b + 1, :nb])
+        assert np.array_equal(sh[b:b + 1, :nb, :nb].astype(np.int64), ref)
