@@ -33,6 +33,7 @@ SPA_SCORE_PREFILL_TOKENS = 2
 SPA_SCORE_DECODE_GROUPED = 3
 SPA_ORDER_SLOT = 0
 SPA_ORDER_ORIGINAL = 1
+SPA_ORDER_KV_ORIGINAL = 2
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -344,10 +345,13 @@ def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
 
 def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q_blk0=0, scale=None,
                              out_dtype=torch.float32, out=None, lse=None, want_lse=True, order="slot",
-                             Tq=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                             Tq=None, kv_order="slot") -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """``order="slot"``: q, out [B, Hq, Tq, d] hold the chunk's slots.  ``order="original"``:
     q, out [B, Hq, T, d] (and lse [B, Hq, T]) in original token order, rows q_pos[b, slot];
-    Tq (the chunk length) defaults to T - q_blk0*blk."""
+    Tq (the chunk length) defaults to T - q_blk0*blk.  ``kv_order="original"``: k, v in
+    original order (slot t is row k_pos[b, t])."""
+    if kv_order not in ("slot", "original"):
+        raise ValueError(f"kv_order must be 'slot' or 'original', not {kv_order!r}")
     _dev(q, "q", torch.bfloat16)
     _dev(k, "k", torch.bfloat16)
     _dev(v, "v", torch.bfloat16)
@@ -374,8 +378,10 @@ def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q
         lse = torch.empty((B, Hq, Tr), dtype=torch.float32, device=q.device)
     st = lib().spa_block_sparse_prefill(_ptr(q), q_blk0, Tq, _ptr(k), _ptr(v), _ptr(q_pos), _ptr(k_pos), _ptr(idx),
                                         _ptr(count), cap, blk, B, Hq, Hkv, d, T, float(scale), _ptr(out),
-                                        _io_dtype(out), _ptr(lse), SPA_ORDER_ORIGINAL if order == "original"
-                                        else SPA_ORDER_SLOT, None, 0, _stream())
+                                        _io_dtype(out), _ptr(lse),
+                                        (SPA_ORDER_ORIGINAL if order == "original" else SPA_ORDER_SLOT)
+                                        | (SPA_ORDER_KV_ORIGINAL if kv_order == "original" else 0), None, 0,
+                                        _stream())
     _check("spa_block_sparse_prefill", st)
     return out, lse
 

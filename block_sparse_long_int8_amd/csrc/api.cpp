@@ -367,7 +367,8 @@ spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const voi
   (void)ws;
   (void)ws_bytes;
   REQUIRE(out_dtype == SPA_F32 || out_dtype == SPA_BF16, SPA_ERR_INVALID_ARG, "unknown out_dtype %d", out_dtype);
-  REQUIRE(order == SPA_ORDER_SLOT || order == SPA_ORDER_ORIGINAL, SPA_ERR_INVALID_ARG, "unknown order %d", order);
+  REQUIRE(order >= 0 && order <= (SPA_ORDER_ORIGINAL | SPA_ORDER_KV_ORIGINAL), SPA_ERR_INVALID_ARG,
+          "unknown order flags %d", order);
   REQUIRE(B >= 0 && Tq >= 0 && q_blk0 >= 0 && Hq >= 1 && Hkv >= 1 && d >= 1 && T >= 1 && cap >= 1,
           SPA_ERR_INVALID_ARG, "bad sizes");
   REQUIRE(Hq % Hkv == 0, SPA_ERR_INVALID_ARG, "Hq %d not a multiple of Hkv %d", Hq, Hkv);
@@ -401,7 +402,8 @@ spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const voi
   a.out = out;
   a.out_bf16 = out_dtype == SPA_BF16;
   a.lse = lse;
-  a.orig_order = order == SPA_ORDER_ORIGINAL;
+  a.orig_order = (order & SPA_ORDER_ORIGINAL) != 0;
+  a.kv_orig = (order & SPA_ORDER_KV_ORIGINAL) != 0;
   return from_hip(spa::launch_prefill(a, (hipStream_t)stream), fn);
 }
 

@@ -3,10 +3,12 @@
 // PBS-Attn page: block-sparse attention computes only the key blocks of a
 // precomputed list ("Declaración del Problema"); tokens may be permuted inside
 // segments, with causality enforced on the original positions (§2).  HGA
-// page: the softmax is exact over the selected tokens.  K and V come in slot
-// (permuted) order; query rows are read, and output rows written, either in
-// the chunk's slot order or at each query's original position, which takes
-// the permutation of Q and the inverse permutation of O off the pipeline.
+// page: the softmax is exact over the selected tokens.  Query rows are read,
+// and output rows written, either in the chunk's slot order or at each
+// query's original position; K and V rows are read either in slot order or
+// at each key's original position.  The original orders take the
+// permutations of Q, K and V and the inverse permutation of O off the
+// pipeline: the kernel applies them as it reads and writes.
 //
 // One workgroup = one (sequence, KV head, query block of 64 slots) and up to
 // four query heads of that KV head: eight waves, wave w owns query head
@@ -15,7 +17,8 @@
 // workgroup into LDS (direct global->LDS 16-byte loads, 16-byte chunks
 // XOR-swizzled by row so that the MFMA operand reads are free of bank
 // conflicts) and read by all eight waves.  K, V and key positions are
-// double-buffered: tile u+1 streams in while tile u is computed.  The
+// double-buffered: tile u+1 streams in while tile u is computed, and the
+// block number and K/V source rows of tile u+2 are loaded meanwhile.  The
 // operand fragments of the two products are read from LDS one step ahead of
 // the MFMAs that consume them.
 //
@@ -88,16 +91,17 @@ __device__ __forceinline__ int wave_min_i(int v) {
 // moves rows 8w..8w+7 of K and of V: each instruction writes 1 KB (4 rows) at
 // LDS base + 16*lane, so lane l fetches the global chunk that the swizzle
 // places at its slot.  Rows past T re-read row T-1 (masked later).
+// src[n4] is the row of K and V that holds this lane's slot of the tile: the
+// slot itself, or with K/V in original order its original position.
 __device__ __forceinline__ void stage(Smem& sm, const uint16_t* __restrict__ kb,
                                       const uint16_t* __restrict__ vb, const int32_t* __restrict__ kpos,
-                                      int tok0, int T, int slot, int w, int lane) {
+                                      int tok0, int T, int slot, int w, int lane, const int (&src)[2]) {
   const int cpos = lane & 15;
 #pragma unroll
   for (int n4 = 0; n4 < 2; ++n4) {
     const int r0 = 8 * w + 4 * n4;
     const int r = r0 + (lane >> 4);
-    const int t = min(tok0 + r, T - 1);
-    const size_t row = (size_t)t * D;
+    const size_t row = (size_t)src[n4] * D;
     __builtin_amdgcn_global_load_lds(kb + row + 8 * (cpos ^ (r & 15)), (lds_void_t*)(sm.k[slot] + r0 * ROWB), 16, 0, 0);
     __builtin_amdgcn_global_load_lds(vb + row + 8 * (cpos ^ vsw(r)), (lds_void_t*)(sm.v[slot] + r0 * ROWB), 16, 0, 0);
   }
@@ -177,9 +181,26 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   const uint16_t* vb = (const uint16_t*)a.v + kv_off;
   const int32_t* kpos = a.k_pos ? a.k_pos + (size_t)b * a.T : nullptr;
 
-  // block list, 64 entries per register chunk (read back with readlane)
+  // K/V rows of this lane's two staging slots in the tile at tok (loaded from
+  // k_pos when K and V are in original order, so a tile's rows are known one
+  // tile before it is staged)
+  auto kv_src = [&](int tok, int (&src)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n4 = 0; n4 < 2; ++n4) {
+      const int t = min(tok + 8 * w + 4 * n4 + (lane >> 4), a.T - 1);
+      src[n4] = a.kv_orig && kpos ? kpos[t] : t;
+    }
+  };
+  // block list, 64 entries per register chunk (read back with readlane); the
+  // chunk holds the entry two tiles ahead, tk0/tk1 the token offsets of tiles
+  // u and u+1
   int chunk = lane < nsel ? lst[lane] : 0;
-  stage(sm, kb, vb, kpos, __builtin_amdgcn_readfirstlane(chunk) * BLK, a.T, 0, w, lane);
+  int tk0 = __builtin_amdgcn_readfirstlane(chunk) * BLK;
+  int tk1 = nsel > 1 ? __builtin_amdgcn_readlane(chunk, 1) * BLK : 0;
+  int src1[2], src2[2] = {0, 0};
+  kv_src(tk0, src1);
+  stage(sm, kb, vb, kpos, tk0, a.T, 0, w, lane, src1);
+  kv_src(tk1, src1);
 
   // Q^T fragments (B operand): lane holds query slot row, d = 16ks + 8hi .. +7
   bf16x8 qf[8];
@@ -203,12 +224,22 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
 
   for (int u = 0; u < nsel; ++u) {
     const int slot = u & 1;
-    const int tok0 = __builtin_amdgcn_readlane(chunk, u & 63) * BLK;
-    if (((u + 1) & 63) == 0 && u + 1 < nsel) chunk = u + 1 + lane < nsel ? lst[u + 1 + lane] : 0;
+    const int tok0 = tk0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile u have landed
     __syncthreads();
-    if (u + 1 < nsel)
-      stage(sm, kb, vb, kpos, __builtin_amdgcn_readlane(chunk, (u + 1) & 63) * BLK, a.T, slot ^ 1, w, lane);
+    // tile u+2's entry and rows first: a wait they may need then comes before
+    // the next tile's loads are issued
+    int tk2 = 0;
+    if (u + 2 < nsel) {
+      if (((u + 2) & 63) == 0) chunk = u + 2 + lane < nsel ? lst[u + 2 + lane] : 0;
+      tk2 = __builtin_amdgcn_readlane(chunk, (u + 2) & 63) * BLK;
+      kv_src(tk2, src2);
+    }
+    if (u + 1 < nsel) stage(sm, kb, vb, kpos, tk1, a.T, slot ^ 1, w, lane, src1);
+    tk0 = tk1;
+    tk1 = tk2;
+    src1[0] = src2[0];
+    src1[1] = src2[1];
     const bool need_mask =
         force_mask || tok0 + BLK > a.T || __any((int)(tok0 + lane < a.T && sm.pos[slot][lane] > qmin));
     if (!active) continue;

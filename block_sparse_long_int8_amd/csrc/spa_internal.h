@@ -157,6 +157,7 @@ struct PrefillArgs {
   int out_bf16;
   float* lse;
   int orig_order;  // q, out, lse indexed by original position q_pos[b, slot] ([.., T, ..]) instead of slot
+  int kv_orig;     // k, v in original order: slot t's row is k_pos[b, t]
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

@@ -187,18 +187,16 @@ class PrefillStep:
 
     The permutation is the caller's (``perm`` [T], shared by the batch, or
     [B, T]) or, with ``spec.perm_kind == "importance"``, computed on the device
-    from Q and K by spa_importance_permutation (one per sequence).  K, V and
-    the indexer vectors are permuted into slot order; the attention reads Q
-    and writes O (``out``) and the log-sum-exp (``lse``) in the original token
-    order.
+    from Q and K by spa_importance_permutation (one per sequence).  Only the
+    per-token indexer vectors are permuted into slot order (the pooling needs
+    each block's tokens together); the attention reads Q, K and V and writes O
+    (``out``) and the log-sum-exp (``lse``) in the original token order, the
+    permutation applied inside the kernel through the slot positions.
     """
 
     def __init__(self, spec: PrefillSpec, device="cuda"):
         self.spec = s = spec
         dev = torch.device(device)
-        bf = torch.bfloat16
-        self.kp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
-        self.vp = torch.empty((s.B, s.Hkv, s.T, s.d), dtype=bf, device=dev)
         self.qIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
         self.kIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
         self.scores = torch.empty((s.B, s.nb, s.nb), dtype=torch.int32, device=dev)
@@ -240,11 +238,6 @@ class PrefillStep:
             L.spa_segment_permute(src[b], perm[b], s.seg, dim=dim - 1, inverse=inverse, dst=dst[b])
         return dst
 
-    def permute_kv(self, k, v, perm):
-        """K and V into slot order (segment-wise permutation along the token axis)."""
-        self._permute(k, perm, 2, self.kp)
-        self._permute(v, perm, 2, self.vp)
-
     def permute_index(self, qI_tok, kI_tok, perm):
         """The per-token indexer vectors into slot order."""
         self._permute(qI_tok, perm, 1, self.qIp)
@@ -268,17 +261,16 @@ class PrefillStep:
         self.select()
         return self.idx, self.count
 
-    def attend(self, q):
-        """Attention of every query (q and out in original order) over its block's selected key blocks."""
+    def attend(self, q, k, v):
+        """Attention of every query over its block's selected key blocks (q, k, v and out in original order)."""
         s = self.spec
-        return L.spa_block_sparse_prefill(q, self.kp, self.vp, self.idx, self.count, s.blk, q_pos=self.pos,
-                                          k_pos=self.pos, out=self.out, lse=self.lse, order="original")
+        return L.spa_block_sparse_prefill(q, k, v, self.idx, self.count, s.blk, q_pos=self.pos, k_pos=self.pos,
+                                          out=self.out, lse=self.lse, order="original", kv_order="original")
 
     def __call__(self, q, k, v, qI_tok, kI_tok, w, perm=None):
         if self.spec.perm_kind == "importance":
             perm = self.importance(q, k)
         self.set_perm(perm)
-        self.permute_kv(k, v, perm)
         self.front(qI_tok, kI_tok, w, perm)
-        self.attend(q)
+        self.attend(q, k, v)
         return self.out

@@ -51,9 +51,10 @@ typedef int spa_status;
 #define SPA_F32 0
 #define SPA_BF16 1
 
-/* row order of the query, output and lse tensors of spa_block_sparse_prefill */
-#define SPA_ORDER_SLOT 0     /* the chunk's slots, in slot (permuted) order        */
-#define SPA_ORDER_ORIGINAL 1 /* the whole sequence, in original token order        */
+/* row orders of spa_block_sparse_prefill (the two flags combine) */
+#define SPA_ORDER_SLOT 0        /* every tensor in slot (permuted) order              */
+#define SPA_ORDER_ORIGINAL 1    /* q, out, lse: the whole sequence, original order    */
+#define SPA_ORDER_KV_ORIGINAL 2 /* k, v: original order, slot t's row is k_pos[b, t]  */
 
 /* spa_index_score modes */
 #define SPA_SCORE_DECODE 0         /* one query row per sequence against its key blocks  */
@@ -289,19 +290,23 @@ spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, co
  * permuted inside segments with causality kept on the original positions
  * (§2); HGA page: exact softmax over the selected tokens.
  *
- * The chunk is query slots q_blk0*blk .. q_blk0*blk+Tq-1; k, v [B, Hkv, T, d]
- * are in slot order.  q_pos, k_pos [B, T] int32 give each slot's original
- * position (NULL = identity).  Query slot u in block a = q_blk0 + i attends the
+ * The chunk is query slots q_blk0*blk .. q_blk0*blk+Tq-1.  q_pos, k_pos [B, T]
+ * int32 give each slot's original position (NULL = identity).  Query slot u in block a = q_blk0 + i attends the
  * key slots t of blocks idx[b, i, 0..count[b,i]-1] (idx [B, Mq, cap], Mq =
  * ceil(Tq/blk), count [B, Mq]) with t < T and k_pos[t] <= q_pos[u].
- * order selects where query rows are read and written:
- *   SPA_ORDER_SLOT:     q [B, Hq, Tq, d], out [B, Hq, Tq, d], lse [B, Hq, Tq],
- *                       row u - q_blk0*blk for slot u;
- *   SPA_ORDER_ORIGINAL: q [B, Hq, T, d], out [B, Hq, T, d], lse [B, Hq, T] in
- *                       the original token order, row q_pos[b, u] for slot u
- *                       (only the chunk's rows are read and written).  This
- *                       spares the caller the permutation of Q and the
- *                       inverse permutation of O (PBS-Attn §2).
+ * order (flags) selects where rows are read and written:
+ *   queries -- without SPA_ORDER_ORIGINAL, q [B, Hq, Tq, d], out [B, Hq, Tq, d]
+ *     and lse [B, Hq, Tq] hold row u - q_blk0*blk for slot u; with it, q [B,
+ *     Hq, T, d], out [B, Hq, T, d] and lse [B, Hq, T] are in the original token
+ *     order, row q_pos[b, u] for slot u (only the chunk's rows are read and
+ *     written);
+ *   keys -- without SPA_ORDER_KV_ORIGINAL, k, v [B, Hkv, T, d] hold slot t in
+ *     row t; with it, in row k_pos[b, t] (the original order).
+ * With both flags the caller permutes nothing: the permutation of Q, K, V and
+ * the inverse permutation of O (PBS-Attn §2) happen inside the kernel.  The
+ * positions used as row numbers (q_pos with SPA_ORDER_ORIGINAL, k_pos with
+ * SPA_ORDER_KV_ORIGINAL) must lie in [0, T): they live on the device and are
+ * not checked.
  * out is SPA_F32 or SPA_BF16; lse fp32 (may be NULL).  A query with no visible
  * key gets out = 0 and lse = -inf.
  * Supported: bf16 inputs, d == 128, blk == 64, Hq % Hkv == 0.  No workspace.

@@ -116,8 +116,10 @@ def test_prefill_and_permute_rejections():
     f = L.spa_block_sparse_prefill
     base = [_fake(), 0, 4096, _fake(2), _fake(3), N, N, _fake(4), _fake(5), 34, 64, 1, 32, 8, 128, 4096, 0.088,
             _fake(6), S.SPA_F32, N, S.SPA_ORDER_SLOT, N, 0, N]
-    b = list(base); b[20] = 2
-    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # unknown row order
+    b = list(base); b[20] = 4
+    assert f(*b) == S.SPA_ERR_INVALID_ARG                      # unknown row-order flag
+    b = list(base); b[20] = -1
+    assert f(*b) == S.SPA_ERR_INVALID_ARG
     b = list(base); b[10] = 32
     assert f(*b) == S.SPA_ERR_UNSUPPORTED                      # blk must be 64
     b = list(base); b[14] = 64

@@ -651,8 +651,8 @@ def test_importance_prefill_pipeline_parity():
 
 
 def test_prefill_chunked_equals_one_shot_bitwise():
-    # chunks of 512 query slots, in original order (rows perm[slot] of q / out / lse) and in slot order,
-    # give exactly the rows of the one-shot call
+    # chunks of 512 query slots, with q / out / lse in original order (rows perm[slot]) or in slot order and
+    # k / v in original order or permuted into slot order, give exactly the rows of the one-shot call
     cfg = gen.SMALL_PREFILL
     inp, t = _prefill_inputs(cfg)
     step = S.PrefillStep(_pspec(cfg))
@@ -661,21 +661,25 @@ def test_prefill_chunked_equals_one_shot_bitwise():
     full, full_lse = step.out.clone(), step.lse.clone()
     blk, T = cfg.blk, cfg.T
     perm = inp["perm"]
+    kp = S.spa_segment_permute(t["k"], t["perm"], cfg.seg, dim=2)
+    vp = S.spa_segment_permute(t["v"], t["perm"], cfg.seg, dim=2)
+    kv = {"original": (t["k"], t["v"]), "slot": (kp, vp)}
     for c0 in range(0, T, 512):
         b0 = c0 // blk
         idx = step.idx[:, b0:b0 + 512 // blk].contiguous()
         cnt = step.count[:, b0:b0 + 512 // blk].contiguous()
         rows = torch.from_numpy(perm[c0:c0 + 512].astype(np.int64)).cuda()
-        oc, lc = S.spa_block_sparse_prefill(t["q"], step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
-                                            q_blk0=b0, Tq=512, order="original")
         qs = t["q"][:, :, rows].contiguous()  # the chunk's queries in slot order
-        os_, ls_ = S.spa_block_sparse_prefill(qs, step.kp, step.vp, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
-                                              q_blk0=b0)
-        torch.cuda.synchronize()
-        assert torch.equal(oc[:, :, rows], full[:, :, rows])
-        assert torch.equal(lc[:, :, rows], full_lse[:, :, rows])
-        assert torch.equal(os_, full[:, :, rows])
-        assert torch.equal(ls_, full_lse[:, :, rows])
+        for kvo, (k, v) in kv.items():
+            oc, lc = S.spa_block_sparse_prefill(t["q"], k, v, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
+                                                q_blk0=b0, Tq=512, order="original", kv_order=kvo)
+            os_, ls_ = S.spa_block_sparse_prefill(qs, k, v, idx, cnt, blk, q_pos=step.pos, k_pos=step.pos,
+                                                  q_blk0=b0, kv_order=kvo)
+            torch.cuda.synchronize()
+            assert torch.equal(oc[:, :, rows], full[:, :, rows]), kvo
+            assert torch.equal(lc[:, :, rows], full_lse[:, :, rows]), kvo
+            assert torch.equal(os_, full[:, :, rows]), kvo
+            assert torch.equal(ls_, full_lse[:, :, rows]), kvo
 
 
 def test_prefill_all_blocks_equals_dense_causal():

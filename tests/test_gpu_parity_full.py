@@ -141,12 +141,13 @@ def test_full_prefill_64k_parity(S):
                dev(inp["kI_tok"]), dev(inp["w"]), dev(inp["perm"]))
     torch.cuda.synchronize()
     perm = inp["perm"]
-    # permutation: sampled slots of the permuted K/V are the source rows perm[t]
+    # the segment permutation at full size: sampled slots of permuted K are the source rows perm[t]
     rows = np.array([0, 1, 4095, 4096, 30000, 65535])
-    kp = step.kp[:, :, rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    kp = S.spa_segment_permute(dev(inp["k"], "bf16"), dev(perm), cfg.seg, dim=2)
+    torch.cuda.synchronize()
+    kp = kp[:, :, rows].cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(kp, inp["k"][:, :, perm[rows]])
-    vp = step.vp[:, :, rows].cpu().view(torch.int16).numpy().view(np.uint16)
-    assert np.array_equal(vp, inp["v"][:, :, perm[rows]])
+    del kp
     print(f"[full prefill parity] {cfg.name}: oracle front end", flush=True)
     front = O.prefill_front(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
