@@ -7,6 +7,9 @@ paths wired as sequences of calls.
 from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORTED, SPA_ERR_WORKSPACE, SPA_F32,
                    SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, SPA_SCORE_DECODE_GROUPED,
                    SPA_ORDER_KV_ORIGINAL, SPA_ORDER_ORIGINAL, SPA_ORDER_SLOT,
+                   SPA_DBG_NONE, SPA_DBG_SEQ_LEN, SPA_DBG_COUNT, SPA_DBG_IDX_RANGE, SPA_DBG_IDX_ORDER, SPA_DBG_HEAD_MODE,
+                   SPA_DBG_Q_POS, SPA_DBG_K_POS, SPA_DBG_PERM_RANGE, SPA_DBG_PERM_DUP,
+                   spa_set_debug_checks, spa_debug_checks, spa_debug_error,
                    LIB_PATH,
                    SpaError, declared_symbols, lib, spa_block_sparse_prefill, spa_index_score,
                    spa_index_score_workspace_size, spa_score_select_decode, spa_segment_permute, spa_select_topk,

@@ -34,6 +34,16 @@ SPA_SCORE_DECODE_GROUPED = 3
 SPA_ORDER_SLOT = 0
 SPA_ORDER_ORIGINAL = 1
 SPA_ORDER_KV_ORIGINAL = 2
+SPA_DBG_NONE = 0
+SPA_DBG_SEQ_LEN = 1
+SPA_DBG_COUNT = 2
+SPA_DBG_IDX_RANGE = 3
+SPA_DBG_IDX_ORDER = 4
+SPA_DBG_HEAD_MODE = 5
+SPA_DBG_Q_POS = 6
+SPA_DBG_K_POS = 7
+SPA_DBG_PERM_RANGE = 8
+SPA_DBG_PERM_DUP = 9
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -45,6 +55,9 @@ _SIGS = {
     "spa_status_string": (ctypes.c_char_p, [_i]),
     "spa_last_error": (ctypes.c_char_p, []),
     "spa_version": (_i, []),
+    "spa_set_debug_checks": (None, [_i]),
+    "spa_debug_checks": (_i, []),
+    "spa_debug_error": (_i, []),
     "spa_index_score": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "spa_index_score_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "spa_select_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -97,7 +110,21 @@ def declared_symbols():
     """Function names declared in include/spa.h."""
     with open(HEADER) as f:
         text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:spa_status|size_t|const char\*|int)\s+(spa_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:spa_status|size_t|const char\*|int|void)\s+(spa_\w+)\s*\(", text, re.M)))
+
+
+def spa_set_debug_checks(on: bool) -> None:
+    """Switch the library's device-side checks of index arrays on or off (process-wide)."""
+    lib().spa_set_debug_checks(int(bool(on)))
+
+
+def spa_debug_checks() -> bool:
+    return bool(lib().spa_debug_checks())
+
+
+def spa_debug_error() -> int:
+    """SPA_DBG_* code of the last device-side check violation on this thread (SPA_DBG_NONE if none)."""
+    return int(lib().spa_debug_error())
 
 
 def _check(fn: str, status: int):

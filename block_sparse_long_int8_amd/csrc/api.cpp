@@ -5,10 +5,13 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/spa.h"
@@ -48,6 +51,72 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
     if (!(cond)) return fail(code, fn, __VA_ARGS__); \
   } while (0)
 
+// ---- device-side checks ------------------------------------------------------
+
+std::atomic<int> g_checks{-1};  // -1: not yet read from the environment
+std::mutex g_checks_lock;       // one checked call at a time: they share the device word
+thread_local int g_check_code = SPA_DBG_NONE;
+
+bool checks_on() {
+  int v = g_checks.load(std::memory_order_relaxed);
+  if (v < 0) {
+    const char* e = std::getenv("SPA_DEBUG_CHECKS");
+    int want = e && e[0] == '1' && e[1] == 0;
+    g_checks.compare_exchange_strong(v, want);
+    v = g_checks.load(std::memory_order_relaxed);
+  }
+  return v == 1;
+}
+
+const char* check_name(int code) {
+  switch (code) {
+    case SPA_DBG_SEQ_LEN: return "seq_len outside its range";
+    case SPA_DBG_COUNT: return "count outside [0, cap]";
+    case SPA_DBG_IDX_RANGE: return "listed block outside its valid range";
+    case SPA_DBG_IDX_ORDER: return "block list not strictly ascending";
+    case SPA_DBG_HEAD_MODE: return "head_mode neither 0 nor 1";
+    case SPA_DBG_Q_POS: return "q_pos outside [0, T)";
+    case SPA_DBG_K_POS: return "k_pos outside [0, T)";
+    case SPA_DBG_PERM_RANGE: return "perm value outside its segment";
+    case SPA_DBG_PERM_DUP: return "perm value repeated in its segment";
+    default: return "unknown violation";
+  }
+}
+
+// With the checks on: run the call's check kernels (launch(s) enqueues them),
+// wait, and turn a violation into SPA_ERR_INVALID_ARG.  With them off: SPA_OK.
+template <class F>
+spa_status device_checks(const char* fn, void* stream, F&& launch) {
+  if (!checks_on()) return SPA_OK;
+  g_check_code = SPA_DBG_NONE;
+  hipStream_t s = (hipStream_t)stream;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return fail(SPA_ERR_INVALID_ARG, fn, "device-side checks are on: the call waits for them and cannot be captured");
+  std::lock_guard<std::mutex> lock(g_checks_lock);
+  unsigned long long word = ~0ull;
+  hipError_t e = spa::dbg_reset(s);
+  if (e == hipSuccess) e = launch(s);
+  if (e == hipSuccess) e = spa::dbg_fetch(&word, s);
+  if (e != hipSuccess) return from_hip(e, fn);
+  if (word == ~0ull) return SPA_OK;
+  g_check_code = (int)(word >> 40);
+  return fail(SPA_ERR_INVALID_ARG, fn, "device-side check: %s (element %llu)", check_name(g_check_code),
+              word & ((1ull << 40) - 1));
+}
+
+#define DEVICE_CHECKS(...)                                                               \
+  do {                                                                                   \
+    const spa_status st_ = device_checks(fn, stream, [&](hipStream_t s_) -> hipError_t { \
+      hipError_t e_ = hipSuccess;                                                        \
+      __VA_ARGS__;                                                                       \
+      return e_;                                                                         \
+    });                                                                                  \
+    if (st_ != SPA_OK) return st_;                                                       \
+  } while (0)
+#define CHECK_STEP(call) \
+  if (e_ == hipSuccess) e_ = (call)
+
 }  // namespace
 
 extern "C" {
@@ -66,6 +135,12 @@ const char* spa_status_string(spa_status s) {
 const char* spa_last_error(void) { return g_last_error.c_str(); }
 
 int spa_version(void) { return 100; }
+
+void spa_set_debug_checks(int on) { g_checks.store(on ? 1 : 0); }
+
+int spa_debug_checks(void) { return checks_on() ? 1 : 0; }
+
+int spa_debug_error(void) { return g_check_code; }
 
 // ------------------------------------------------------------------ scores --
 
@@ -95,11 +170,14 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   REQUIRE(qI && kI && w && scores, SPA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned16(qI) && aligned16(kI) && aligned16(scores), SPA_ERR_INVALID_ARG, "qI, kI and scores must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
-  if (mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED) {
+  if (mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED)
     REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode mode needs seq_len");
+  if (mode != SPA_SCORE_DECODE && mode != SPA_SCORE_DECODE_GROUPED)
+    REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
+  if (seq_len) DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, (long long)nKb * blk, SPA_DBG_SEQ_LEN, s_)));
+  if (mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED) {
     return from_hip(spa::launch_score_decode(qI, kI, w, B, H_idx, r, Mq, nKb, seq_len, blk, scores, s), fn);
   }
-  REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
   const int8_t* qb = qI;
   const int8_t* kb = kI;
   if (mode == SPA_SCORE_PREFILL_TOKENS) {
@@ -148,6 +226,7 @@ spa_status spa_index_score_q4(const int8_t* qI, const uint8_t* codes, const uint
   REQUIRE(qI && codes && exps && w && scores && seq_len, SPA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned16(qI) && aligned16(codes) && aligned16(scores), SPA_ERR_INVALID_ARG,
           "qI, codes and scores must be 16-byte aligned");
+  DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, (long long)nKb * blk, SPA_DBG_SEQ_LEN, s_)));
   return from_hip(spa::launch_score_decode_q4(qI, codes, exps, w, B, H_idx, Mq, nKb, seq_len, blk, scores,
                                               (hipStream_t)stream),
                   fn);
@@ -185,6 +264,7 @@ static spa_status select_common(const char* fn, const int32_t* scores, int B, in
   REQUIRE(aligned16(scores) && aligned16(idx) && aligned16(count) && aligned16(qI) && aligned16(kI) &&
               aligned16(scores_out),
           SPA_ERR_INVALID_ARG, "scores, idx, count, qI, kI and scores_out must be 16-byte aligned");
+  if (seq_len) DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, (long long)nKb * blk, SPA_DBG_SEQ_LEN, s_)));
   spa::SelectArgs a;
   a.scores = scores;
   a.B = B;
@@ -305,6 +385,12 @@ static spa_status decode_common(const char* fn, int per_group, const void* q, co
   const size_t need = spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d);
   REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  DEVICE_CHECKS({
+    CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, Tcap, SPA_DBG_SEQ_LEN, s_));
+    if (head_mode) CHECK_STEP(spa::dbg_range_u8(head_mode, Hkv, 0, 1, SPA_DBG_HEAD_MODE, s_));
+    const int rows_per_seq = per_group ? Hkv : 1;
+    CHECK_STEP(spa::dbg_lists(idx, count, (long long)B * rows_per_seq, cap, rows_per_seq, seq_len, blk, 0, s_));
+  });
   spa::DecodeArgs a;
   a.q = q;
   a.k = k_cache;
@@ -381,6 +467,14 @@ spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const voi
   REQUIRE(q && k && v && idx && count && out, SPA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out), SPA_ERR_INVALID_ARG,
           "tensor pointers must be 16-byte aligned");
+  DEVICE_CHECKS({
+    const long long Mq = (Tq + blk - 1) / blk;
+    CHECK_STEP(spa::dbg_lists(idx, count, (long long)B * Mq, cap, (int)Mq, nullptr, blk, (T + blk - 1) / blk, s_));
+    if (q_pos && (order & SPA_ORDER_ORIGINAL))
+      CHECK_STEP(spa::dbg_range_i32(q_pos, (long long)B * T, 0, T - 1, SPA_DBG_Q_POS, s_));
+    if (k_pos && (order & SPA_ORDER_KV_ORIGINAL))
+      CHECK_STEP(spa::dbg_range_i32(k_pos, (long long)B * T, 0, T - 1, SPA_DBG_K_POS, s_));
+  });
   spa::PrefillArgs a;
   a.q = q;
   a.q_blk0 = q_blk0;
@@ -436,6 +530,7 @@ spa_status spa_importance_permutation(const void* q, const void* k, int B, int H
   const size_t need = spa_importance_permutation_workspace_size(B, Hq, T);
   REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
   REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (seq_len) DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, T, SPA_DBG_SEQ_LEN, s_)));
   return from_hip(spa::launch_importance(q, k, B, Hq, Hkv, T, seq_len, proxy, scale, seg, imp, perm, ws,
                                          (hipStream_t)stream),
                   fn);
@@ -452,6 +547,7 @@ spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T,
   const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
   const uintptr_t n = (uintptr_t)outer * (uintptr_t)T * row_bytes;
   REQUIRE(s0 + n <= d0 || d0 + n <= s0, SPA_ERR_INVALID_ARG, "src and dst overlap");
+  DEVICE_CHECKS(CHECK_STEP(spa::dbg_perm(perm, T, seg, s_)));
   return from_hip(spa::launch_permute(src, dst, outer, T, row_bytes, perm, inverse, (hipStream_t)stream), fn);
 }
 

@@ -165,4 +165,17 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
                           const int32_t* perm, int inverse, hipStream_t s);
 
+
+// ---- optional device-side checks (debug_checks.hip) ------------------------
+// Each launches a check kernel on s that records violations in one device word;
+// dbg_fetch copies the word back and synchronises s (all ones = no violation,
+// else (code << 40) | element index).
+hipError_t dbg_reset(hipStream_t s);
+hipError_t dbg_range_i32(const int32_t* v, long long n, long long lo, long long hi, int code, hipStream_t s);
+hipError_t dbg_range_u8(const uint8_t* v, long long n, long long lo, long long hi, int code, hipStream_t s);
+hipError_t dbg_lists(const int32_t* idx, const int32_t* count, long long rows, int cap, int rows_per_seq,
+                     const int32_t* seq_len, int blk, int nb, hipStream_t s);
+hipError_t dbg_perm(const int32_t* perm, int T, int seg, hipStream_t s);
+hipError_t dbg_fetch(unsigned long long* word, hipStream_t s);
+
 }  // namespace spa

@@ -9,8 +9,9 @@
  * the cache written by spa_quantize_selector_keys when keys enter it; the
  * spa_select_*_hist variants select without sorting)
  * and one permuted block-sparse prefill is
- *     [spa_importance_permutation ->] spa_segment_permute -> spa_index_score (prefill)
- *     -> spa_select_topk (prefill) -> spa_block_sparse_prefill -> spa_segment_permute (inverse)
+ *     [spa_importance_permutation ->] spa_segment_permute (indexer vectors)
+ *     -> spa_index_score (prefill) -> spa_select_topk (prefill)
+ *     -> spa_block_sparse_prefill (Q, K, V and O in the original token order)
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer to a dense row-major array with
@@ -22,12 +23,14 @@
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error the function returns a negative status and launches nothing.
  *     Values inside device arrays (idx, count, perm, positions, seq_len) are
- *     trusted: they must satisfy the stated ranges.
+ *     trusted: they must satisfy the stated ranges.  The optional device-side
+ *     checks (spa_set_debug_checks) verify them before a call's kernels run.
  *   - Pointers to bf16/fp32/int tensors must be 16-byte aligned.
  *   - The only process-wide state is a cache of the GPU's compute-unit count,
  *     taken on first use (it sets the decode work split and so the decode
- *     workspace size; size and call on the same device).  Calls on different
- *     streams may run concurrently as long as their workspaces do not overlap.
+ *     workspace size; size and call on the same device), and the on/off
+ *     switch of the device-side checks.  Calls on different streams may run
+ *     concurrently as long as their workspaces do not overlap.
  *   - bf16 is passed as its 16-bit pattern (uint16 storage).
  */
 #ifndef SPA_H_
@@ -70,6 +73,56 @@ const char* spa_last_error(void);
 
 /* Library version as major*10000 + minor*100 + patch. */
 int spa_version(void);
+
+/*
+ * Device-side checks of the values inside device arrays.
+ *
+ * The entry points trust the contents of their device arrays (the host cannot
+ * read them without waiting).  With the checks on, a call that reads such
+ * arrays first launches check kernels over them on its stream, waits for them
+ * (the call then blocks the host and cannot be captured into a graph: under
+ * capture it returns SPA_ERR_INVALID_ARG) and, if a value breaks the call's
+ * stated ranges, returns SPA_ERR_INVALID_ARG without launching anything else;
+ * spa_last_error() names the violation and spa_debug_error() returns its code.
+ * What is checked:
+ *   seq_len       -- spa_index_score, spa_index_score_q4, spa_select_*,
+ *                    spa_score_select_decode: 1 <= seq_len[b] <= nKb*blk;
+ *                    spa_sparse_decode_attn*: 1 <= seq_len[b] <= Tcap;
+ *                    spa_importance_permutation: 1 <= seq_len[b] <= T;
+ *   block lists   -- spa_sparse_decode_attn* and spa_block_sparse_prefill:
+ *                    0 <= count <= cap and the first count entries of each
+ *                    row strictly ascending in [0, ceil(seq_len[b]/blk))
+ *                    (decode) or [0, ceil(T/blk)) (prefill);
+ *   head_mode     -- spa_sparse_decode_attn*: every entry 0 or 1;
+ *   positions     -- spa_block_sparse_prefill: q_pos with SPA_ORDER_ORIGINAL,
+ *                    k_pos with SPA_ORDER_KV_ORIGINAL, in [0, T);
+ *   perm          -- spa_segment_permute: each perm[t] in t's segment and,
+ *                    for seg <= 262144, no value twice in a segment.
+ * The checks share one device word per GPU and run one call at a time in the
+ * process (a lock); stream and current device must be the same GPU.
+ * Off by default; the environment variable SPA_DEBUG_CHECKS=1 at the first
+ * call switches them on, spa_set_debug_checks switches them at any time.
+ */
+#define SPA_DBG_NONE 0
+#define SPA_DBG_SEQ_LEN 1    /* seq_len outside the call's range          */
+#define SPA_DBG_COUNT 2      /* count outside [0, cap]                    */
+#define SPA_DBG_IDX_RANGE 3  /* a listed block outside its valid range    */
+#define SPA_DBG_IDX_ORDER 4  /* a list not strictly ascending             */
+#define SPA_DBG_HEAD_MODE 5  /* head_mode neither 0 nor 1                 */
+#define SPA_DBG_Q_POS 6      /* q_pos used as a row number, outside [0, T) */
+#define SPA_DBG_K_POS 7      /* k_pos used as a row number, outside [0, T) */
+#define SPA_DBG_PERM_RANGE 8 /* perm[t] outside t's segment              */
+#define SPA_DBG_PERM_DUP 9   /* a value twice in one segment of perm      */
+
+/* Switch the device-side checks on (1) or off (0) for the whole process. */
+void spa_set_debug_checks(int on);
+
+/* 1 if the device-side checks are on, else 0. */
+int spa_debug_checks(void);
+
+/* Code (SPA_DBG_*) of the violation behind the last call on the calling host
+   thread that ran the device-side checks; SPA_DBG_NONE if it found none. */
+int spa_debug_error(void);
 
 /*
  * spa_index_score -- int8 indexer block scores, exact in int32.
@@ -357,8 +410,8 @@ size_t spa_importance_permutation_workspace_size(int B, int Hq, int T);
  * (permutations stay inside contiguous segments of seg tokens).
  * src and dst are viewed as [outer, T, row_bytes].  inverse == 0:
  * dst[o, t] = src[o, perm[t]]; inverse == 1: dst[o, perm[t]] = src[o, t].
- * perm [T] int32 must map every segment [s*seg, (s+1)*seg) onto itself (not
- * checked).  src and dst must not overlap.  Pointers need 16-byte alignment
+ * perm [T] int32 must map every segment [s*seg, (s+1)*seg) onto itself
+ * (checked only by the device-side checks).  src and dst must not overlap.  Pointers need 16-byte alignment
  * only when row_bytes % 16 == 0 (the fast path); otherwise any alignment.
  */
 spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,

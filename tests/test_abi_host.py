@@ -204,3 +204,21 @@ def test_int4_selector_rejections():
     assert f(*b) == S.SPA_ERR_INVALID_ARG
     b = list(base); b[4] = 0
     assert f(*b) == S.SPA_OK
+
+
+def test_debug_check_switch_and_codes():
+    # the switch is process-wide state; the codes match the header
+    was = L.spa_debug_checks()
+    try:
+        S.spa_set_debug_checks(True)
+        assert S.spa_debug_checks()
+        S.spa_set_debug_checks(False)
+        assert not S.spa_debug_checks()
+    finally:
+        L.spa_set_debug_checks(was)
+    assert L.spa_debug_error() == S.SPA_DBG_NONE
+    import re
+    with open(S.declared_symbols.__globals__["HEADER"]) as f:
+        text = f.read()
+    for name, val in re.findall(r"#define (SPA_DBG_\w+) (\d+)", text):
+        assert getattr(S, name) == int(val), name
