@@ -451,7 +451,7 @@ def bench_prefill(args, cfg):
     log(f"[bench] inputs resident: {sum(t.numel() * t.element_size() for t in x.values()) / 2**30:.2f} GiB")
 
     stages = (("importance_perm",) if importance else ()) + \
-        ("permute_index", "pool_score", "select", "attention")
+        ("pool_score", "select", "attention")
 
     def run(ev=None):
         marks = iter(range(len(stages) + 1))
@@ -467,9 +467,7 @@ def bench_prefill(args, cfg):
         else:
             perm = x["perm"]
         step.set_perm(perm)
-        step.permute_index(x["qI"], x["kI"], perm)
-        mark()
-        step.score(x["w"])
+        step.score(x["qI"], x["kI"], x["w"])
         mark()
         step.select()
         mark()
@@ -508,7 +506,7 @@ def bench_prefill(args, cfg):
     nq = cfg.nb
     score_ops = 2.0 * cfg.r * cfg.H_idx * (nq * (nq - 1) // 2) * cfg.B
     score_s = st_ms["pool_score"] * 1e-3
-    perm_bytes = cfg.B * cfg.T * (2 * cfg.H_idx * cfg.r) * 2
+    pool_bytes = cfg.B * cfg.T * (2 * cfg.H_idx * cfg.r)
     traffic = load_traffic(args.traffic_json, source_sha("prefill_attn.hip"))
     res = {
         "metric": f"block-sparse prefill tokens/s ({cfg.name}, 1 GPU); attention TFLOP/s vs bf16 MFMA peak",
@@ -537,10 +535,9 @@ def bench_prefill(args, cfg):
         "stage_timing": "a second pass of the same steps with events between stages",
         "scoring": {"int8_ops": score_ops, "tops": score_ops / score_s / 1e12,
                     "frac_of_int8_mfma_peak": score_ops / score_s / 1e12 / INT8_MFMA_PEAK_TOPS,
-                    "note": "pool + score launch: two per-token pooling passes and the block-pair scoring"},
-        "permute": {"bytes": perm_bytes, "gbs": perm_bytes / (st_ms["permute_index"] * 1e-3) / 1e9,
-                    "note": "the int8 indexer vectors only: the attention reads Q, K, V and writes O in "
-                            "original token order"},
+                    "pool_read_bytes": pool_bytes,
+                    "note": "one pooling launch over both per-token tensors (gathered through the permutation) "
+                            "and the block-pair scoring launch"},
         "selected_blocks": {"mean": float(counts.mean()), "max": int(counts.max())},
     }
     if importance:

@@ -8,7 +8,7 @@ from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORT
                    SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, SPA_SCORE_DECODE_GROUPED,
                    SPA_ORDER_KV_ORIGINAL, SPA_ORDER_ORIGINAL, SPA_ORDER_SLOT,
                    SPA_DBG_NONE, SPA_DBG_SEQ_LEN, SPA_DBG_COUNT, SPA_DBG_IDX_RANGE, SPA_DBG_IDX_ORDER, SPA_DBG_HEAD_MODE,
-                   SPA_DBG_Q_POS, SPA_DBG_K_POS, SPA_DBG_PERM_RANGE, SPA_DBG_PERM_DUP,
+                   SPA_DBG_Q_POS, SPA_DBG_K_POS, SPA_DBG_PERM_RANGE, SPA_DBG_PERM_DUP, SPA_DBG_TOK_POS,
                    spa_set_debug_checks, spa_debug_checks, spa_debug_error,
                    LIB_PATH,
                    SpaError, declared_symbols, lib, spa_block_sparse_prefill, spa_index_score,

@@ -44,6 +44,7 @@ SPA_DBG_Q_POS = 6
 SPA_DBG_K_POS = 7
 SPA_DBG_PERM_RANGE = 8
 SPA_DBG_PERM_DUP = 9
+SPA_DBG_TOK_POS = 10
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -58,7 +59,7 @@ _SIGS = {
     "spa_set_debug_checks": (None, [_i]),
     "spa_debug_checks": (_i, []),
     "spa_debug_error": (_i, []),
-    "spa_index_score": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp, _sz, _vp]),
+    "spa_index_score": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _sz, _vp]),
     "spa_index_score_workspace_size": (_sz, [_i, _i, _i, _i, _i, _i]),
     "spa_select_topk": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
     "spa_select_topp": (_i, [_vp, _i, _i, _i, _i, _vp, _i, _i, _i, _i, _f, _f, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]),
@@ -165,10 +166,12 @@ def spa_index_score_workspace_size(B, H_idx, r, Mq, nKb, mode) -> int:
 
 
 def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=0, nKb=None, Mq=None,
-                    scores=None, ws=None) -> torch.Tensor:
+                    scores=None, ws=None, tok_pos=None) -> torch.Tensor:
     """Block scores (int32).  Layouts as in include/spa.h; returns scores.
 
-    For SPA_SCORE_DECODE_GROUPED, ``Mq`` is the number of groups (required).
+    For SPA_SCORE_DECODE_GROUPED, ``Mq`` is the number of groups (required).  With ``tok_pos``
+    (SPA_SCORE_PREFILL_TOKENS only) qI and kI hold every token in original order and slot t
+    pools row tok_pos[b, t]; Mq defaults to the blocks from q_blk0 to the end.
     """
     _dev(qI, "qI", torch.int8)
     _dev(kI, "kI", torch.int8)
@@ -193,10 +196,16 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
             # per-token vectors: whole blocks only (the pooling kernel reads Mq*blk / nKb*blk tokens)
             if qI.shape[1] % blk or kI.shape[1] % blk:
                 raise ValueError("per-token indexer inputs must hold a whole number of blocks")
-            Mq = qI.shape[1] // blk if Mq is None else Mq
             nKb = kI.shape[1] // blk if nKb is None else nKb
-            if Mq * blk > qI.shape[1] or nKb * blk > kI.shape[1]:
+            if Mq is None:
+                Mq = nKb - q_blk0 if tok_pos is not None else qI.shape[1] // blk
+            q_rows = nKb * blk if tok_pos is not None else Mq * blk
+            if q_rows > qI.shape[1] or nKb * blk > kI.shape[1]:
                 raise ValueError("Mq/nKb exceed the per-token inputs")
+            if tok_pos is not None:
+                _dev(tok_pos, "tok_pos", torch.int32)
+                if tok_pos.numel() != B * nKb * blk:
+                    raise ValueError(f"tok_pos must hold B*nKb*blk = {B * nKb * blk} positions")
         shape = (B, Mq, nKb)
     if seq_len is not None:
         _dev(seq_len, "seq_len", torch.int32)
@@ -205,8 +214,8 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
     need = spa_index_score_workspace_size(B, H, r, Mq, nKb, mode)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=qI.device)
-    st = lib().spa_index_score(_ptr(qI), _ptr(kI), _ptr(w), B, H, r, Mq, nKb, q_blk0, _ptr(seq_len), blk, mode,
-                               _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
+    st = lib().spa_index_score(_ptr(qI), _ptr(kI), _ptr(w), B, H, r, Mq, nKb, q_blk0, _ptr(seq_len), _ptr(tok_pos),
+                               blk, mode, _ptr(scores), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     _check("spa_index_score", st)
     return scores
 

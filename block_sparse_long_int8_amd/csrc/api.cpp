@@ -79,6 +79,7 @@ const char* check_name(int code) {
     case SPA_DBG_K_POS: return "k_pos outside [0, T)";
     case SPA_DBG_PERM_RANGE: return "perm value outside its segment";
     case SPA_DBG_PERM_DUP: return "perm value repeated in its segment";
+    case SPA_DBG_TOK_POS: return "tok_pos outside [0, nKb*blk)";
     default: return "unknown violation";
   }
 }
@@ -151,8 +152,9 @@ size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, 
 }
 
 spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
-                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len, int blk,
-                           int mode, int32_t* scores, void* ws, size_t ws_bytes, void* stream) {
+                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len,
+                           const int32_t* tok_pos, int blk, int mode, int32_t* scores, void* ws,
+                           size_t ws_bytes, void* stream) {
   const char* fn = "spa_index_score";
   REQUIRE(mode == SPA_SCORE_DECODE || mode == SPA_SCORE_PREFILL_POOLED || mode == SPA_SCORE_PREFILL_TOKENS ||
               mode == SPA_SCORE_DECODE_GROUPED,
@@ -166,6 +168,13 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   if (mode == SPA_SCORE_DECODE_GROUPED)
     REQUIRE(Mq >= 1 && H_idx % Mq == 0, SPA_ERR_INVALID_ARG, "grouped decode needs Mq groups dividing H_idx (Mq=%d H_idx=%d)",
             Mq, H_idx);
+  if (tok_pos) {
+    REQUIRE(mode == SPA_SCORE_PREFILL_TOKENS, SPA_ERR_INVALID_ARG, "tok_pos needs mode SPA_SCORE_PREFILL_TOKENS");
+    REQUIRE(!seq_len, SPA_ERR_UNSUPPORTED, "tok_pos with seq_len is not supported");
+    REQUIRE((long)q_blk0 + Mq <= nKb, SPA_ERR_INVALID_ARG, "query blocks [%d, %ld) exceed nKb = %d with tok_pos",
+            q_blk0, (long)q_blk0 + Mq, nKb);
+    REQUIRE((long)nKb * blk <= 0x7FFFFFFFL, SPA_ERR_UNSUPPORTED, "nKb*blk exceeds the int32 range");
+  }
   if (B == 0 || Mq == 0 || nKb == 0) return ok();
   REQUIRE(qI && kI && w && scores, SPA_ERR_INVALID_ARG, "null tensor pointer");
   REQUIRE(aligned16(qI) && aligned16(kI) && aligned16(scores), SPA_ERR_INVALID_ARG, "qI, kI and scores must be 16-byte aligned");
@@ -175,6 +184,9 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   if (mode != SPA_SCORE_DECODE && mode != SPA_SCORE_DECODE_GROUPED)
     REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
   if (seq_len) DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, (long long)nKb * blk, SPA_DBG_SEQ_LEN, s_)));
+  if (tok_pos)
+    DEVICE_CHECKS(CHECK_STEP(
+        spa::dbg_range_i32(tok_pos, (long long)B * nKb * blk, 0, (long long)nKb * blk - 1, SPA_DBG_TOK_POS, s_)));
   if (mode == SPA_SCORE_DECODE || mode == SPA_SCORE_DECODE_GROUPED) {
     return from_hip(spa::launch_score_decode(qI, kI, w, B, H_idx, r, Mq, nKb, seq_len, blk, scores, s), fn);
   }
@@ -186,9 +198,9 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
     REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     int8_t* pq = (int8_t*)ws;
     int8_t* pk = pq + align256((size_t)B * Mq * H_idx * r);
-    hipError_t e = spa::launch_pool_blocks(qI, B, Mq * blk, Mq, q_blk0 * blk, H_idx, r, blk, seq_len, pq, s);
-    if (e != hipSuccess) return from_hip(e, fn);
-    e = spa::launch_pool_blocks(kI, B, nKb * blk, nKb, 0, H_idx, r, blk, seq_len, pk, s);
+    const int npos = nKb * blk;
+    hipError_t e = spa::launch_pool_pair(qI, tok_pos ? npos : Mq * blk, q_blk0 * blk, q_blk0 * blk, Mq, kI, npos, nKb,
+                                         B, H_idx, blk, seq_len, tok_pos, npos, pq, pk, s);
     if (e != hipSuccess) return from_hip(e, fn);
     qb = pq;
     kb = pk;

@@ -224,36 +224,73 @@ __global__ void __launch_bounds__(256) score_decode_q4_kernel(const int8_t* __re
 }
 
 // --------------------------------------------------------------- pooling ----
-// x_tok [B, n_tok, H*r] int8 whose token 0 is absolute token tok0; block jb of
-// the output covers absolute tokens [tok0 + jb*blk, +blk) below seq_len.
-// grid: (nblocks, B); block = H*r/4 threads (one 4-byte word each).
-__global__ void pool_blocks_kernel(const int8_t* __restrict__ x_tok, int n_tok, int nblocks,
-                                   int tok0, int HR, int blk, const int32_t* __restrict__ seq_len,
-                                   int8_t* __restrict__ out) {
+// Both per-token tensors of a prefill scoring call are pooled by one launch:
+// grid (max(nblocks), B, 2), z = 0 the query chunk, z = 1 the keys.  One
+// workgroup pools one block: with r = 16 a token's vector of head h is the
+// 16-byte chunk h of its row, thread (token lane tl, head c) loads chunk c of
+// the block's tokens tl, tl + TL, ... (TL = 256 / H lanes) and sums its 16
+// signed bytes; the TL partial sums of each byte meet in LDS.  Slot t of a
+// block is row t - row_off of the tensor, or row tok_pos[b, t] when the
+// tensors are in original token order (the segment permutation is applied by
+// this gather).  Tokens at or past the slot limit are left out of the mean.
+struct PoolJob {
+  const int8_t* x;  // [B, rows, H*16]
+  int rows;         // rows per sequence
+  int slot0;        // slot of the first token of block 0
+  int row_off;      // row = slot - row_off without tok_pos
+  int nblocks;
+  int8_t* out;      // [B, nblocks, H*16]
+};
+
+constexpr int kPoolThreads = 256;
+
+__global__ void __launch_bounds__(kPoolThreads) pool_kernel(PoolJob jq, PoolJob jk, int H, int blk,
+                                                           const int32_t* __restrict__ seq_len,
+                                                           const int32_t* __restrict__ tok_pos, int npos) {
+  __shared__ int part[kPoolThreads * 16];
+  const PoolJob& j = blockIdx.z ? jk : jq;
   const int jb = blockIdx.x;
+  if (jb >= j.nblocks) return;
   const int b = blockIdx.y;
-  const int word = threadIdx.x;
-  if (word * 4 >= HR) return;
-  const int L = seq_len ? seq_len[b] : tok0 + n_tok;
-  const int a0 = tok0 + jb * blk;
-  const int n = max(0, min(min(a0 + blk, L), tok0 + n_tok) - a0);
-  int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-  const int8_t* base = x_tok + ((size_t)b * n_tok + (a0 - tok0)) * HR + word * 4;
-  for (int t = 0; t < n; ++t) {
-    const int v = *reinterpret_cast<const int*>(base + (size_t)t * HR);
-    s0 += (int)(int8_t)(v & 0xFF);
-    s1 += (int)(int8_t)((v >> 8) & 0xFF);
-    s2 += (int)(int8_t)((v >> 16) & 0xFF);
-    s3 += v >> 24;  // arithmetic shift keeps the sign of the top byte
+  const int tid = threadIdx.x;
+  const int TL = kPoolThreads / H;
+  const int c = tid % H, tl = tid / H;
+  const int a0 = j.slot0 + jb * blk;
+  int lim = j.slot0 + j.nblocks * blk;
+  if (!tok_pos) lim = min(lim, j.row_off + j.rows);
+  if (seq_len) lim = min(lim, seq_len[b]);
+  const int n = max(0, min(a0 + blk, lim) - a0);
+  int acc[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0;
+  if (tl < TL) {
+    for (int t = tl; t < n; t += TL) {
+      const int slot = a0 + t;
+      const int row = tok_pos ? tok_pos[(size_t)b * npos + slot] : slot - j.row_off;
+      const uint4 v = *reinterpret_cast<const uint4*>(j.x + ((size_t)b * j.rows + row) * (size_t)(H * 16) + c * 16);
+      const unsigned w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int x = (int)w4[q];
+        acc[4 * q + 0] += (int)(int8_t)(x & 0xFF);
+        acc[4 * q + 1] += (int)(int8_t)((x >> 8) & 0xFF);
+        acc[4 * q + 2] += (int)(int8_t)((x >> 16) & 0xFF);
+        acc[4 * q + 3] += x >> 24;  // arithmetic shift keeps the sign of the top byte
+      }
+    }
   }
-  int res = 0;
-  if (n > 0) {
-    const int dn = 2 * n;
-    const int m0 = floor_div_pos(2 * s0 + n, dn), m1 = floor_div_pos(2 * s1 + n, dn);
-    const int m2 = floor_div_pos(2 * s2 + n, dn), m3 = floor_div_pos(2 * s3 + n, dn);
-    res = (m0 & 0xFF) | ((m1 & 0xFF) << 8) | ((m2 & 0xFF) << 16) | ((m3 & 0xFF) << 24);
+#pragma unroll
+  for (int e = 0; e < 16; ++e) part[e * kPoolThreads + tid] = acc[e];
+  __syncthreads();
+  // thread o < 16H finishes byte e = o / H of head ch = o % H (neighbouring
+  // threads read neighbouring LDS words)
+  int8_t* ob = j.out + ((size_t)b * j.nblocks + jb) * (size_t)(H * 16);
+  for (int o = tid; o < H * 16; o += kPoolThreads) {
+    const int e = o / H, ch = o - e * H;
+    int sum = 0;
+    for (int l = 0; l < TL; ++l) sum += part[e * kPoolThreads + l * H + ch];
+    ob[ch * 16 + e] = n > 0 ? (int8_t)floor_div_pos(2 * sum + n, 2 * n) : 0;
   }
-  *reinterpret_cast<int*>(out + ((size_t)b * nblocks + jb) * HR + word * 4) = res;
 }
 
 // ------------------------------------------------------- prefill (MFMA) ----
@@ -345,12 +382,14 @@ hipError_t launch_score_decode_q4(const int8_t* qI, const uint8_t* codes, const 
   return hipGetLastError();
 }
 
-hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok, int nblocks, int tok0, int H,
-                              int r, int blk, const int32_t* seq_len, int8_t* out, hipStream_t s) {
-  const int HR = H * r;
-  dim3 grid(nblocks, B);
-  pool_blocks_kernel<<<grid, (HR / 4 + 63) / 64 * 64, 0, s>>>(x_tok, n_tok, nblocks, tok0, HR,
-                                                                blk, seq_len, out);
+hipError_t launch_pool_pair(const int8_t* q_tok, int q_rows, int q_slot0, int q_row_off, int Mq,
+                            const int8_t* k_tok, int k_rows, int nKb, int B, int H, int blk,
+                            const int32_t* seq_len, const int32_t* tok_pos, int npos, int8_t* q_out,
+                            int8_t* k_out, hipStream_t s) {
+  const PoolJob jq{q_tok, q_rows, q_slot0, q_row_off, Mq, q_out};
+  const PoolJob jk{k_tok, k_rows, 0, 0, nKb, k_out};
+  dim3 grid(Mq > nKb ? Mq : nKb, B, 2);
+  pool_kernel<<<grid, kPoolThreads, 0, s>>>(jq, jk, H, blk, seq_len, tok_pos, npos);
   return hipGetLastError();
 }
 

@@ -49,9 +49,14 @@ hipError_t launch_quantize_keys(const int8_t* kI, long n_vec, uint8_t* codes, ui
 hipError_t launch_score_decode_q4(const int8_t* qI, const uint8_t* codes, const uint8_t* exps, const int8_t* w,
                                   int B, int H, int groups, int nKb, const int32_t* seq_len, int blk,
                                   int32_t* scores, hipStream_t s);
-hipError_t launch_pool_blocks(const int8_t* x_tok, int B, int n_tok_per_seq, int nblocks,
-                              int tok0, int H, int r, int blk, const int32_t* seq_len,
-                              int8_t* out, hipStream_t s);
+// Mean-pools per-token int8 vectors (r = 16, H heads) of the query chunk (Mq
+// blocks from slot q_slot0) and of the keys (nKb blocks from slot 0), both in
+// one launch.  Slot t is row t - row_off of its tensor (q_row_off for the
+// queries, 0 for the keys), or row tok_pos[b, t] (tok_pos [B, npos]) if given.
+hipError_t launch_pool_pair(const int8_t* q_tok, int q_rows, int q_slot0, int q_row_off, int Mq,
+                            const int8_t* k_tok, int k_rows, int nKb, int B, int H, int blk,
+                            const int32_t* seq_len, const int32_t* tok_pos, int npos, int8_t* q_out,
+                            int8_t* k_out, hipStream_t s);
 hipError_t launch_score_prefill(const int8_t* qIb, const int8_t* kIb, const int8_t* w, int B,
                                 int H, int Mq, int nKb, int q_blk0, const int32_t* seq_len,
                                 int blk, int32_t* scores, hipStream_t s);

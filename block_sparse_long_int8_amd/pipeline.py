@@ -187,18 +187,16 @@ class PrefillStep:
 
     The permutation is the caller's (``perm`` [T], shared by the batch, or
     [B, T]) or, with ``spec.perm_kind == "importance"``, computed on the device
-    from Q and K by spa_importance_permutation (one per sequence).  Only the
-    per-token indexer vectors are permuted into slot order (the pooling needs
-    each block's tokens together); the attention reads Q, K and V and writes O
-    (``out``) and the log-sum-exp (``lse``) in the original token order, the
-    permutation applied inside the kernel through the slot positions.
+    from Q and K by spa_importance_permutation (one per sequence).  Nothing is
+    copied into slot order: the pooling of the indexer vectors gathers each
+    block's tokens through the slot positions, and the attention reads Q, K
+    and V and writes O (``out``) and the log-sum-exp (``lse``) in the original
+    token order through the same positions.
     """
 
     def __init__(self, spec: PrefillSpec, device="cuda"):
         self.spec = s = spec
         dev = torch.device(device)
-        self.qIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
-        self.kIp = torch.empty((s.B, s.T, s.H_idx, s.r), dtype=torch.int8, device=dev)
         self.scores = torch.empty((s.B, s.nb, s.nb), dtype=torch.int32, device=dev)
         self.idx = torch.empty((s.B, s.nb, s.cap), dtype=torch.int32, device=dev)
         self.count = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
@@ -230,34 +228,21 @@ class PrefillStep:
             self.pos = perm.reshape(1, -1) if s.B == 1 else perm.reshape(1, -1).expand(s.B, -1).contiguous()
         return self.pos
 
-    def _permute(self, src, perm, dim, dst, inverse=False):
+    def score(self, qI_tok, kI_tok, w):
+        """Pool the per-token vectors (original order) into the blocks of the permuted order, gathered
+        through the slot positions, and score every (query block, past key block)."""
         s = self.spec
-        if perm.dim() == 1:
-            return L.spa_segment_permute(src, perm, s.seg, dim=dim, inverse=inverse, dst=dst)
-        for b in range(s.B):  # one permutation per sequence
-            L.spa_segment_permute(src[b], perm[b], s.seg, dim=dim - 1, inverse=inverse, dst=dst[b])
-        return dst
-
-    def permute_index(self, qI_tok, kI_tok, perm):
-        """The per-token indexer vectors into slot order."""
-        self._permute(qI_tok, perm, 1, self.qIp)
-        self._permute(kI_tok, perm, 1, self.kIp)
-
-    def score(self, w):
-        """Pool the permuted per-token vectors into blocks and score every (query block, past key block)."""
-        s = self.spec
-        return L.spa_index_score(self.qIp, self.kIp, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
-                                 ws=self.score_ws)
+        return L.spa_index_score(qI_tok, kI_tok, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
+                                 ws=self.score_ws, tok_pos=self.pos)
 
     def select(self):
         s = self.spec
         return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
                                  count=self.count, algo=s.select_algo)
 
-    def front(self, qI_tok, kI_tok, w, perm):
-        """Permute the indexer inputs, pool, score and select."""
-        self.permute_index(qI_tok, kI_tok, perm)
-        self.score(w)
+    def front(self, qI_tok, kI_tok, w):
+        """Pool and score the indexer inputs in the permuted order, then select (after set_perm)."""
+        self.score(qI_tok, kI_tok, w)
         self.select()
         return self.idx, self.count
 
@@ -271,6 +256,6 @@ class PrefillStep:
         if self.spec.perm_kind == "importance":
             perm = self.importance(q, k)
         self.set_perm(perm)
-        self.front(qI_tok, kI_tok, w, perm)
+        self.front(qI_tok, kI_tok, w)
         self.attend(q, k, v)
         return self.out

@@ -9,9 +9,10 @@
  * the cache written by spa_quantize_selector_keys when keys enter it; the
  * spa_select_*_hist variants select without sorting)
  * and one permuted block-sparse prefill is
- *     [spa_importance_permutation ->] spa_segment_permute (indexer vectors)
- *     -> spa_index_score (prefill) -> spa_select_topk (prefill)
- *     -> spa_block_sparse_prefill (Q, K, V and O in the original token order)
+ *     [spa_importance_permutation ->] spa_index_score (prefill, tok_pos = the
+ *     permutation) -> spa_select_topk (prefill) -> spa_block_sparse_prefill,
+ *     every tensor in the original token order (the kernels apply the
+ *     permutation; spa_segment_permute does it for other tensors)
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer to a dense row-major array with
@@ -96,6 +97,7 @@ int spa_version(void);
  *   head_mode     -- spa_sparse_decode_attn*: every entry 0 or 1;
  *   positions     -- spa_block_sparse_prefill: q_pos with SPA_ORDER_ORIGINAL,
  *                    k_pos with SPA_ORDER_KV_ORIGINAL, in [0, T);
+ *                    spa_index_score: tok_pos in [0, nKb*blk);
  *   perm          -- spa_segment_permute: each perm[t] in t's segment and,
  *                    for seg <= 262144, no value twice in a segment.
  * The checks share one device word per GPU and run one call at a time in the
@@ -113,6 +115,7 @@ int spa_version(void);
 #define SPA_DBG_K_POS 7      /* k_pos used as a row number, outside [0, T) */
 #define SPA_DBG_PERM_RANGE 8 /* perm[t] outside t's segment              */
 #define SPA_DBG_PERM_DUP 9   /* a value twice in one segment of perm      */
+#define SPA_DBG_TOK_POS 10   /* tok_pos outside [0, nKb*blk)               */
 
 /* Switch the device-side checks on (1) or off (0) for the whole process. */
 void spa_set_debug_checks(int on);
@@ -148,16 +151,25 @@ int spa_debug_error(void);
  *   before the query block, and j < ceil(seq_len[b]/blk) when seq_len is given);
  *   INT32_MIN elsewhere.  seq_len may be NULL.
  * mode SPA_SCORE_PREFILL_TOKENS:
- *   qI [B, Mq*blk, H_idx, r] per-token query vectors of the chunk (its first
- *   token is block q_blk0's first token), kI [B, nKb*blk, H_idx, r] per-token
- *   key vectors; each block is mean-pooled to floor(mean + 1/2) over its tokens
- *   below seq_len (block importance by mean pooling, PBS-Attn page §4), then
- *   scored as in POOLED mode.  Needs spa_index_score_workspace_size bytes.
+ *   per-token vectors; block i's vector is the mean of its blk slots' vectors
+ *   (slots below seq_len), rounded to floor(mean + 1/2) (block importance by
+ *   mean pooling, PBS-Attn page §4); the blocks are then scored as in POOLED
+ *   mode.  Needs spa_index_score_workspace_size bytes.
+ *   tok_pos == NULL: the tensors are in slot order, qI [B, Mq*blk, H_idx, r]
+ *     the chunk's slots (its first row is block q_blk0's first slot) and kI
+ *     [B, nKb*blk, H_idx, r] every key slot.
+ *   tok_pos [B, nKb*blk] int32: the tensors are in the original token order,
+ *     qI and kI [B, nKb*blk, H_idx, r], and slot t's vector is row
+ *     tok_pos[b, t] (values in [0, nKb*blk)), so the segment permutation of
+ *     PBS-Attn §2 happens inside the pooling.  Needs q_blk0 + Mq <= nKb and
+ *     seq_len == NULL (else SPA_ERR_UNSUPPORTED).
+ * tok_pos must be NULL in the other modes.
  * Supported: r % 4 == 0, 1 <= H_idx, H_idx*r <= 1024; PREFILL modes need r == 16.
  */
 spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H_idx,
-                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len, int blk,
-                           int mode, int32_t* scores, void* ws, size_t ws_bytes, void* stream);
+                           int r, int Mq, int nKb, int q_blk0, const int32_t* seq_len,
+                           const int32_t* tok_pos, int blk, int mode, int32_t* scores, void* ws,
+                           size_t ws_bytes, void* stream);
 size_t spa_index_score_workspace_size(int B, int H_idx, int r, int Mq, int nKb, int mode);
 
 /*

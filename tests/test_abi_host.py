@@ -38,28 +38,35 @@ def _fake(n=1):
 
 def test_index_score_rejections():
     f = L.spa_index_score
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 7, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), N, 64, 7, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert b"unknown mode" in L.spa_last_error()
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 15, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert f(_fake(), _fake(2), _fake(3), 1, 128, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 2, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert f(N, _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 15, 1, 10, 0, _fake(4), N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 128, 16, 1, 10, 0, _fake(4), N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 2, 10, 0, _fake(4), N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(N, _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, N, N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     # misaligned kI
-    assert f(_fake(), ctypes.c_void_p(0x2004), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), ctypes.c_void_p(0x2004), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), N, 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     # prefill needs r == 16
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 8, 4, 10, 0, N, 64, 1, _fake(5), N, 0, N) == S.SPA_ERR_UNSUPPORTED
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 8, 4, 10, 0, N, N, 64, 1, _fake(5), N, 0, N) == S.SPA_ERR_UNSUPPORTED
     # per-token prefill without workspace
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_WORKSPACE
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, N, 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_WORKSPACE
     # grouped decode: the groups must divide H_idx
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 3, 10, 0, _fake(4), 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 3, 10, 0, _fake(4), N, 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     assert b"groups" in L.spa_last_error()
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 0, 10, 0, _fake(4), 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
-    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 0, 10, 0, _fake(4), N, 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, N, N, 64, 3, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
     # empty batch is a valid no-op
-    assert f(N, N, N, 0, 8, 16, 1, 10, 0, N, 64, 0, N, N, 0, N) == S.SPA_OK
+    assert f(N, N, N, 0, 8, 16, 1, 10, 0, N, N, 64, 0, N, N, 0, N) == S.SPA_OK
     assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 2) == 2 * 1024 * 128
     assert L.spa_index_score_workspace_size(1, 8, 16, 1024, 1024, 0) == 0
+    # tok_pos: per-token prefill only, without seq_len, chunk inside the key blocks
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 1, 10, 0, _fake(4), _fake(6), 64, 0, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert b"tok_pos" in L.spa_last_error()
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 0, _fake(4), _fake(6), 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_UNSUPPORTED
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 7, N, _fake(6), 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_INVALID_ARG
+    assert b"exceed nKb" in L.spa_last_error()
+    assert f(_fake(), _fake(2), _fake(3), 1, 8, 16, 4, 10, 6, N, _fake(6), 64, 2, _fake(5), N, 0, N) == S.SPA_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("suffix", ["", "_hist"])

@@ -555,6 +555,30 @@ def test_pool_ragged_tokens():
         assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("H", [1, 3, 8, 64])
+def test_scores_tokens_gathered_through_positions(H):
+    # per-token vectors in original order, pooled in the permuted order through tok_pos (one
+    # permutation per sequence), for a chunk of query blocks: the oracle permutes, pools, scores
+    rng = np.random.default_rng(20 + H)
+    B, nb, blk, seg = 2, 12, 64, 192
+    T = nb * blk
+    xq = rng.integers(-128, 128, size=(B, T, H, 16), dtype=np.int8)
+    xk = rng.integers(-128, 128, size=(B, T, H, 16), dtype=np.int8)
+    w = rng.integers(1, 5, size=(B, nb, H), dtype=np.int8)
+    perm = np.stack([np.concatenate([s0 + rng.permutation(seg) for s0 in range(0, T, seg)])
+                     for _ in range(B)]).astype(np.int32)
+    ref = np.concatenate([O.score_prefill(O.pool_blocks(O.segment_permute(xq[b:b + 1], perm[b], 1), blk),
+                                          O.pool_blocks(O.segment_permute(xk[b:b + 1], perm[b], 1), blk),
+                                          w[b:b + 1]) for b in range(B)])
+    full = S.spa_index_score(dev(xq), dev(xk), dev(w), blk, mode=S.SPA_SCORE_PREFILL_TOKENS, tok_pos=dev(perm))
+    q0, mq = 5, 4
+    part = S.spa_index_score(dev(xq), dev(xk), dev(np.ascontiguousarray(w[:, q0:q0 + mq])), blk,
+                             mode=S.SPA_SCORE_PREFILL_TOKENS, tok_pos=dev(perm), q_blk0=q0, Mq=mq)
+    torch.cuda.synchronize()
+    assert np.array_equal(full.cpu().numpy().astype(np.int64), ref)
+    assert np.array_equal(part.cpu().numpy().astype(np.int64), ref[:, q0:q0 + mq])
+
+
 def test_segment_permute_bitexact():
     rng = np.random.default_rng(4)
     T, seg = 1000, 256
