@@ -3,10 +3,13 @@
 Each case draws one configuration that the named workloads do not cover
 together: block size, GQA ratio, indexer heads, reserved blocks, top-k or dual
 top-p budgets, ragged sequence lengths, local-window heads, fp32 or bf16, and
-the selection path (separate sorted, separate sort-free, or fused).  The
-parity bars are the suite's: scores and top-k lists bit-exact, top-p lists by
+the selection path (separate sorted, separate sort-free, or fused).  Every
+fourth case of the decode, prefill and variant sweeps runs with the library's
+device-side checks on, which must accept every input and change no result.
+The parity bars are the suite's: scores and top-k lists bit-exact, top-p lists by
 the set rule, attention within max |diff| <= 1e-2 and relative L2 <= 2e-3.
 """
+import contextlib
 import dataclasses
 
 import numpy as np
@@ -32,6 +35,20 @@ def _lib():
 
 
 PATHS = ("separate", "fused", "separate-hist")
+
+
+@contextlib.contextmanager
+def _checks(seed: int):
+    """Every fourth seed runs with the device-side checks on."""
+    on = seed % 4 == 3
+    if on:
+        S.spa_set_debug_checks(True)
+    try:
+        yield
+    finally:
+        if on:
+            assert S.spa_debug_error() == S.SPA_DBG_NONE
+            S.spa_set_debug_checks(False)
 
 
 def _draw(seed: int):
@@ -85,7 +102,8 @@ def test_decode_random_sweep(seed):
                         local_window_tok=cfg.local_window_tok,
                         select_algo="hist" if path.endswith("hist") else "sort")
     step = S.DecodeStep(spec, fused=path == "fused")
-    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
+    with _checks(seed):
+        step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
     torch.cuda.synchronize()
     ref = O.decode_step(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
@@ -131,7 +149,8 @@ def test_prefill_random_sweep(seed):
     step = S.PrefillStep(S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk,
                                        H_idx=cfg.H_idx, r=cfg.r, k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local,
                                        seg=cfg.seg))
-    out = step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
+    with _checks(seed):
+        out = step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
     torch.cuda.synchronize()
     front = O.prefill_front(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
@@ -177,7 +196,8 @@ def test_decode_variant_random_sweep(seed):
                         select_algo="hist" if path.endswith("hist") else "sort")
     step = S.DecodeStep(spec)
     kI = step.quantize_selector(t["kI"]) if cfg.selector_q4 else t["kI"]
-    step(t["q"], t["k"], t["v"], t["qI"], kI, t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
+    with _checks(seed):
+        step(t["q"], t["k"], t["v"], t["qI"], kI, t["w"], t["seq_len"], t["head_mode"], keep_scores=True)
     torch.cuda.synchronize()
     ref = O.decode_step(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
