@@ -183,6 +183,12 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
     REQUIRE(seq_len, SPA_ERR_INVALID_ARG, "decode mode needs seq_len");
   if (mode != SPA_SCORE_DECODE && mode != SPA_SCORE_DECODE_GROUPED)
     REQUIRE(r == 16, SPA_ERR_UNSUPPORTED, "prefill scoring supports r == 16 only (got %d)", r);
+  if (mode == SPA_SCORE_PREFILL_TOKENS) {
+    const size_t need = spa_index_score_workspace_size(B, H_idx, r, Mq, nKb, mode);
+    REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
+    REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  }
+  // every host-side check above; the device-side checks (when on) below
   if (seq_len) DEVICE_CHECKS(CHECK_STEP(spa::dbg_range_i32(seq_len, B, 1, (long long)nKb * blk, SPA_DBG_SEQ_LEN, s_)));
   if (tok_pos)
     DEVICE_CHECKS(CHECK_STEP(
@@ -193,9 +199,6 @@ spa_status spa_index_score(const int8_t* qI, const int8_t* kI, const int8_t* w, 
   const int8_t* qb = qI;
   const int8_t* kb = kI;
   if (mode == SPA_SCORE_PREFILL_TOKENS) {
-    const size_t need = spa_index_score_workspace_size(B, H_idx, r, Mq, nKb, mode);
-    REQUIRE(ws && ws_bytes >= need, SPA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws_bytes);
-    REQUIRE(aligned16(ws), SPA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
     int8_t* pq = (int8_t*)ws;
     int8_t* pk = pq + align256((size_t)B * Mq * H_idx * r);
     const int npos = nKb * blk;

@@ -229,3 +229,23 @@ def test_debug_check_switch_and_codes():
         text = f.read()
     for name, val in re.findall(r"#define (SPA_DBG_\w+) (\d+)", text):
         assert getattr(S, name) == int(val), name
+
+
+def test_host_rejections_precede_device_checks():
+    # with the device-side checks on, every host-side rejection still returns first, before any
+    # device work (these calls pass fake host addresses and no GPU is needed)
+    was = L.spa_debug_checks()
+    L.spa_set_debug_checks(1)
+    try:
+        test_index_score_rejections()
+        for suffix in ("", "_hist"):
+            test_select_rejections(suffix)
+        for name in ("spa_sparse_decode_attn", "spa_sparse_decode_attn_grouped"):
+            test_decode_attn_rejections(name)
+        test_prefill_and_permute_rejections()
+        test_score_select_rejections()
+        test_importance_permutation_rejections()
+        test_int4_selector_rejections()
+    finally:
+        L.spa_set_debug_checks(was)
+    assert L.spa_debug_error() == S.SPA_DBG_NONE
