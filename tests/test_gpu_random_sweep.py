@@ -152,6 +152,16 @@ def test_prefill_random_sweep(seed):
     with _checks(seed):
         out = step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["perm"])
     torch.cuda.synchronize()
+    if seed % 2:
+        # K and V copied into slot order first, then read in slot order: bit for bit the in-kernel gather
+        pos = step.pos
+        kp = torch.stack([S.spa_segment_permute(t["k"][b], pos[b].contiguous(), cfg.seg, dim=1) for b in range(cfg.B)])
+        vp = torch.stack([S.spa_segment_permute(t["v"][b], pos[b].contiguous(), cfg.seg, dim=1) for b in range(cfg.B)])
+        o2, l2 = S.spa_block_sparse_prefill(t["q"], kp, vp, step.idx, step.count, cfg.blk, q_pos=pos, k_pos=pos,
+                                            order="original", kv_order="slot")
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out)
+        assert torch.equal(l2, step.lse)
     front = O.prefill_front(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
     assert sel_lists(step.idx, step.count) == front["sel"]
