@@ -20,7 +20,8 @@
  *     never allocates device memory: temporaries live in a caller-provided
  *     workspace sized by the matching *_workspace_size function.
  *   - Calls are asynchronous on the caller's stream (a hipStream_t passed as
- *     void*; NULL is the default stream).  Nothing synchronises.
+ *     void*; NULL is the default stream).  Nothing synchronises, unless the
+ *     device-side checks are on.
  *   - Arguments are validated on the host before anything is enqueued; on any
  *     error the function returns a negative status and launches nothing.
  *     Values inside device arrays (idx, count, perm, positions, seq_len) are
