@@ -41,8 +41,8 @@ constexpr int kD = 128;        // head dimension
 constexpr int kProxyMax = 64;  // proxy queries per head (two 32-row MFMA halves)
 constexpr int kImpChunk = 1024;  // keys per workgroup and head
 constexpr int kImpTile = 32;     // keys per MFMA tile
-constexpr int kSortThreads = 512;
-constexpr int kSortEPT = 8;
+constexpr int kSortThreads = 1024;
+constexpr int kSortEPT = 4;
 constexpr int kSortMax = kSortThreads * kSortEPT;  // longest segment the sort handles (4096)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
