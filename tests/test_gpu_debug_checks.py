@@ -239,3 +239,19 @@ def test_checked_call_refuses_graph_capture(checks):
     assert e.value.status == S.SPA_ERR_INVALID_ARG
     assert "captured" in e.value.detail
     torch.cuda.synchronize()
+
+
+def test_pooling_positions(checks):
+    # tok_pos gathers the per-token indexer vectors; row T of sequence 0 is row 0 of sequence 1
+    rng = np.random.default_rng(3)
+    B, nb, blk, H = 2, 8, 64, 8
+    T = nb * blk
+    x = dev(rng.integers(-128, 128, size=(B, T, H, 16), dtype=np.int8))
+    w = dev(rng.integers(1, 5, size=(B, nb, H), dtype=np.int8))
+    pos = np.tile(np.arange(T, dtype=np.int32), (B, 1))
+    S.spa_index_score(x, x, w, blk, mode=S.SPA_SCORE_PREFILL_TOKENS, tok_pos=dev(pos))
+    torch.cuda.synchronize()
+    assert S.spa_debug_error() == S.SPA_DBG_NONE
+    bad = pos.copy()
+    bad[0, 100] = T
+    _expect(S.SPA_DBG_TOK_POS, S.spa_index_score, x, x, w, blk, mode=S.SPA_SCORE_PREFILL_TOKENS, tok_pos=dev(bad))
