@@ -1,5 +1,6 @@
 """Plant plausible mistakes into a copy of the oracle (on the CPU) and check
-that the pins in test_oracle_pins.py reject every one of them.
+that the pins in test_oracle_pins.py and test_oracle_driver_pins.py reject
+every one of them.
 """
 import os
 import shutil
@@ -59,7 +60,35 @@ MUTATIONS = [
     ("int4_exponent_from_one", "    for e in range(8):\n        c = np.floor_divide(", "    for e in range(1, 8):\n        c = np.floor_divide("),
     ("int4_nibbles_swapped", "(c[..., 0::2] | (c[..., 1::2] << 4))", "(c[..., 1::2] | (c[..., 0::2] << 4))"),
     ("segment_check_loose", "return bool(np.all(np.asarray(perm) // seg == np.arange(T) // seg))", "return True"),
+    # wiring of the whole-path drivers
+    ("front_identity_positions", "pos=perm.astype(np.int64))", "pos=np.arange(len(perm)))"),
+    ("front_qI_unpermuted", "qIb = pool_blocks(qI_p, cfg.blk)", "qIb = pool_blocks(inp[\"qI_tok\"], cfg.blk)"),
+    ("front_kI_unpermuted", "kIb = pool_blocks(kI_p, cfg.blk)", "kIb = pool_blocks(inp[\"kI_tok\"], cfg.blk)"),
+    ("step_lse_not_inverted", "res[\"lse\"] = segment_permute(lse_slot, perm, axis=2, inverse=True)",
+     "res[\"lse\"] = lse_slot"),
+    ("step_o_not_inverted", "res[\"o\"] = segment_permute(o_slot, perm, axis=2, inverse=True)", "res[\"o\"] = o_slot"),
+    ("step_q_unpermuted", "qp = segment_permute(inp[\"q\"], perm, axis=2)", "qp = inp[\"q\"]"),
+    ("step_v_unpermuted", "vp = segment_permute(inp[\"v\"], perm, axis=2)", "vp = inp[\"v\"]"),
+    ("decode_int4_branch_dropped", "if getattr(cfg, \"selector_q4\", False):", "if False:"),
+    ("decode_int4_branch_always", "if getattr(cfg, \"selector_q4\", False):", "if True:"),
+    ("decode_topp_beta_dropped", "\"topp\",\n                                  beta=cfg.beta, p=cfg.p",
+     "\"topp\",\n                                  p=cfg.p"),
+    ("decode_group_topp_beta_dropped", "\"topp\",\n                                              beta=cfg.beta, p=cfg.p",
+     "\"topp\",\n                                              p=cfg.p"),
+    ("decode_head_mode_dropped", "                              inp[\"head_mode\"], cfg.local_sink_tok, cfg.local_window_tok,\n"
+     "                              batches=batches, heads=heads)",
+     "                              None, cfg.local_sink_tok, cfg.local_window_tok,\n"
+     "                              batches=batches, heads=heads)"),
+    ("decode_sink_window_swapped", "                              inp[\"head_mode\"], cfg.local_sink_tok, cfg.local_window_tok,\n"
+     "                              batches=batches, heads=heads)",
+     "                              inp[\"head_mode\"], cfg.local_window_tok, cfg.local_sink_tok,\n"
+     "                              batches=batches, heads=heads)"),
+    ("dense_mass_scale_dropped", "x = (K @ to_f64(q[h], dtype)) * scale", "x = (K @ to_f64(q[h], dtype))"),
+    ("dense_mass_gqa_modulo", "K = to_f64(k[h // G, :L], dtype)", "K = to_f64(k[h % Hkv, :L], dtype)"),
+    ("dense_mass_ignores_seq_len", "K = to_f64(k[h // G, :L], dtype)", "K = to_f64(k[h // G], dtype)"),
 ]
+
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_driver_pins.py"]
 
 
 def test_mutation_list_applies():
@@ -76,7 +105,7 @@ def test_pins_reject_planted_mistake(tmp_path, name, old, new):
     shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), pkg / "__init__.py")
     (pkg / "spa_oracle.py").write_text(src.replace(old, new))
     env = dict(os.environ, SPA_ORACLE_UNDER_TEST=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"]
+                       + [os.path.join(ROOT, "tests", f) for f in PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
