@@ -1,10 +1,12 @@
 """ctypes binding of libspa.so: argument marshalling only.
 
 Every function here has the name of the C entry point it calls (include/spa.h)
-and does nothing but check shapes, allocate outputs with torch (device memory
-plumbing), pass raw pointers and torch's current HIP stream, and raise on a
-non-zero status.  All arithmetic runs in the library's HIP kernels.  If the
-library is missing the import fails loudly: there is no fallback path.
+and does nothing but check each tensor argument against the layout the entry
+point reads (exact shape, dtype, contiguity, one device; ValueError before any
+launch), allocate outputs with torch (device memory plumbing), pass raw
+pointers and torch's current HIP stream, and raise on a non-zero status.  All
+arithmetic runs in the library's HIP kernels.  If the library is missing the
+import fails loudly: there is no fallback path.
 """
 from __future__ import annotations
 
@@ -141,14 +143,45 @@ def _stream() -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _dev(t: torch.Tensor, name: str, dtype=None):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+def _want(t: Optional[torch.Tensor], name: str, shape=None, dtype=None, optional: bool = False):
+    """Check one tensor argument against the layout the C entry point reads: exact
+    shape, dtype and contiguity.  Raises ValueError (nothing is launched)."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _on_device(**tensors):
+    """Every given tensor lives on the same GPU (checked after the shapes)."""
+    devs = set()
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        devs.add(t.device)
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
+def _ws(ws: Optional[torch.Tensor], need: int, name: str = "ws"):
+    """A caller workspace must be a contiguous uint8 tensor of at least ``need`` bytes."""
+    if ws is None:
+        return None
+    _want(ws, name, dtype=torch.uint8)
+    if ws.numel() < need:
+        raise ValueError(f"{name} holds {ws.numel()} bytes, the call needs {need}")
+    return ws
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -173,25 +206,36 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
     (SPA_SCORE_PREFILL_TOKENS only) qI and kI hold every token in original order and slot t
     pools row tok_pos[b, t]; Mq defaults to the blocks from q_blk0 to the end.
     """
-    _dev(qI, "qI", torch.int8)
-    _dev(kI, "kI", torch.int8)
-    _dev(w, "w", torch.int8)
-    if mode == SPA_SCORE_DECODE:
+    for name, t in (("qI", qI), ("kI", kI), ("w", w)):
+        _want(t, name, dtype=torch.int8)
+    if mode in (SPA_SCORE_DECODE, SPA_SCORE_DECODE_GROUPED):
+        if qI.dim() != 3:
+            raise ValueError("decode scoring: qI must be [B, H_idx, r]")
         B, H, r = qI.shape
-        nKb = kI.shape[1]
-        Mq = 1
-        shape = (B, nKb)
-    elif mode == SPA_SCORE_DECODE_GROUPED:
-        B, H, r = qI.shape
-        nKb = kI.shape[1]
-        if Mq is None:
-            raise ValueError("grouped decode scoring needs Mq (the number of groups)")
-        shape = (B, Mq, nKb)
-    else:
+        nKb = kI.shape[1] if nKb is None else nKb
+        if mode == SPA_SCORE_DECODE:
+            Mq = 1
+            shape = (B, nKb)
+        else:
+            if Mq is None:
+                raise ValueError("grouped decode scoring needs Mq (the number of groups)")
+            shape = (B, Mq, nKb)
+        _want(kI, "kI", (B, nKb, H, r))
+        _want(w, "w", (B, H))
+        _want(seq_len, "seq_len", (B,), torch.int32)
+        if tok_pos is not None:
+            raise ValueError("tok_pos is only for SPA_SCORE_PREFILL_TOKENS")
+    elif mode in (SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS):
+        if qI.dim() != 4:
+            raise ValueError("prefill scoring: qI must be [B, rows, H_idx, r]")
         B, _, H, r = qI.shape
         if mode == SPA_SCORE_PREFILL_POOLED:
             Mq = qI.shape[1] if Mq is None else Mq
             nKb = kI.shape[1] if nKb is None else nKb
+            _want(qI, "qI", (B, Mq, H, r))
+            _want(kI, "kI", (B, nKb, H, r))
+            if tok_pos is not None:
+                raise ValueError("tok_pos is only for SPA_SCORE_PREFILL_TOKENS")
         else:
             # per-token vectors: whole blocks only (the pooling kernel reads Mq*blk / nKb*blk tokens)
             if qI.shape[1] % blk or kI.shape[1] % blk:
@@ -200,18 +244,20 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
             if Mq is None:
                 Mq = nKb - q_blk0 if tok_pos is not None else qI.shape[1] // blk
             q_rows = nKb * blk if tok_pos is not None else Mq * blk
-            if q_rows > qI.shape[1] or nKb * blk > kI.shape[1]:
-                raise ValueError("Mq/nKb exceed the per-token inputs")
-            if tok_pos is not None:
-                _dev(tok_pos, "tok_pos", torch.int32)
-                if tok_pos.numel() != B * nKb * blk:
-                    raise ValueError(f"tok_pos must hold B*nKb*blk = {B * nKb * blk} positions")
+            _want(qI, "qI", (B, q_rows, H, r))
+            _want(kI, "kI", (B, nKb * blk, H, r))
+            _want(tok_pos, "tok_pos", (B, nKb * blk), torch.int32, optional=True)
+        _want(w, "w", (B, Mq, H))
+        _want(seq_len, "seq_len", (B,), torch.int32, optional=True)
         shape = (B, Mq, nKb)
-    if seq_len is not None:
-        _dev(seq_len, "seq_len", torch.int32)
+    else:
+        raise ValueError(f"unknown scoring mode {mode}")
+    _want(scores, "scores", shape, torch.int32, optional=True)
+    need = spa_index_score_workspace_size(B, H, r, Mq, nKb, mode)
+    _ws(ws, need)
+    _on_device(qI=qI, kI=kI, w=w, seq_len=seq_len, tok_pos=tok_pos, scores=scores, ws=ws)
     if scores is None:
         scores = torch.empty(shape, dtype=torch.int32, device=qI.device)
-    need = spa_index_score_workspace_size(B, H, r, Mq, nKb, mode)
     if need and ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=qI.device)
     st = lib().spa_index_score(_ptr(qI), _ptr(kI), _ptr(w), B, H, r, Mq, nKb, q_blk0, _ptr(seq_len), _ptr(tok_pos),
@@ -222,9 +268,12 @@ def spa_index_score(qI, kI, w, blk, seq_len=None, mode=SPA_SCORE_DECODE, q_blk0=
 
 def spa_quantize_selector_keys(kI, codes=None, exps=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """int8 key vectors [..., 16] -> int4 codes [..., 8] uint8 and exponents [...] uint8."""
-    _dev(kI, "kI", torch.int8)
+    _want(kI, "kI", dtype=torch.int8)
     r = kI.shape[-1]
     lead = tuple(kI.shape[:-1])
+    _want(codes, "codes", lead + (r // 2,), torch.uint8, optional=True)
+    _want(exps, "exps", lead, torch.uint8, optional=True)
+    _on_device(kI=kI, codes=codes, exps=exps)
     if codes is None:
         codes = torch.empty(lead + (r // 2,), dtype=torch.uint8, device=kI.device)
     if exps is None:
@@ -236,21 +285,25 @@ def spa_quantize_selector_keys(kI, codes=None, exps=None) -> Tuple[torch.Tensor,
 
 def spa_index_score_q4(qI, codes, exps, w, blk, seq_len, mode=SPA_SCORE_DECODE, Mq=None, scores=None) -> torch.Tensor:
     """Decode scores from the int4 selector cache; Mq is the number of groups in grouped mode."""
-    _dev(qI, "qI", torch.int8)
-    _dev(codes, "codes", torch.uint8)
-    _dev(exps, "exps", torch.uint8)
-    _dev(w, "w", torch.int8)
-    _dev(seq_len, "seq_len", torch.int32)
+    _want(qI, "qI", dtype=torch.int8)
+    if qI.dim() != 3:
+        raise ValueError("qI must be [B, H_idx, r]")
     B, H, r = qI.shape
-    nKb = codes.shape[1]
-    if codes.shape != (B, nKb, H, r // 2) or exps.shape != (B, nKb, H):
+    _want(codes, "codes", dtype=torch.uint8)
+    nKb = codes.shape[1] if codes.dim() == 4 else -1
+    if codes.shape != (B, nKb, H, r // 2) or tuple(exps.shape) != (B, nKb, H):
         raise ValueError("codes must be [B, nKb, H_idx, r/2] and exps [B, nKb, H_idx]")
+    _want(exps, "exps", (B, nKb, H), torch.uint8)
+    _want(w, "w", (B, H), torch.int8)
+    _want(seq_len, "seq_len", (B,), torch.int32)
     Mq = 1 if mode == SPA_SCORE_DECODE else Mq
     if Mq is None:
         raise ValueError("grouped decode scoring needs Mq (the number of groups)")
+    shape = (B, nKb) if mode == SPA_SCORE_DECODE else (B, Mq, nKb)
+    _want(scores, "scores", shape, torch.int32, optional=True)
+    _on_device(qI=qI, codes=codes, exps=exps, w=w, seq_len=seq_len, scores=scores)
     if scores is None:
-        scores = torch.empty((B, nKb) if mode == SPA_SCORE_DECODE else (B, Mq, nKb), dtype=torch.int32,
-                             device=qI.device)
+        scores = torch.empty(shape, dtype=torch.int32, device=qI.device)
     st = lib().spa_index_score_q4(_ptr(qI), _ptr(codes), _ptr(exps), _ptr(w), B, H, r, Mq, nKb, _ptr(seq_len), blk,
                                   mode, _ptr(scores), _stream())
     _check("spa_index_score_q4", st)
@@ -259,23 +312,32 @@ def spa_index_score_q4(qI, codes, exps, w, blk, seq_len, mode=SPA_SCORE_DECODE, 
 
 # --------------------------------------------------------------- selection --
 
-def _sel_out(scores, cap, idx, count):
+def _sel_out(scores, cap, idx, count, seq_len, prefill):
+    """Check the selection tensors (scores [B, nKb] or [B, M, nKb]; idx, count to match) and
+    allocate the missing outputs."""
+    _want(scores, "scores", dtype=torch.int32)
+    if scores.dim() not in (2, 3):
+        raise ValueError("scores must be [B, nKb] or [B, M, nKb]")
     B = scores.shape[0]
     M = 1 if scores.dim() == 2 else scores.shape[1]
+    rows = (B,) if scores.dim() == 2 else (B, M)
+    _want(idx, "idx", rows + (cap,), torch.int32, optional=True)
+    _want(count, "count", rows, torch.int32, optional=True)
+    _want(seq_len, "seq_len", (B,), torch.int32, optional=prefill)
+    _on_device(scores=scores, idx=idx, count=count, seq_len=seq_len)
     if idx is None:
-        idx = torch.empty((B, M, cap) if scores.dim() == 3 else (B, cap), dtype=torch.int32, device=scores.device)
+        idx = torch.empty(rows + (cap,), dtype=torch.int32, device=scores.device)
     if count is None:
-        count = torch.empty((B, M) if scores.dim() == 3 else (B,), dtype=torch.int32, device=scores.device)
+        count = torch.empty(rows, dtype=torch.int32, device=scores.device)
     return B, M, idx, count
 
 
 def spa_select_topk(scores, blk, n_sink, n_local, k, cap, seq_len=None, prefill=False, q_blk0=0,
                     idx=None, count=None, algo="sort") -> Tuple[torch.Tensor, torch.Tensor]:
     """algo "sort" calls spa_select_topk, "hist" spa_select_topk_hist (same result)."""
-    _dev(scores, "scores", torch.int32)
-    B, M, idx, count = _sel_out(scores, cap, idx, count)
-    nKb = scores.shape[-1]
     name = _sel_name("spa_select_topk", algo)
+    B, M, idx, count = _sel_out(scores, cap, idx, count, seq_len, prefill)
+    nKb = scores.shape[-1]
     st = getattr(lib(), name)(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
                               k, _ptr(idx), _ptr(count), cap, None, 0, _stream())
     _check(name, st)
@@ -291,10 +353,9 @@ def _sel_name(base, algo):
 def spa_select_topp(scores, blk, n_sink, n_local, beta, p, k_min, k_max, cap, seq_len=None, prefill=False,
                     q_blk0=0, idx=None, count=None, algo="sort") -> Tuple[torch.Tensor, torch.Tensor]:
     """algo "sort" calls spa_select_topp, "hist" spa_select_topp_hist."""
-    _dev(scores, "scores", torch.int32)
-    B, M, idx, count = _sel_out(scores, cap, idx, count)
-    nKb = scores.shape[-1]
     name = _sel_name("spa_select_topp", algo)
+    B, M, idx, count = _sel_out(scores, cap, idx, count, seq_len, prefill)
+    nKb = scores.shape[-1]
     st = getattr(lib(), name)(_ptr(scores), B, M, nKb, q_blk0, _ptr(seq_len), blk, n_sink, n_local, int(prefill),
                               float(beta), float(p), k_min, k_max, _ptr(idx), _ptr(count), cap, None, 0, _stream())
     _check(name, st)
@@ -304,12 +365,20 @@ def spa_select_topp(scores, blk, n_sink, n_local, beta, p, k_min, k_max, cap, se
 def spa_score_select_decode(qI, kI, w, seq_len, blk, n_sink, n_local, cap, mode="topp", k=0, beta=1.0, p=0.9,
                             k_min=0, k_max=0, scores_out=None, idx=None, count=None):
     """Fused decode scoring + selection; returns (idx, count)."""
-    _dev(qI, "qI", torch.int8)
-    _dev(kI, "kI", torch.int8)
-    _dev(w, "w", torch.int8)
-    _dev(seq_len, "seq_len", torch.int32)
+    if mode not in ("topk", "topp"):
+        raise ValueError(f"mode must be 'topk' or 'topp', not {mode!r}")
+    _want(qI, "qI", dtype=torch.int8)
+    if qI.dim() != 3:
+        raise ValueError("qI must be [B, H_idx, r]")
     B, H, r = qI.shape
-    nKb = kI.shape[1]
+    nKb = kI.shape[1] if kI.dim() == 4 else -1
+    _want(kI, "kI", (B, nKb, H, r), torch.int8)
+    _want(w, "w", (B, H), torch.int8)
+    _want(seq_len, "seq_len", (B,), torch.int32)
+    _want(scores_out, "scores_out", (B, nKb), torch.int32, optional=True)
+    _want(idx, "idx", (B, cap), torch.int32, optional=True)
+    _want(count, "count", (B,), torch.int32, optional=True)
+    _on_device(qI=qI, kI=kI, w=w, seq_len=seq_len, scores_out=scores_out, idx=idx, count=count)
     if idx is None:
         idx = torch.empty((B, cap), dtype=torch.int32, device=qI.device)
     if count is None:
@@ -346,18 +415,31 @@ def spa_sparse_decode_attn_grouped(q, k_cache, v_cache, seq_len, idx, count, blk
 
 def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode, local_sink_tok, local_window_tok,
                  scale, out_dtype, out, lse, ws, want_lse):
-    _dev(q, "q")
-    _dev(k_cache, "k_cache", q.dtype)
-    _dev(v_cache, "v_cache", q.dtype)
-    _dev(seq_len, "seq_len", torch.int32)
-    _dev(idx, "idx", torch.int32)
-    _dev(count, "count", torch.int32)
+    _want(q, "q")
+    if q.dim() != 3:
+        raise ValueError(f"{name}: q must be [B, Hq, d]")
+    io = _io_dtype(q)
     B, Hq, d = q.shape
-    _, Hkv, Tcap, _ = k_cache.shape
+    if k_cache.dim() != 4:
+        raise ValueError(f"{name}: k_cache must be [B, Hkv, Tcap, d]")
+    Hkv, Tcap = k_cache.shape[1], k_cache.shape[2]
+    _want(k_cache, "k_cache", (B, Hkv, Tcap, d), q.dtype)
+    _want(v_cache, "v_cache", (B, Hkv, Tcap, d), q.dtype)
+    _want(seq_len, "seq_len", (B,), torch.int32)
+    rows = (B, Hkv) if name.endswith("_grouped") else (B,)
     cap = idx.shape[-1]
-    rows = B * Hkv if name.endswith("_grouped") else B
-    if idx.numel() != rows * cap or count.numel() != rows:
-        raise ValueError(f"{name}: idx must hold {rows} lists of {cap} and count {rows} entries")
+    _want(idx, "idx", rows + (cap,), torch.int32)
+    _want(count, "count", rows, torch.int32)
+    _want(head_mode, "head_mode", (Hkv,), torch.uint8, optional=True)
+    if out is not None:
+        out_dtype = out.dtype
+    _io_dtype(torch.empty(0, dtype=out_dtype))
+    _want(out, "out", (B, Hq, d), out_dtype, optional=True)
+    _want(lse, "lse", (B, Hq), torch.float32, optional=True)
+    need = spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d)
+    _ws(ws, need)
+    _on_device(q=q, k_cache=k_cache, v_cache=v_cache, seq_len=seq_len, idx=idx, count=count, head_mode=head_mode,
+               out=out, lse=lse, ws=ws)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -365,11 +447,8 @@ def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if ws is None:
-        ws = torch.empty(max(1, spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d)), dtype=torch.uint8,
-                         device=q.device)
-    if head_mode is not None:
-        _dev(head_mode, "head_mode", torch.uint8)
-    st = getattr(lib(), name)(_ptr(q), _ptr(k_cache), _ptr(v_cache), _io_dtype(q), _ptr(seq_len), _ptr(idx),
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    st = getattr(lib(), name)(_ptr(q), _ptr(k_cache), _ptr(v_cache), io, _ptr(seq_len), _ptr(idx),
                               _ptr(count), cap, blk, _ptr(head_mode), local_sink_tok, local_window_tok, B, Hq, Hkv, d,
                               Tcap, float(scale), _ptr(out), _io_dtype(out), _ptr(lse), _ptr(ws), ws.numel(),
                               _stream())
@@ -385,18 +464,19 @@ def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q
     """``order="slot"``: q, out [B, Hq, Tq, d] hold the chunk's slots.  ``order="original"``:
     q, out [B, Hq, T, d] (and lse [B, Hq, T]) in original token order, rows q_pos[b, slot];
     Tq (the chunk length) defaults to T - q_blk0*blk.  ``kv_order="original"``: k, v in
-    original order (slot t is row k_pos[b, t])."""
+    original order (slot t is row k_pos[b, t]).  idx [B, ceil(Tq/blk), cap], count
+    [B, ceil(Tq/blk)]; q_pos, k_pos [B, T] int32."""
     if kv_order not in ("slot", "original"):
         raise ValueError(f"kv_order must be 'slot' or 'original', not {kv_order!r}")
-    _dev(q, "q", torch.bfloat16)
-    _dev(k, "k", torch.bfloat16)
-    _dev(v, "v", torch.bfloat16)
-    _dev(idx, "idx", torch.int32)
-    _dev(count, "count", torch.int32)
     if order not in ("slot", "original"):
         raise ValueError(f"order must be 'slot' or 'original', not {order!r}")
+    _want(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, rows, d] and k, v [B, Hkv, T, d]")
     B, Hq, Tr, d = q.shape
-    _, Hkv, T, _ = k.shape
+    Hkv, T = k.shape[1], k.shape[2]
+    _want(k, "k", (B, Hkv, T, d), torch.bfloat16)
+    _want(v, "v", (B, Hkv, T, d), torch.bfloat16)
     if order == "slot":
         Tq = Tr if Tq is None else Tq
         if Tq != Tr:
@@ -405,7 +485,20 @@ def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q
         if Tr != T:
             raise ValueError("in original order q holds the whole sequence (T rows)")
         Tq = T - q_blk0 * blk if Tq is None else Tq
+    if q_blk0 < 0 or Tq < 0 or q_blk0 * blk + Tq > T:
+        raise ValueError(f"chunk [{q_blk0 * blk}, {q_blk0 * blk + Tq}) exceeds the {T} key slots")
+    Mq = -(-Tq // blk)
     cap = idx.shape[-1]
+    _want(idx, "idx", (B, Mq, cap), torch.int32)
+    _want(count, "count", (B, Mq), torch.int32)
+    _want(q_pos, "q_pos", (B, T), torch.int32, optional=order == "slot")
+    _want(k_pos, "k_pos", (B, T), torch.int32, optional=kv_order == "slot")
+    if out is not None:
+        out_dtype = out.dtype
+    _io_dtype(torch.empty(0, dtype=out_dtype))
+    _want(out, "out", (B, Hq, Tr, d), out_dtype, optional=True)
+    _want(lse, "lse", (B, Hq, Tr), torch.float32, optional=True)
+    _on_device(q=q, k=k, v=v, idx=idx, count=count, q_pos=q_pos, k_pos=k_pos, out=out, lse=lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
@@ -425,13 +518,15 @@ def spa_block_sparse_prefill(q, k, v, idx, count, blk, q_pos=None, k_pos=None, q
 # ------------------------------------------------------------- permutation --
 
 def spa_segment_permute(src, perm, seg, dim, inverse=False, dst=None) -> torch.Tensor:
-    """Permute ``src`` along ``dim`` (dst[t] = src[perm[t]], or the inverse)."""
-    _dev(src, "src")
-    _dev(perm, "perm", torch.int32)
+    """Permute ``src`` along ``dim`` (dst[t] = src[perm[t]], or the inverse); perm [T] int32."""
+    _want(src, "src")
+    T = src.shape[dim]
+    _want(perm, "perm", (T,), torch.int32)
+    _want(dst, "dst", tuple(src.shape), src.dtype, optional=True)
+    _on_device(src=src, perm=perm, dst=dst)
     if dst is None:
         dst = torch.empty_like(src)
     outer = math.prod(src.shape[:dim])
-    T = src.shape[dim]
     row_bytes = math.prod(src.shape[dim + 1:]) * src.element_size()
     st = lib().spa_segment_permute(_ptr(src), _ptr(dst), outer, T, row_bytes, _ptr(perm), seg, int(inverse),
                                    _stream())
@@ -450,14 +545,20 @@ def spa_importance_permutation(q, k, seg, proxy=64, seq_len=None, scale=None, im
     """Importance of every key from the last ``proxy`` queries and the segment-wise
     descending-importance permutation; q [B, Hq, T, d], k [B, Hkv, T, d] bf16.
     Returns (imp [B, T] fp32, perm [B, T] int32)."""
-    _dev(q, "q", torch.bfloat16)
-    _dev(k, "k", torch.bfloat16)
+    _want(q, "q", dtype=torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, Hq, T, d] and k [B, Hkv, T, d]")
     B, Hq, T, d = q.shape
     Hkv = k.shape[1]
     if k.shape != (B, Hkv, T, d):
         raise ValueError("k must be [B, Hkv, T, d] with q's B, T and d")
-    if seq_len is not None:
-        _dev(seq_len, "seq_len", torch.int32)
+    _want(k, "k", (B, Hkv, T, d), torch.bfloat16)
+    _want(seq_len, "seq_len", (B,), torch.int32, optional=True)
+    _want(imp, "imp", (B, T), torch.float32, optional=True)
+    _want(perm, "perm", (B, T), torch.int32, optional=True)
+    need = spa_importance_permutation_workspace_size(B, Hq, T)
+    _ws(ws, need)
+    _on_device(q=q, k=k, seq_len=seq_len, imp=imp, perm=perm, ws=ws)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if imp is None:
@@ -465,8 +566,7 @@ def spa_importance_permutation(q, k, seg, proxy=64, seq_len=None, scale=None, im
     if perm is None:
         perm = torch.empty((B, T), dtype=torch.int32, device=q.device)
     if ws is None:
-        ws = torch.empty(max(1, spa_importance_permutation_workspace_size(B, Hq, T)), dtype=torch.uint8,
-                         device=q.device)
+        ws = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
     st = lib().spa_importance_permutation(_ptr(q), _ptr(k), B, Hq, Hkv, T, d, _ptr(seq_len), proxy, float(scale), seg,
                                           _ptr(imp), _ptr(perm), _ptr(ws), ws.numel(), _stream())
     _check("spa_importance_permutation", st)

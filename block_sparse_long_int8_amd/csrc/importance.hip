@@ -370,11 +370,12 @@ __global__ void __launch_bounds__(256) importance_sum_kernel(ImpArgs a, int npar
   a.imp[(size_t)b * a.T + t] = v;
 }
 
-// grid (ceil(T/seg), B), block 512: a descending register bitonic sort of the
-// segment's 64-bit keys (bits(importance) << 32) | ~position -- the largest
-// importance first, equal importances by lower position, keys at or past
-// seq_len (importance part 0) after every valid key and in their own order,
-// padding (key 0, position all ones) last -- then the permutation.
+// grid (ceil(T/seg), B), block kSortThreads (1024, four keys each): a
+// descending register bitonic sort of the segment's 64-bit keys
+// (bits(importance) << 32) | ~position -- the largest importance first, equal
+// importances by lower position, keys at or past seq_len (importance part 0)
+// after every valid key and in their own order, padding (key 0, position all
+// ones) last -- then the permutation.
 __global__ void __launch_bounds__(kSortThreads) importance_sort_kernel(ImpArgs a) {
   __shared__ unsigned long long lds[kSortMax];
   const int b = blockIdx.y;
