@@ -2,10 +2,14 @@
 
 DecodeStep:  spa_index_score -> spa_select_topk | spa_select_topp (or both in
              one launch: spa_score_select_decode) -> spa_sparse_decode_attn
-PrefillStep: spa_segment_permute (K, V, per-token indexer vectors)
-             -> spa_index_score (per-token, pooled) -> spa_select_topk (prefill rows)
-             -> spa_block_sparse_prefill (original order: Q read and O written at
-                each query's original position, so neither is permuted)
+PrefillStep: [spa_importance_permutation, or the caller's permutation]
+             -> per chunk of query blocks:
+                spa_index_score (per-token vectors in original order, pooled per
+                block of the permuted order by gathering through the slot
+                positions) -> spa_select_topk (prefill rows)
+                -> spa_block_sparse_prefill (Q, K, V read and O, lse written at
+                   each slot's original position, so nothing is copied into the
+                   permuted order and nothing is inverse-permuted)
 
 Only marshalling lives here; every step runs in the HIP library.
 """
@@ -172,6 +176,7 @@ class PrefillSpec:
     select_algo: str = "sort"     # "sort" (bitonic) | "hist" (radix threshold, no sort)
     perm_kind: str = "given"      # "given" (the caller's permutation) | "importance" (computed per call)
     proxy: int = 64               # proxy queries of the importance permutation
+    chunk: int = 0                # query tokens per chunk (0: one chunk covering T); a multiple of seg
 
     @property
     def nb(self) -> int:
@@ -181,9 +186,14 @@ class PrefillSpec:
     def cap(self) -> int:
         return max(1, min(self.nb, self.n_sink + self.n_local + 1 + self.k))
 
+    @property
+    def chunk_blocks(self) -> int:
+        """Query blocks per chunk."""
+        return self.nb if self.chunk <= 0 else min(self.nb, self.chunk // self.blk)
+
 
 class PrefillStep:
-    """Permuted block-sparse prefill of one attention layer (one chunk covering T).
+    """Permuted block-sparse prefill of one attention layer, in chunks of query blocks.
 
     The permutation is the caller's (``perm`` [T], shared by the batch, or
     [B, T]) or, with ``spec.perm_kind == "importance"``, computed on the device
@@ -192,15 +202,27 @@ class PrefillStep:
     block's tokens through the slot positions, and the attention reads Q, K
     and V and writes O (``out``) and the log-sum-exp (``lse``) in the original
     token order through the same positions.
+
+    With ``spec.chunk`` the query blocks run in chunks of that many tokens
+    (chunked prefill): each chunk scores its rows against the key blocks before
+    them, selects and attends.  A chunk is a whole number of permutation
+    segments, so no segment straddles two chunks, and the results are the
+    one-shot results bit for bit.
     """
 
     def __init__(self, spec: PrefillSpec, device="cuda"):
         self.spec = s = spec
+        if s.chunk < 0 or (s.chunk and (s.chunk % s.seg or s.chunk % s.blk)):
+            raise ValueError(f"chunk ({s.chunk}) must be a whole number of segments ({s.seg}) and blocks ({s.blk})")
         dev = torch.device(device)
-        self.scores = torch.empty((s.B, s.nb, s.nb), dtype=torch.int32, device=dev)
-        self.idx = torch.empty((s.B, s.nb, s.cap), dtype=torch.int32, device=dev)
-        self.count = torch.empty((s.B, s.nb), dtype=torch.int32, device=dev)
-        n = L.spa_index_score_workspace_size(s.B, s.H_idx, s.r, s.nb, s.nb, L.SPA_SCORE_PREFILL_TOKENS)
+        cb = s.chunk_blocks
+        self.chunks = [(a0, min(cb, s.nb - a0)) for a0 in range(0, s.nb, cb)]
+        # per chunk: scores [B, m, nb], block lists [B, m, cap], counts [B, m]
+        self._scores = [torch.empty((s.B, m, s.nb), dtype=torch.int32, device=dev) for _, m in self.chunks]
+        self._idx = [torch.empty((s.B, m, s.cap), dtype=torch.int32, device=dev) for _, m in self.chunks]
+        self._count = [torch.empty((s.B, m), dtype=torch.int32, device=dev) for _, m in self.chunks]
+        n = max(L.spa_index_score_workspace_size(s.B, s.H_idx, s.r, m, s.nb, L.SPA_SCORE_PREFILL_TOKENS)
+                for _, m in self.chunks)
         self.score_ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
         self.out = torch.empty((s.B, s.Hq, s.T, s.d), dtype=s.out_dtype, device=dev)
         self.lse = torch.empty((s.B, s.Hq, s.T), dtype=torch.float32, device=dev)
@@ -212,6 +234,25 @@ class PrefillStep:
             self.imp_ws = torch.empty(max(1, n), dtype=torch.uint8, device=dev)
         elif s.perm_kind != "given":
             raise ValueError(f"perm_kind must be 'given' or 'importance', not {s.perm_kind!r}")
+
+    @staticmethod
+    def _rows(parts):
+        return parts[0] if len(parts) == 1 else torch.cat(parts, dim=1)
+
+    @property
+    def scores(self) -> torch.Tensor:
+        """Block-pair scores of every query block, [B, nb, nb] (a copy when chunked)."""
+        return self._rows(self._scores)
+
+    @property
+    def idx(self) -> torch.Tensor:
+        """Selected key blocks of every query block, [B, nb, cap] (a copy when chunked)."""
+        return self._rows(self._idx)
+
+    @property
+    def count(self) -> torch.Tensor:
+        """Number of selected key blocks of every query block, [B, nb] (a copy when chunked)."""
+        return self._rows(self._count)
 
     def importance(self, q, k):
         """Importance-sorted segment permutation of each sequence (PBS-Attn §3) into self.perm."""
@@ -228,34 +269,53 @@ class PrefillStep:
             self.pos = perm.reshape(1, -1) if s.B == 1 else perm.reshape(1, -1).expand(s.B, -1).contiguous()
         return self.pos
 
-    def score(self, qI_tok, kI_tok, w):
-        """Pool the per-token vectors (original order) into the blocks of the permuted order, gathered
-        through the slot positions, and score every (query block, past key block)."""
-        s = self.spec
-        return L.spa_index_score(qI_tok, kI_tok, w, s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS, scores=self.scores,
-                                 ws=self.score_ws, tok_pos=self.pos)
+    @staticmethod
+    def _w_rows(w, a0, m):
+        ws = w[:, a0:a0 + m]
+        return ws if ws.is_contiguous() else ws.contiguous()
 
-    def select(self):
+    def score(self, qI_tok, kI_tok, w, c=None):
+        """Pool the per-token vectors (original order) into the blocks of the permuted order, gathered
+        through the slot positions, and score each query block of chunk ``c`` (every chunk if None)
+        against the key blocks before it."""
         s = self.spec
-        return L.spa_select_topk(self.scores, s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, idx=self.idx,
-                                 count=self.count, algo=s.select_algo)
+        for ci in (range(len(self.chunks)) if c is None else (c,)):
+            a0, m = self.chunks[ci]
+            L.spa_index_score(qI_tok, kI_tok, self._w_rows(w, a0, m), s.blk, mode=L.SPA_SCORE_PREFILL_TOKENS,
+                              q_blk0=a0, Mq=m, nKb=s.nb, scores=self._scores[ci], ws=self.score_ws, tok_pos=self.pos)
+        return self._scores[0] if len(self.chunks) == 1 else None
+
+    def select(self, c=None):
+        s = self.spec
+        for ci in (range(len(self.chunks)) if c is None else (c,)):
+            a0, _ = self.chunks[ci]
+            L.spa_select_topk(self._scores[ci], s.blk, s.n_sink, s.n_local, s.k, s.cap, prefill=True, q_blk0=a0,
+                              idx=self._idx[ci], count=self._count[ci], algo=s.select_algo)
+        return (self._idx[0], self._count[0]) if len(self.chunks) == 1 else None
 
     def front(self, qI_tok, kI_tok, w):
         """Pool and score the indexer inputs in the permuted order, then select (after set_perm)."""
         self.score(qI_tok, kI_tok, w)
         self.select()
-        return self.idx, self.count
 
-    def attend(self, q, k, v):
-        """Attention of every query over its block's selected key blocks (q, k, v and out in original order)."""
+    def attend(self, q, k, v, c=None):
+        """Attention of every query of chunk ``c`` (every chunk if None) over its block's selected key
+        blocks (q, k, v and out in original order)."""
         s = self.spec
-        return L.spa_block_sparse_prefill(q, k, v, self.idx, self.count, s.blk, q_pos=self.pos, k_pos=self.pos,
-                                          out=self.out, lse=self.lse, order="original", kv_order="original")
+        for ci in (range(len(self.chunks)) if c is None else (c,)):
+            a0, m = self.chunks[ci]
+            Tq = min(m * s.blk, s.T - a0 * s.blk)
+            L.spa_block_sparse_prefill(q, k, v, self._idx[ci], self._count[ci], s.blk, q_pos=self.pos,
+                                       k_pos=self.pos, q_blk0=a0, Tq=Tq, out=self.out, lse=self.lse,
+                                       order="original", kv_order="original")
+        return self.out, self.lse
 
     def __call__(self, q, k, v, qI_tok, kI_tok, w, perm=None):
         if self.spec.perm_kind == "importance":
             perm = self.importance(q, k)
         self.set_perm(perm)
-        self.front(qI_tok, kI_tok, w)
-        self.attend(q, k, v)
+        for ci in range(len(self.chunks)):
+            self.score(qI_tok, kI_tok, w, ci)
+            self.select(ci)
+            self.attend(q, k, v, ci)
         return self.out

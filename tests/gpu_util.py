@@ -10,10 +10,28 @@ def dev(x: np.ndarray, dtype: str = None) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
+def check_list_rows(idx: np.ndarray, count: np.ndarray):
+    """Every selection row as the library writes it: count in [0, cap], the first count entries
+    strictly ascending (so free of duplicates) and non-negative, the rest of the row -1."""
+    cap = idx.shape[-1]
+    rows = idx.reshape(-1, cap)
+    cnt = count.reshape(-1)
+    assert rows.shape[0] == cnt.shape[0], "idx and count rows differ"
+    for r in range(rows.shape[0]):
+        c = int(cnt[r])
+        assert 0 <= c <= cap, f"row {r}: count {c} outside [0, {cap}]"
+        live = rows[r, :c]
+        assert (live >= 0).all(), f"row {r}: negative block index in the list"
+        assert (np.diff(live) > 0).all(), f"row {r}: list not strictly ascending"
+        assert (rows[r, c:] == -1).all(), f"row {r}: entries past count are not -1"
+
+
 def sel_lists(idx: torch.Tensor, count: torch.Tensor):
-    """Device idx/count -> nested python lists of selected block indices."""
+    """Device idx/count -> nested python lists of selected block indices (rows checked
+    ascending, duplicate-free and padded with -1 first)."""
     idx = idx.cpu().numpy()
     count = count.cpu().numpy()
+    check_list_rows(idx, count)
     if idx.ndim == 2:
         return [idx[b, :count[b]].tolist() for b in range(idx.shape[0])]
     return [[idx[b, i, :count[b, i]].tolist() for i in range(idx.shape[1])] for b in range(idx.shape[0])]
@@ -41,6 +59,8 @@ def check_topp_row(gpu_sel, info, k_min, k_max, p, tol=1e-5):
     res = set(info["reserved"])
     order = info["order"]
     cum = info["cum"]
+    gpu_sel = list(gpu_sel)
+    assert all(a < b for a, b in zip(gpu_sel, gpu_sel[1:])), "GPU list not strictly ascending"
     assert res <= set(gpu_sel), "reserved block missing"
     chosen = [j for j in gpu_sel if j not in res]
     kg = len(chosen)

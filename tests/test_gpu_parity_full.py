@@ -1,8 +1,9 @@
 """GPU parity at the named workloads' full sizes, in the launch
 configuration the benchmark uses.  Decode workloads are checked in full
 (the oracle finishes them in seconds); the 64K permuted prefill is checked
-bit-exactly on every score and every selected block list, and on sampled
-query blocks for the attention output.
+bit-exactly on every score and every selected block list, on the first and
+last query block of every 4096-token segment for the attention output, and,
+run in 8192-token chunks, bit for bit against the one-shot run.
 """
 import numpy as np
 import pytest
@@ -20,6 +21,12 @@ def S():
     import block_sparse_long_int8_amd as mod
     mod.lib()
     return mod
+
+
+def segment_ends(cfg):
+    """The first and the last query block of every permutation segment."""
+    spb = cfg.seg // cfg.blk
+    return sorted({b for s0 in range(0, cfg.nb, spb) for b in (s0, min(cfg.nb, s0 + spb) - 1)})
 
 
 FULL_DECODE = [gen.TINY_DECODE, gen.DECODE_32K, gen.DECODE_64K_HEADSPLIT, gen.DECODE_128K_TOPP]
@@ -152,8 +159,9 @@ def test_full_prefill_64k_parity(S):
     front = O.prefill_front(inp)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
     assert sel_lists(step.idx, step.count) == front["sel"]
-    blocks = [0, 1, 2, 63, 64, 65, 511, 1023]
-    print(f"[full prefill parity] {cfg.name}: oracle attention on blocks {blocks}", flush=True)
+    blocks = segment_ends(cfg)
+    print(f"[full prefill parity] {cfg.name}: oracle attention on {len(blocks)} blocks (each segment's first and "
+          f"last)", flush=True)
     ref = O.prefill_step(inp, front=front, blocks=blocks)
     slots = np.concatenate([np.arange(i * cfg.blk, (i + 1) * cfg.blk) for i in blocks])
     # the query in slot t is written at its original position perm[t]
@@ -190,8 +198,37 @@ def test_full_prefill_64k_importance_parity(S):
     front = O.prefill_front(inp2)
     assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), front["scores"])
     assert sel_lists(step.idx, step.count) == front["sel"]
-    blocks = [0, 1, 63, 64, 512, 1023]
+    blocks = segment_ends(cfg)
+    print(f"[full prefill parity] {cfg.name}: oracle attention on {len(blocks)} blocks", flush=True)
     ref = O.prefill_step(inp2, front=front, blocks=blocks)
     slots = np.concatenate([np.arange(i * cfg.blk, (i + 1) * cfg.blk) for i in blocks])
-    o_g = out[:, :, torch.from_numpy(use[slots].astype(np.int64)).cuda()].cpu().numpy()
-    attn_close(o_g, ref["o_slot"][:, :, slots])
+    rows = torch.from_numpy(use[slots].astype(np.int64)).cuda()
+    attn_close(out[:, :, rows].cpu().numpy(), ref["o_slot"][:, :, slots])
+    assert np.allclose(step.lse[:, :, rows].cpu().numpy(), ref["lse_slot"][:, :, slots], atol=1e-4, rtol=1e-5)
+
+
+def test_full_prefill_64k_chunked_equals_one_shot(S):
+    """The 64K permuted prefill run as a chunked prefill, 8 chunks of 8192 tokens (each chunk
+    scores, selects and attends its query blocks against the key blocks before them),
+    equals the one-shot run bit for bit: scores, block lists, O and lse."""
+    cfg = gen.PREFILL_64K
+    print(f"[full prefill chunked] {cfg.name}: generating", flush=True)
+    inp = gen.make(cfg)
+    t = [dev(inp["q"], "bf16"), dev(inp["k"], "bf16"), dev(inp["v"], "bf16"), dev(inp["qI_tok"]),
+         dev(inp["kI_tok"]), dev(inp["w"]), dev(inp["perm"])]
+
+    def spec(chunk):
+        return S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                             k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, chunk=chunk)
+    one = S.PrefillStep(spec(0))
+    one(*t)
+    torch.cuda.synchronize()
+    print(f"[full prefill chunked] {cfg.name}: one shot done, 8 chunks next", flush=True)
+    ch = S.PrefillStep(spec(8192))
+    assert len(ch.chunks) == 8
+    ch(*t)
+    torch.cuda.synchronize()
+    assert torch.equal(ch.scores, one.scores)
+    assert torch.equal(ch.idx, one.idx) and torch.equal(ch.count, one.count)
+    assert torch.equal(ch.out, one.out)
+    assert torch.equal(ch.lse, one.lse)
