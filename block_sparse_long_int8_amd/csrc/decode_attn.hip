@@ -38,6 +38,8 @@
 //     descriptors (item, first token, valid count) are computed 64 at a time,
 //     one per lane, so no tile waits on a dependent index load.
 // fp32 tile (d in {64, 128}): plain VALU version of the same online softmax.
+#include <atomic>
+
 #include "spa_internal.h"
 
 namespace spa {
@@ -846,21 +848,28 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
 }
 
-int g_workers = 0;
+// Persistent decode workers per device, filled on first use.  Threads that
+// race on the first call compute the same value, and the atomic makes the
+// race well defined.  Devices past kMaxDevices are queried on every call.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_workers[kMaxDevices];
 
 }  // namespace
 
 int decode_workers() {
-  if (g_workers == 0) {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    // kOcc 4-wave workgroups per CU, one tile in flight per wave
-    g_workers = cus * kOcc * kWPB;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  std::atomic<int>* slot = dev < kMaxDevices ? &g_workers[dev] : nullptr;
+  if (slot) {
+    const int cached = slot->load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
   }
-  return g_workers;
+  int cus = 256, v = 0;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+  // kOcc 4-wave workgroups per CU
+  const int workers = cus * kOcc * kWPB;
+  if (slot) slot->store(workers, std::memory_order_relaxed);
+  return workers;
 }
 
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers) {

@@ -28,11 +28,13 @@
  *     trusted: they must satisfy the stated ranges.  The optional device-side
  *     checks (spa_set_debug_checks) verify them before a call's kernels run.
  *   - Pointers to bf16/fp32/int tensors must be 16-byte aligned.
- *   - The only process-wide state is a cache of the GPU's compute-unit count,
- *     taken on first use (it sets the decode work split and so the decode
- *     workspace size; size and call on the same device), and the on/off
- *     switch of the device-side checks.  Calls on different streams may run
- *     concurrently as long as their workspaces do not overlap.
+ *   - The only process-wide state is a per-device cache of each GPU's
+ *     compute-unit count, taken atomically on first use on that device (it
+ *     sets the decode work split and so the decode workspace size; size and
+ *     call with the same device current), and the on/off switch of the
+ *     device-side checks.  Calls from several host threads, and calls on
+ *     different streams, may run concurrently as long as their workspaces do
+ *     not overlap.
  *   - bf16 is passed as its 16-bit pattern (uint16 storage).
  */
 #ifndef SPA_H_
