@@ -73,6 +73,8 @@ def parse():
                     help="counter-measured HBM traffic of the dominant launch (default profiles/<workload>_traffic.json)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="run one plain device copy of this size before the timed steps (counter calibration)")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="prefill: query tokens per chunk (0 = one chunk covering the sequence)")
     a = ap.parse_args()
     prefill = a.workload.startswith("prefill")
     if a.steps is None:
@@ -102,12 +104,17 @@ def source_sha(*names) -> str:
 
 
 def load_traffic(path, sha):
-    """Counter-measured bytes per launch, if they were taken on the current kernel source."""
+    """Counter-measured HBM bytes per launch of the dominant kernel, as stored by profile_summary.py, if
+    they were taken on the current kernel source (else None: the counters would describe another kernel)."""
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tj = json.load(f)
     return tj.get("traffic_bytes_per_launch") if tj.get("kernel_source_sha") == sha else None
+
+
+TRAFFIC_NOTE = ("stored counter figure (rocprofv3 FETCH_SIZE and WRITE_SIZE passes scaled by a copy of known size, "
+                "profiles/{w}_traffic.json), not measured in this run; null when the kernel source changed since")
 
 
 def pct(v, q):
@@ -124,14 +131,18 @@ def dev(x, dt=None):
 
 
 def calibration_copy(mib):
+    """One plain copy of ``mib`` MiB through the library's permute_kernel (identity permutation:
+    exactly mib MiB read and mib MiB written), the reference the HBM byte counters are scaled by."""
     import torch
-    n = mib << 20
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
+
+    import block_sparse_long_int8_amd as S
+    rows = (mib << 20) // 4096
+    src = torch.ones((1, rows, 4096), dtype=torch.uint8, device="cuda")
+    perm = torch.arange(rows, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
-    dst.copy_(src)
+    S.spa_segment_permute(src, perm, rows, dim=1)
     torch.cuda.synchronize()
-    del src, dst
+    del src, perm
     log(f"[bench] calibration copy of {mib} MiB done")
 
 
@@ -254,31 +265,27 @@ def bench_decode(args, cfg):
     log(f"[bench] inputs resident: {copies} copies of {per_copy / 2**30:.3f} GiB; "
         f"{(ab + ib) / 1e6:.1f} MB touched per step")
 
-    # HIP graphs: one per input set (a single step) and one chunk of
-    # C = min(copies, steps) consecutive steps on input sets 0 .. C-1, so that
-    # the steps inside a chunk follow each other without a launch boundary.
-    # The timed steps use input set j % copies for step j.
+    # HIP graphs: one graph of C = min(copies, steps) consecutive steps on input
+    # sets 0 .. C-1 (steps inside a graph follow each other without a launch
+    # boundary) and one of the remaining K mod C steps; the timed steps use input
+    # set j % copies for step j.
     use_graph = args.launch == "graph" and copies <= 64
     step_args = [(x["q"], x["k"], x["v"], x["qI"], sel_keys(x), x["w"], seq_len, head_mode) for x in sets]
     chunk_len = min(copies, args.steps)
-    graphs = [step.capture(*a) for a in step_args] if use_graph else None
+    tail_len = args.steps % chunk_len
     chunk = step.capture_steps(step_args[:chunk_len]) if use_graph else None
+    tail = step.capture_steps(step_args[:tail_len]) if use_graph and tail_len else None
     if use_graph:
-        log(f"[bench] captured {len(graphs)} single-step graphs and a {chunk_len}-step graph")
+        log(f"[bench] captured a {chunk_len}-step graph" + (f" and a {tail_len}-step graph" if tail else ""))
 
-    def run_steps(n):
-        """Launch n steps on input sets 0, 1, ... (mod copies)."""
-        j = 0
+    def launches(n):
+        """The launches of n steps on input sets 0, 1, ... (mod copies): (graph or None, steps)."""
+        out, j = [], 0
         while j < n:
-            if use_graph and j % copies == 0 and n - j >= chunk_len:
-                chunk.replay()
-                j += chunk_len
-            elif use_graph:
-                graphs[j % copies].replay()
-                j += 1
-            else:
-                run(j)
-                j += 1
+            m = chunk_len if n - j >= chunk_len else n - j
+            out.append((chunk if m == chunk_len else tail, m) if use_graph else (None, 1))
+            j += m if use_graph else 1
+        return out
 
     def run(i, ev=None):
         x = sets[i % copies]
@@ -295,24 +302,39 @@ def bench_decode(args, cfg):
         if ev is not None:
             ev[2].record()
 
+    def run_steps(n):
+        """Untimed steps: whole graphs of chunk_len steps (n rounded up), or eager steps."""
+        for j in range(-(-n // chunk_len) if use_graph else n):
+            chunk.replay() if use_graph else run(j)
+
     run_steps(args.warmup)
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
         calibration_copy(args.copy_calibration_mib)
 
-    # the timed steps: launches only, bracketed by one event pair
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the timed steps, an event after each launch (a graph of chunk_len steps, or one eager step);
+    # value comes from the first and last event, the per-step spread from the launches between them
+    plan = launches(args.steps)
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
-    run_steps(args.steps)
-    stop.record()
+    evt[0].record()
+    j = 0
+    for n, (g, m) in enumerate(plan):
+        if g is not None:
+            g.replay()
+        else:
+            run(j)
+        j += m
+        evt[n + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
+    total_ms = evt[0].elapsed_time(evt[-1])
+    per_step = [evt[n].elapsed_time(evt[n + 1]) / m for n, (_, m) in enumerate(plan)]
     ms_step = total_ms / args.steps
-    log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events, {wall * 1e3:.3f} ms wall")
+    log(f"[bench] timed {args.steps} steps in {len(plan)} launches: {total_ms:.3f} ms on events, "
+        f"{wall * 1e3:.3f} ms wall")
     # a second pass of the same steps with events between the stages, for the per-stage breakdown
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -353,8 +375,12 @@ def bench_decode(args, cfg):
                    "select_path": args.select_path, "select_algo": args.select_algo},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_source": TRAFFIC_NOTE.format(w=args.workload),
                      "kernel": "spa_sparse_decode_attn (decode main kernel + decode_merge_kernel)",
                      "algorithmic_bytes_per_launch": ab, "avg_launch_ms": attn_s * 1e3},
+        "step_ms_p10_p50_p90": [pct(per_step, 10), pct(per_step, 50), pct(per_step, 90)],
+        "step_timing": (f"events around each timed graph launch ({chunk_len} steps each), per step"
+                        if use_graph else "events around each timed step"),
         "stages_ms": {select_name: float(np.mean(sel_ms)), "attention": float(np.mean(attn_ms))},
         "staged_step_ms_p10_p50_p90": [pct(step_ms, 10), pct(step_ms, 50), pct(step_ms, 90)],
         "stage_timing": "a second pass of the same steps, launched call by call with events between stages",
@@ -444,7 +470,7 @@ def bench_prefill(args, cfg):
     importance = cfg.perm_kind == "importance"
     spec = S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
                          k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, select_algo=args.select_algo,
-                         perm_kind="importance" if importance else "given", proxy=cfg.proxy)
+                         perm_kind="importance" if importance else "given", proxy=cfg.proxy, chunk=args.chunk)
     step = S.PrefillStep(spec)
     step(x["q"], x["k"], x["v"], x["qI"], x["kI"], x["w"], None if importance else x["perm"])
     torch.cuda.synchronize()
@@ -480,14 +506,15 @@ def bench_prefill(args, cfg):
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
         calibration_copy(args.copy_calibration_mib)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evt = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
+    evt[0].record()
     for i in range(args.steps):
         run()
-    stop.record()
+        evt[i + 1].record()
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
+    total_ms = evt[0].elapsed_time(evt[-1])
+    per_step = [evt[j].elapsed_time(evt[j + 1]) for j in range(args.steps)]
     ms_step = total_ms / args.steps
     log(f"[bench] timed {args.steps} steps: {total_ms:.3f} ms on events")
     # a second pass with events between the stages, for the per-stage breakdown
@@ -498,6 +525,7 @@ def bench_prefill(args, cfg):
     st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
 
     idx, counts = step.idx[0].cpu().numpy(), step.count[0].cpu().numpy()
+    chunks = len(step.chunks)
     used_perm = step.perm[0].cpu().numpy() if importance else inp["perm"]
     pairs = prefill_pairs(used_perm, idx, counts, cfg.blk)
     flop = 4.0 * cfg.d * cfg.Hq * pairs * cfg.B
@@ -525,12 +553,17 @@ def bench_prefill(args, cfg):
                    "blk": cfg.blk, "H_idx": cfg.H_idx, "r": cfg.r, "k": cfg.k, "n_sink": cfg.n_sink,
                    "seg": cfg.seg, "causal": True, "seed": args.seed, "select_algo": args.select_algo,
                    "permutation": "importance-sorted (last query block as proxy)" if importance
-                   else "uniform random per segment", "heavy_hitter_frac": cfg.hh_frac},
+                   else "uniform random per segment", "heavy_hitter_frac": cfg.hh_frac,
+                   "chunks": chunks, "chunk_tokens": args.chunk or cfg.T},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-                     "kernel": "spa_block_sparse_prefill (prefill attention kernel)",
-                     "algorithmic_flop_per_launch": flop, "attended_pairs_per_head": pairs,
-                     "avg_launch_ms": attn_s * 1e3},
+                     "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic if chunks == 1 else None,
+                     "traffic_source": TRAFFIC_NOTE.format(w=args.workload) + " (one-chunk runs only)",
+                     "kernel": "spa_block_sparse_prefill (prefill attention kernel"
+                               + (f", {chunks} launches per step" if chunks > 1 else "") + ")",
+                     "algorithmic_flop_per_launch": flop / chunks, "attended_pairs_per_head": pairs,
+                     "avg_launch_ms": attn_s * 1e3 / chunks},
+        "step_ms_p10_p50_p90": [pct(per_step, 10), pct(per_step, 50), pct(per_step, 90)],
+        "step_timing": "events between the timed steps themselves",
         "stages_ms": st_ms,
         "stage_timing": "a second pass of the same steps with events between stages",
         "scoring": {"int8_ops": score_ops, "tops": score_ops / score_s / 1e12,
