@@ -75,6 +75,8 @@ _SIGS = {
     "spa_sparse_decode_attn_grouped": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
                                             _f, _vp, _i, _vp, _vp, _sz, _vp]),
     "spa_sparse_decode_attn_workspace_size": (_sz, [_i, _i, _i, _i]),
+    "spa_sparse_decode_attn_noalloc": (_i, [_vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                            _f, _vp, _i, _vp, _vp]),
     "spa_block_sparse_prefill": (_i, [_vp, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f,
                                       _vp, _i, _vp, _i, _vp, _sz, _vp]),
     "spa_segment_permute": (_i, [_vp, _vp, _i64, _i, _sz, _vp, _i, _i, _vp]),
@@ -413,6 +415,15 @@ def spa_sparse_decode_attn_grouped(q, k_cache, v_cache, seq_len, idx, count, blk
                         head_mode, local_sink_tok, local_window_tok, scale, out_dtype, out, lse, ws, want_lse)
 
 
+def spa_sparse_decode_attn_noalloc(q, k_cache, v_cache, seq_len, idx, count, blk, head_mode=None, local_sink_tok=0,
+                                   local_window_tok=0, scale=None, out_dtype=torch.float32, out=None, lse=None,
+                                   want_lse=True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """spa_sparse_decode_attn on the library's own workspace (no workspace argument; the library
+    allocates nothing).  Pass ``out`` (and ``lse``) to keep torch from allocating them."""
+    return _decode_attn("spa_sparse_decode_attn_noalloc", q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
+                        local_sink_tok, local_window_tok, scale, out_dtype, out, lse, None, want_lse)
+
+
 def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode, local_sink_tok, local_window_tok,
                  scale, out_dtype, out, lse, ws, want_lse):
     _want(q, "q")
@@ -436,6 +447,7 @@ def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
     _io_dtype(torch.empty(0, dtype=out_dtype))
     _want(out, "out", (B, Hq, d), out_dtype, optional=True)
     _want(lse, "lse", (B, Hq), torch.float32, optional=True)
+    noalloc = name.endswith("_noalloc")
     need = spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d)
     _ws(ws, need)
     _on_device(q=q, k_cache=k_cache, v_cache=v_cache, seq_len=seq_len, idx=idx, count=count, head_mode=head_mode,
@@ -446,12 +458,12 @@ def _decode_attn(name, q, k_cache, v_cache, seq_len, idx, count, blk, head_mode,
         out = torch.empty((B, Hq, d), dtype=out_dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    if ws is None:
+    if ws is None and not noalloc:
         ws = torch.empty(max(1, need), dtype=torch.uint8, device=q.device)
+    tail = () if noalloc else (_ptr(ws), ws.numel())
     st = getattr(lib(), name)(_ptr(q), _ptr(k_cache), _ptr(v_cache), io, _ptr(seq_len), _ptr(idx),
                               _ptr(count), cap, blk, _ptr(head_mode), local_sink_tok, local_window_tok, B, Hq, Hkv, d,
-                              Tcap, float(scale), _ptr(out), _io_dtype(out), _ptr(lse), _ptr(ws), ws.numel(),
-                              _stream())
+                              Tcap, float(scale), _ptr(out), _io_dtype(out), _ptr(lse), *tail, _stream())
     _check(name, st)
     return out, lse
 

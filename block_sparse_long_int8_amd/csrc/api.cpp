@@ -456,6 +456,27 @@ spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, co
                        scale, out, out_dtype, lse, ws, ws_bytes, stream);
 }
 
+spa_status spa_sparse_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                          const int32_t* count, int cap, int blk,
+                                          const uint8_t* head_mode, int local_sink_tok,
+                                          int local_window_tok, int B, int Hq, int Hkv, int d,
+                                          int Tcap, float scale, void* out, int out_dtype, float* lse,
+                                          void* stream) {
+  const char* fn = "spa_sparse_decode_attn_noalloc";
+  const size_t need = spa_sparse_decode_attn_workspace_size(B, Hq, Hkv, d);
+  const size_t have = spa::decode_scratch_bytes();
+  REQUIRE(need <= have, SPA_ERR_UNSUPPORTED,
+          "B=%d Hq=%d Hkv=%d d=%d needs %zu bytes of decode workspace; the library's own scratch holds %zu "
+          "(use spa_sparse_decode_attn with a workspace)", B, Hq, Hkv, d, need, have);
+  void* ws = nullptr;
+  const hipError_t e = spa::decode_scratch(&ws);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, fn, "scratch address lookup failed: %d (%s)", (int)e, hipGetErrorString(e));
+  return decode_common(fn, 0, q, k_cache, v_cache, io_dtype, seq_len, idx, count, cap, blk, head_mode,
+                       local_sink_tok, local_window_tok, B, Hq, Hkv, d, Tcap, scale, out, out_dtype, lse, ws, have,
+                       stream);
+}
+
 // ----------------------------------------------------------------- prefill --
 
 spa_status spa_block_sparse_prefill(const void* q, int q_blk0, int Tq, const void* k,

@@ -39,6 +39,7 @@
 //     one per lane, so no tile waits on a dependent index load.
 // fp32 tile (d in {64, 128}): plain VALU version of the same online softmax.
 #include <atomic>
+#include <mutex>
 
 #include "spa_internal.h"
 
@@ -848,6 +849,19 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   if (a.lse && c4 == 0) a.lse[(size_t)b * a.Hq + g * G + h] = lse_v;
 }
 
+// Decode workspace for callers that cannot allocate (spa_sparse_decode_attn_noalloc):
+// one file-scope device array per GPU the library runs on, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol); it looks up the array's device
+// address once per device, with that device current, and uses that address.
+// The decode kernels need nothing in it cleared: workgroup 0 writes the plan
+// header and item offsets, every wave writes the partials it produces, and
+// the merge reads only those.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::mutex g_scratch_lock;
+void* g_scratch_addr[64];  // per device, guarded by g_scratch_lock
+
 // Persistent decode workers per device, filled on first use.  Threads that
 // race on the first call compute the same value, and the atomic makes the
 // race well defined.  Devices past kMaxDevices are queried on every call.
@@ -870,6 +884,25 @@ int decode_workers() {
   const int workers = cus * kOcc * kWPB;
   if (slot) slot->store(workers, std::memory_order_relaxed);
   return workers;
+}
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= (int)(sizeof(g_scratch_addr) / sizeof(g_scratch_addr[0]))) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_lock);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *ptr = g_scratch_addr[dev];
+  return hipSuccess;
 }
 
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers) {

@@ -136,6 +136,10 @@ struct DecodeArgs {
 };
 size_t decode_ws_bytes(int B, int Hq, int Hkv, int d, int workers);
 int decode_workers();  // persistent workers (waves) for the current device
+// The library's own decode workspace on the current device (a file-scope device
+// array of decode_scratch_bytes(); its address is looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // Key importance and importance-sorted segment permutation (importance.hip)

@@ -351,6 +351,31 @@ spa_status spa_sparse_decode_attn_grouped(const void* q, const void* k_cache, co
                                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * spa_sparse_decode_attn_noalloc -- spa_sparse_decode_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): no workspace argument.
+ *
+ * Arguments, outputs, limits and the arithmetic are those of
+ * spa_sparse_decode_attn (the same kernels).  The workspace is a 16 MiB device
+ * array that the library holds on each GPU it runs on until the process ends;
+ * its address is looked up on the first call on each device (with that device
+ * current).  The call allocates nothing and frees nothing.
+ * Errors: SPA_ERR_UNSUPPORTED if spa_sparse_decode_attn_workspace_size(B, Hq,
+ * Hkv, d) exceeds 16 MiB (about B*Hkv + 2048 <= 4032 partial slots at 8 query
+ * heads per KV head); otherwise as spa_sparse_decode_attn.
+ * Every call on one GPU shares that GPU's array: calls ordered on one stream are
+ * fine, but two calls that may overlap in time on one GPU (different streams, or
+ * different host threads without ordering) race and give undefined results.
+ */
+spa_status spa_sparse_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          int io_dtype, const int32_t* seq_len, const int32_t* idx,
+                                          const int32_t* count, int cap, int blk,
+                                          const uint8_t* head_mode, int local_sink_tok,
+                                          int local_window_tok, int B, int Hq, int Hkv, int d,
+                                          int Tcap, float scale, void* out, int out_dtype, float* lse,
+                                          void* stream);
+
+/*
  * spa_block_sparse_prefill -- causal attention of a query chunk over selected key blocks.
  *
  * PBS-Attn page: block-sparse attention that skips key blocks outside a
