@@ -16,8 +16,9 @@
 // DPP row moves, 16 a swizzle, 32 a permute, and only stages that pair
 // different waves go through LDS;
 // top-k keeps the first k, top-p turns the sorted scores into fp32 masses
-// exp(beta * (s - s_max)), scans them in rank order and keeps the shortest
-// prefix whose normalised mass reaches p (clamped to [k_min, k_max]).  A
+// exp(beta * (s - s_max)) (one hardware exp2 each), scans them in rank order
+// and keeps the shortest prefix whose mass reaches p times the total (clamped
+// to [k_min, k_max]).  A
 // bitmask over block indices then emits the reserved and kept blocks in
 // ascending order with a block-wide prefix count.
 #include "bitonic.h"
@@ -112,7 +113,7 @@ __device__ __forceinline__ void block_max2_int(int& a, int& b, int* scratch) {
 // grid: B*M rows; block N / EPT threads; dynamic LDS: N * 8 bytes.
 // Sorts the row's candidates (N = 2^LOG2N >= candidates) in rank order.
 template <int LOG2N, bool SCORED>
-__global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
+__global__ void __launch_bounds__(kSortThreads) select_kernel(SelectArgs a) {
   constexpr int N = 1 << LOG2N;
   constexpr int EPT = N > 2 * kSortThreads ? N / kSortThreads : 2;
   extern __shared__ unsigned long long lds64[];
@@ -152,7 +153,7 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
     const int H = a.H;
     const int4* krow = reinterpret_cast<const int4*>(a.kI + (size_t)b * nKb * H * 16);
     const int npairs = nbv << log2H;
-    constexpr int U = 8;  // loads in flight per thread
+    constexpr int U = 16;  // loads in flight per thread
     for (int p0 = 0; p0 < npairs; p0 += U * (int)blockDim.x) {
       int4 kv[U];
 #pragma unroll
@@ -170,7 +171,13 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
         dot = __builtin_amdgcn_sdot4(qv.z, kv[u].z, dot, false);
         dot = __builtin_amdgcn_sdot4(qv.w, kv[u].w, dot, false);
         int v = p < npairs ? w_s[h] * max(dot, 0) : 0;
-        for (int o = 1; o < H; o <<= 1) v += __shfl_xor(v, o, kWave);
+        // sum over the block's H neighbouring lanes (lane moves, no LDS round trip)
+        if (H >= 2) v += (int)lane_xor<1>((unsigned)v);
+        if (H >= 4) v += (int)lane_xor<2>((unsigned)v);
+        if (H >= 8) v += (int)lane_xor<4>((unsigned)v);
+        if (H >= 16) v += (int)lane_xor<8>((unsigned)v);
+        if (H >= 32) v += (int)lane_xor<16>((unsigned)v);
+        if (H >= 64) v += (int)lane_xor<32>((unsigned)v);
         if (p < npairs && h == 0) s_lds[p >> log2H] = v;
       }
     }
@@ -251,26 +258,30 @@ __global__ void __launch_bounds__(kMaxThreads) select_kernel(SelectArgs a) {
   } else if (n_cand == 0) {
     k_sel = 0;
   } else {
+    // masses exp(beta (s - s_max)) as exp2 of a prescaled argument (one
+    // v_exp_f32 each); the cumulative mass is compared with p * Z
     float mass[EPT];
     float local = 0.f;
+    const float bl2 = a.beta * 1.4426950408889634f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int r = tid * EPT + e;
-      mass[e] = r < n_cand ? expf(a.beta * (float)((long long)rscore[e] - smax)) : 0.f;
+      mass[e] = r < n_cand ? __builtin_amdgcn_exp2f(bl2 * (float)((long long)rscore[e] - smax)) : 0.f;
       local += mass[e];
     }
     float Z;
     float run = block_excl_scan_float(local, fscratch, &Z);
-    // k_p = 1 + the first rank at which the normalised cumulative mass
-    // reaches p (cumulative mass does not decrease with rank, so this is one
-    // rank up to rounding at thread boundaries; the minimum keeps it
-    // deterministic; no crossing only if rounding keeps the total below p)
+    const float pz = a.p * Z;
+    // k_p = 1 + the first rank at which the cumulative mass reaches p * Z
+    // (cumulative mass does not decrease with rank, so this is one rank up to
+    // rounding at thread boundaries; the minimum keeps it deterministic; no
+    // crossing only if rounding keeps the total below p * Z)
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const int r = tid * EPT + e;
-      const bool before = run / Z < a.p;
+      const bool before = run < pz;
       run += mass[e];
-      if (r < n_cand && before && !(run / Z < a.p)) atomicMin(&kp_s, r + 1);
+      if (r < n_cand && before && !(run < pz)) atomicMin(&kp_s, r + 1);
     }
     __syncthreads();
     const int kp = min(kp_s, n_cand);
