@@ -22,6 +22,13 @@
 // operand fragments of the two products are read from LDS one step ahead of
 // the MFMAs that consume them.
 //
+// The two buffers are separate LDS arrays and the tile loop is unrolled by
+// two, so every LDS read names its buffer at compile time.  The compiler
+// must otherwise assume that a read may overlap a global->LDS load still in
+// flight and waits for all of them (vmcnt(0)) before it: with one array
+// indexed by u & 1, each tile's V and position reads waited for the next
+// tile's loads to land, which serialised the prefetch with the compute.
+//
 // Per 64-key tile a wave computes, with v_mfma_f32_32x32x16_bf16:
 //   S^T[64 keys, 32 queries] = K . Q^T      (2 x 8 MFMA)
 //   O^T[128, 32 queries]    += V^T . P^T    (4 x 4 MFMA)
@@ -61,10 +68,19 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
-struct Smem {
-  uint8_t k[2][TILEB];
-  uint8_t v[2][TILEB];
-  int32_t pos[2][BLK];
+// the two staging buffers, as distinct objects (see above)
+__shared__ __attribute__((aligned(16))) uint8_t lds_k0[TILEB];
+__shared__ __attribute__((aligned(16))) uint8_t lds_k1[TILEB];
+__shared__ __attribute__((aligned(16))) uint8_t lds_v0[TILEB];
+__shared__ __attribute__((aligned(16))) uint8_t lds_v1[TILEB];
+__shared__ __attribute__((aligned(16))) int32_t lds_p0[BLK];
+__shared__ __attribute__((aligned(16))) int32_t lds_p1[BLK];
+
+template <int S> struct Slot {
+  static constexpr int value = S;
+  static __device__ __forceinline__ uint8_t* k() { return S ? lds_k1 : lds_k0; }
+  static __device__ __forceinline__ uint8_t* v() { return S ? lds_v1 : lds_v0; }
+  static __device__ __forceinline__ int32_t* pos() { return S ? lds_p1 : lds_p0; }
 };
 
 // byte offset of 16-byte chunk c of row r inside a swizzled tile
@@ -87,29 +103,30 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return v;
 }
 
-// Stage key block tok0 (K, V rows and positions) into buffer `slot`.  Wave w
+// Stage key block tok0 (K, V rows and positions) into buffer S.  Wave w
 // moves rows 8w..8w+7 of K and of V: each instruction writes 1 KB (4 rows) at
 // LDS base + 16*lane, so lane l fetches the global chunk that the swizzle
 // places at its slot.  Rows past T re-read row T-1 (masked later).
 // src[n4] is the row of K and V that holds this lane's slot of the tile: the
 // slot itself, or with K/V in original order its original position.
-__device__ __forceinline__ void stage(Smem& sm, const uint16_t* __restrict__ kb,
-                                      const uint16_t* __restrict__ vb, const int32_t* __restrict__ kpos,
-                                      int tok0, int T, int slot, int w, int lane, const int (&src)[2]) {
+template <int S>
+__device__ __forceinline__ void stage(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
+                                      const int32_t* __restrict__ kpos, int tok0, int T, int w, int lane,
+                                      const int (&src)[2]) {
   const int cpos = lane & 15;
 #pragma unroll
   for (int n4 = 0; n4 < 2; ++n4) {
     const int r0 = 8 * w + 4 * n4;
     const int r = r0 + (lane >> 4);
     const size_t row = (size_t)src[n4] * D;
-    __builtin_amdgcn_global_load_lds(kb + row + 8 * (cpos ^ (r & 15)), (lds_void_t*)(sm.k[slot] + r0 * ROWB), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(vb + row + 8 * (cpos ^ vsw(r)), (lds_void_t*)(sm.v[slot] + r0 * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(kb + row + 8 * (cpos ^ (r & 15)), (lds_void_t*)(Slot<S>::k() + r0 * ROWB), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(vb + row + 8 * (cpos ^ vsw(r)), (lds_void_t*)(Slot<S>::v() + r0 * ROWB), 16, 0, 0);
   }
   if (w == 0) {
     if (kpos)
-      __builtin_amdgcn_global_load_lds(kpos + min(tok0 + lane, T - 1), (lds_void_t*)sm.pos[slot], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds(kpos + min(tok0 + lane, T - 1), (lds_void_t*)Slot<S>::pos(), 4, 0, 0);
     else
-      sm.pos[slot][lane] = tok0 + lane;
+      Slot<S>::pos()[lane] = tok0 + lane;
   }
 }
 
@@ -118,7 +135,6 @@ __device__ __forceinline__ void stage(Smem& sm, const uint16_t* __restrict__ kb,
 // consecutive workgroups -- which the dispatcher spreads over the XCDs --
 // work on different KV heads and the longest lists start first.
 __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) Smem sm;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   const int G = a.Hq / a.Hkv;
@@ -199,7 +215,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   int tk1 = nsel > 1 ? __builtin_amdgcn_readlane(chunk, 1) * BLK : 0;
   int src1[2], src2[2] = {0, 0};
   kv_src(tk0, src1);
-  stage(sm, kb, vb, kpos, tk0, a.T, 0, w, lane, src1);
+  stage<0>(kb, vb, kpos, tk0, a.T, w, lane, src1);
   kv_src(tk1, src1);
 
   // Q^T fragments (B operand): lane holds query slot row, d = 16ks + 8hi .. +7
@@ -222,8 +238,9 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   float mrun = -INFINITY, lsum = 0.f;
   const int grp = lane >> 4, s16 = lane & 15;
 
-  for (int u = 0; u < nsel; ++u) {
-    const int slot = u & 1;
+  // one tile: compute tile u from buffer S while tile u+1 streams into the other
+  auto tile = [&](auto slot_tag, const int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
     const int tok0 = tk0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile u have landed
     __syncthreads();
@@ -235,14 +252,14 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
       tk2 = __builtin_amdgcn_readlane(chunk, (u + 2) & 63) * BLK;
       kv_src(tk2, src2);
     }
-    if (u + 1 < nsel) stage(sm, kb, vb, kpos, tk1, a.T, slot ^ 1, w, lane, src1);
+    if (u + 1 < nsel) stage<S ^ 1>(kb, vb, kpos, tk1, a.T, w, lane, src1);
     tk0 = tk1;
     tk1 = tk2;
     src1[0] = src2[0];
     src1[1] = src2[1];
     const bool need_mask =
-        force_mask || tok0 + BLK > a.T || __any((int)(tok0 + lane < a.T && sm.pos[slot][lane] > qmin));
-    if (!active) continue;
+        force_mask || tok0 + BLK > a.T || __any((int)(tok0 + lane < a.T && Slot<S>::pos()[lane] > qmin));
+    if (!active) return;
 
     // ---- S^T = K . Q^T
     f32x16 s[2];
@@ -250,7 +267,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[mt][e] = 0.f;
-    const uint8_t* kt = sm.k[slot];
+    const uint8_t* kt = Slot<S>::k();
     bf16x8 kf[8][2];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
@@ -276,7 +293,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
 #pragma unroll
         for (int aa = 0; aa < 4; ++aa) {
           const int key0 = 32 * mt + 8 * aa + 4 * hi;
-          const int4 kp4 = *reinterpret_cast<const int4*>(&sm.pos[slot][key0]);
+          const int4 kp4 = *reinterpret_cast<const int4*>(&Slot<S>::pos()[key0]);
           const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
@@ -302,21 +319,21 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     }
     const float nb = mrun == -INFINITY ? 0.f : -mrun;
     bf16x8 pf[4];
-    float ps = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: no 32-long dependent chain
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4) {
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = __builtin_amdgcn_exp2f(fmaf(s[kb4 >> 1][8 * (kb4 & 1) + e], c2, nb));
-        ps += p[e];
+        ps[e & 3] += p[e];
       }
       pf[kb4] = as_bf16x8(uint4{cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                                 cvt_pk_bf16(p[6], p[7])});
     }
-    lsum += ps;
+    lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
     // ---- O^T += V^T . P^T
-    const uint8_t* vt = sm.v[slot];
+    const uint8_t* vt = Slot<S>::v();
     bf16x8 vf[4][4];
 #pragma unroll
     for (int kb4 = 0; kb4 < 4; ++kb4)
@@ -343,6 +360,10 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  for (int u = 0; u < nsel; u += 2) {
+    tile(Slot<0>{}, u);
+    if (u + 1 < nsel) tile(Slot<1>{}, u + 1);
   }
   if (!active || !row_ok) return;
 
