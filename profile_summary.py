@@ -15,7 +15,9 @@ Two kinds of runs feed it:
   copy (bytes / counter KiB), the ratio to the algorithmic bytes, and MFMA utilisation
   as rocprofv3 defines MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (the GUI-active
   cycles of one XCD x SIMDs); the per-dispatch GRBM_GUI_ACTIVE value sums the 8 XCDs) when
-  those counters were taken; ``--json PATH`` also writes the traffic figures for bench.py.
+  those counters were taken; ``--json PATH`` also writes the traffic figures for bench.py:
+  the first kernel's, or with ``--op NAME,NAME=ALG_BYTES`` the sum over an operation made of
+  several launches (one dispatch of each per call).
 
 Kernels are matched by exact name: the demangled function name without its namespace,
 argument list or return type, with or without its template arguments
@@ -184,13 +186,26 @@ def counters(args):
         out.append(f"| `{name}` | {fmt(e.get('algorithmic_bytes'), 'MB')} | {fmt(e.get('fetch_bytes'), 'MB')} | "
                    f"{fmt(e.get('write_bytes'), 'MB')} | {fmt(e.get('traffic_over_algorithmic'), 'r')} | "
                    f"{fmt(e.get('mfma_util'))} |")
+    op = None
+    if args.op:
+        names, _, alg = args.op.partition("=")
+        names = names.split(",")
+        parts = [summary[n].get("traffic_bytes") for n in names]
+        total = sum(parts) if all(p is not None for p in parts) else None
+        op = {"kernels": names, "traffic_bytes": total, "algorithmic_bytes": float(alg) if alg else None}
+        if total is not None and alg:
+            op["traffic_over_algorithmic"] = total / float(alg)
+        out += ["", f"Operation {' + '.join(names)}: "
+                f"{fmt(total, 'MB')} of HBM traffic per call against {fmt(op['algorithmic_bytes'], 'MB')} "
+                f"algorithmic ({fmt(op.get('traffic_over_algorithmic'), 'r')})."]
     print("\n".join(out))
     if args.json:
         main = summary[args.kernel[0].partition("=")[0]]
         with open(args.json, "w") as f:
-            json.dump({"kernels": summary, "fetch_factor": fetch_f, "write_factor": write_f,
+            json.dump({"kernels": summary, "operation": op, "fetch_factor": fetch_f, "write_factor": write_f,
                        "kernel_source_sha": source_sha(*args.sources) if args.sources else None,
-                       "sources": args.sources, "traffic_bytes_per_launch": main.get("traffic_bytes"),
+                       "sources": args.sources,
+                       "traffic_bytes_per_launch": op["traffic_bytes"] if op else main.get("traffic_bytes"),
                        "commands": args.command}, f, indent=1)
 
 
@@ -211,6 +226,7 @@ def main(argv=None):
     c.add_argument("--note", default="")
     c.add_argument("--json", default=None)
     c.add_argument("--sources", nargs="*", default=[], help="csrc files whose hash tags the traffic figure")
+    c.add_argument("--op", default=None, help="NAME,NAME=ALGORITHMIC_BYTES: an operation of several launches")
     a = ap.parse_args(argv)
     trace(a) if a.what == "trace" else counters(a)
 

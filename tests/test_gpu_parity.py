@@ -490,6 +490,31 @@ def test_topp_edge_cases(algo):
             check_topp_row(gsel[b], info[b], kmin, kmax, p)
 
 
+def test_topp_short_list_and_full_sort():
+    """Top-p rows with 3, 40, 100, 200, 300 and 1500 blocks near the maximum.
+
+    The near blocks score within 40 of the maximum, the rest at least 150,000 below
+    it, so the nucleus lies among the near blocks: fewer than k_min of them (the floor
+    decides), a few dozen to a few hundred (the mass decides), and more than k_max can
+    take (the cap decides).  Every row must satisfy the oracle's set rule.
+    """
+    rng = np.random.default_rng(11)
+    B, nb, blk = 6, 2048, 64
+    beta, p, kmin, kmax = 0.125, 0.9, 16, 512
+    s = rng.integers(-200_000, -100_000, size=(B, nb))
+    for b, n_near in enumerate((3, 40, 100, 200, 300, 1500)):
+        # candidates are blocks 1 .. nb-5 (block 0 is the sink, the last 4 the local window)
+        near = rng.choice(np.arange(1, nb - 4), n_near, replace=False)
+        s[b, near] = 50_000 - rng.integers(0, 41, size=n_near)
+    s = s.astype(np.int32)
+    L = np.full(B, nb * blk, dtype=np.int32)
+    idx, cnt = S.spa_select_topp(dev(s), blk, 1, 4, beta, p, kmin, kmax, 5 + kmax, seq_len=dev(L))
+    gsel = sel_lists(idx, cnt)
+    _, info = O.select_decode(s.astype(np.int64), L, blk, 1, 4, "topp", beta=beta, p=p, k_min=kmin, k_max=kmax)
+    for b in range(B):
+        check_topp_row(gsel[b], info[b], kmin, kmax, p)
+
+
 @pytest.mark.parametrize("spread", [7, 3000, 2_000_000, 1_500_000_000], ids=["r7", "r3e3", "r2e6", "r1.5e9"])
 def test_select_hist_matches_oracle_across_score_ranges(spread):
     """The radix threshold search over one to four 8-bit levels picks the oracle's sets.
