@@ -388,10 +388,7 @@ static spa_status decode_common(const char* fn, int per_group, const void* q, co
   REQUIRE(std::isfinite(scale), SPA_ERR_INVALID_ARG, "scale must be finite");
   REQUIRE(blk == 16 || blk == 32 || blk == 64 || blk == 128, SPA_ERR_UNSUPPORTED, "blk %d not in {16,32,64,128}", blk);
   REQUIRE(Hq / Hkv <= 16, SPA_ERR_UNSUPPORTED, "more than 16 query heads per KV head (%d)", Hq / Hkv);
-  if (io_dtype == SPA_BF16)
-    REQUIRE(d == 128, SPA_ERR_UNSUPPORTED, "bf16 decode supports d == 128 only (got %d)", d);
-  else
-    REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "fp32 decode supports d in {64,128} (got %d)", d);
+  REQUIRE(d == 64 || d == 128, SPA_ERR_UNSUPPORTED, "decode supports d in {64,128} (got %d)", d);
   REQUIRE((long)B * Hkv <= 4096, SPA_ERR_UNSUPPORTED, "B*Hkv = %ld exceeds 4096", (long)B * Hkv);
   if (B == 0) return ok();
   REQUIRE(q && k_cache && v_cache && out && seq_len && idx && count, SPA_ERR_INVALID_ARG, "null tensor pointer");

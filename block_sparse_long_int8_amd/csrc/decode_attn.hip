@@ -235,29 +235,22 @@ __device__ void write_empty_items(const DecodeArgs& a, const int* item_start, in
 }
 
 // ------------------------------------------------------------ bf16 path ----
-constexpr int D = 128;
-
-struct TileRegs {
-  uint4 k[8];  // [mt*4 + j]
-  uint4 v[8];  // [i]
+// Head dimension DD = 128 or 64.  Per 32-token tile, with 16x16x32 MFMAs:
+// S^T[32 tokens, 16 heads] = K . Q^T in 2 x DD/32 products (lane (m, g4)
+// holds key row m of each 16-token half and d = 8 (4 j + g4) .. +7 of d-step
+// j, the same d order as the Q operand), and O^T[DD, 16 heads] += V^T . P^T in
+// VW = DD/16 products, lane m holding d = VW m .. VW m + VW-1 of 8 tokens.
+template <int DD> struct Bf16Shape {
+  static constexpr int KS = DD / 32;  // 32-wide d-steps of the score products
+  static constexpr int VW = DD / 16;  // d values per lane of a V row: 8 (16 bytes) or 4 (8 bytes)
+  static constexpr int VWORDS = VW / 2;
 };
 
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ kb, const uint16_t* __restrict__ vb,
-                                          int tok0, int nvalid, int lane, TileRegs& t) {
-  const int m = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int tau = min(16 * mt + m, nvalid - 1);
-    const uint16_t* row = kb + (size_t)(tok0 + tau) * D;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = load_nt16(row + 8 * (4 * j + g4));
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nvalid - 1);
-    t.v[i] = load_nt16(vb + (size_t)(tok0 + tau) * D + 8 * m);
-  }
-}
+template <int DD>
+struct TileRegs {
+  uint4 k[2 * Bf16Shape<DD>::KS];            // [mt * KS + j]
+  uint32_t v[8][Bf16Shape<DD>::VWORDS];      // [i][word]: VW bf16 of one token row
+};
 
 // Same operand layout through raw buffer loads on the (b, g) slab.  An offset
 // past num_records returns zeros without touching memory, so a tile can be
@@ -271,46 +264,64 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, int off) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 buf_ld8(__amdgpu_buffer_rsrc_t r, int off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kBufNT);
+  return uint2{v.x, v.y};
+}
+
+template <int DD>
 __device__ __forceinline__ void load_tile_buf(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv, int tok0,
-                                              int nvalid, bool real, int lane, TileRegs& t) {
+                                              int nvalid, bool real, int lane, TileRegs<DD>& t) {
+  using SH = Bf16Shape<DD>;
   const int m = lane & 15, g4 = lane >> 4;
   const int nv = real ? nvalid : 1;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int tau = min(16 * mt + m, nv - 1);
-    const int row = real ? (tok0 + tau) * (D * 2) : kBufOOB;
+    const int row = real ? (tok0 + tau) * (DD * 2) : kBufOOB;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) t.k[mt * 4 + j] = buf_ld16(rk, row + (real ? 16 * (4 * j + g4) : 0));
+    for (int j = 0; j < SH::KS; ++j) t.k[mt * SH::KS + j] = buf_ld16(rk, row + (real ? 16 * (4 * j + g4) : 0));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int tau = min(16 * (i >> 2) + 4 * g4 + (i & 3), nv - 1);
-    t.v[i] = buf_ld16(rv, real ? (tok0 + tau) * (D * 2) + 16 * m : kBufOOB);
+    const int off = real ? (tok0 + tau) * (DD * 2) + 2 * SH::VW * m : kBufOOB;
+    if constexpr (SH::VW == 8) {
+      const uint4 u = buf_ld16(rv, off);
+      t.v[i][0] = u.x;
+      t.v[i][1] = u.y;
+      t.v[i][2] = u.z;
+      t.v[i][3] = u.w;
+    } else {
+      const uint2 u = buf_ld8(rv, off);
+      t.v[i][0] = u.x;
+      t.v[i][1] = u.y;
+    }
   }
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
+template <int DD>
 struct HeadState {
-  float m;       // running max of scaled logits (log2 domain), per column
-  float l;       // lane-partial running sum
-  f32x4 o[8];    // O^T accumulators, [jj] -> rows d = 32*g4 + 8*r + jj
+  float m;                           // running max of scaled logits (log2 domain), per column
+  float l;                           // lane-partial running sum
+  f32x4 o[Bf16Shape<DD>::VW];        // O^T accumulators, [jj] -> rows d = VW (4 g4 + r) + jj
 };
 
-__device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg, int nvalid,
-                                          float scale_log2, int lane, HeadState& st) {
+template <int DD>
+__device__ __forceinline__ void tile_math(const TileRegs<DD>& t, const bf16x8* qreg, int nvalid,
+                                          float scale_log2, int lane, HeadState<DD>& st) {
+  using SH = Bf16Shape<DD>;
   const int g4 = lane >> 4;
   f32x4 s[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[mt * 4 + j]), qreg[j], s[mt], 0, 0, 0);
+    for (int j = 0; j < SH::KS; ++j)
+      s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(t.k[mt * SH::KS + j]), qreg[j], s[mt], 0, 0, 0);
   }
   float x[8];
   float tmax = -INFINITY;
@@ -344,21 +355,21 @@ __device__ __forceinline__ void tile_math(const TileRegs& t, const bf16x8* qreg,
   st.m = m_new;
   if (__any((int)resc)) {
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) st.o[jj] *= corr;
+    for (int jj = 0; jj < SH::VW; ++jj) st.o[jj] *= corr;
   }
   // P^T operand: k index 8*g4 + e <-> token 16*(e/4) + 4*g4 + (e%4)
   const uint4 pu = {cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3]), cvt_pk_bf16(p[4], p[5]),
                     cvt_pk_bf16(p[6], p[7])};
   const bf16x8 pb = as_bf16x8(pu);
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    // V^T operand of output rows d = 8m + jj: element jj of each of the 8 token rows
+  for (int jj = 0; jj < SH::VW; ++jj) {
+    // V^T operand of output rows d = VW m + jj: element jj of each of the 8 token rows
     const int wsel = jj >> 1;
     uint32_t a4[4];
 #pragma unroll
     for (int aa = 0; aa < 4; ++aa) {
-      const uint32_t lo = word_of(t.v[2 * aa], wsel);
-      const uint32_t hi = word_of(t.v[2 * aa + 1], wsel);
+      const uint32_t lo = t.v[2 * aa][wsel];
+      const uint32_t hi = t.v[2 * aa + 1][wsel];
       a4[aa] = (jj & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
     }
     const uint4 au = {a4[0], a4[1], a4[2], a4[3]};
@@ -413,8 +424,10 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item
 // before the math of tile t, across item boundaries; the Q operands of the
 // wave's items are staged in LDS up front.  Two workgroups per CU (two waves per SIMD, <= 256 registers
 // each) let one wave's math overlap the other's loads.
-template <int OCC>
+template <int OCC, int DD>
 __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a, int n_items, int workers) {
+  using SH = Bf16Shape<DD>;
+  constexpr int D = DD;
   __shared__ int item_start[kMaxItems + 1];
   __shared__ int scratch[kWPB];
   __shared__ uint4 qcache[kWPB][kQCache][4][kWave];  // Q operands of a wave's first items
@@ -470,7 +483,7 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   auto load_q = [&](int it, uint4* qr) {
     const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < SH::KS; ++j) {
       uint4 qv = {0u, 0u, 0u, 0u};
       if (m < G) qv = *reinterpret_cast<const uint4*>(q + ((size_t)b * a.Hq + g * G + m) * D + 8 * (4 * j + g4));
       qr[j] = qv;
@@ -482,24 +495,24 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   {
     const int it_last = find_item(item_start, n_items, t1 - 1);
     for (int c = 0; c < kQCache && it_first + c <= it_last; ++c) {
-      uint4 qr[4];
+      uint4 qr[SH::KS];
       load_q(it_first + c, qr);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qcache[wv][c][j][lane] = qr[j];
+      for (int j = 0; j < SH::KS; ++j) qcache[wv][c][j][lane] = qr[j];
     }
   }
-  bf16x8 qcur[4];
+  bf16x8 qcur[SH::KS];
   auto set_q = [&](int it) {
     const int c = it - it_first;
-    uint4 qr[4];
+    uint4 qr[SH::KS];
     if (c < kQCache) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) qr[j] = qcache[wv][c][j][lane];
+      for (int j = 0; j < SH::KS; ++j) qr[j] = qcache[wv][c][j][lane];
     } else {
       load_q(it, qr);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qcur[j] = as_bf16x8(qr[j]);
+    for (int j = 0; j < SH::KS; ++j) qcur[j] = as_bf16x8(qr[j]);
   };
   // (b, g) slab of the K and V caches as buffer resources
   const unsigned slab_bytes = (unsigned)((size_t)a.Tcap * D * 2);
@@ -514,16 +527,16 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   };
   // placeholder loads (real == false) fetch nothing; a tile with no valid token
   // is one of them and its math is fully masked
-  auto load_kv = [&](int it, int tok0, int nv, bool real, TileRegs& tr) {
-    load_tile_buf(rsrc(kc, it), rsrc(vc, it), tok0, nv, real && nv > 0, lane, tr);
+  auto load_kv = [&](int it, int tok0, int nv, bool real, TileRegs<DD>& tr) {
+    load_tile_buf<DD>(rsrc(kc, it), rsrc(vc, it), tok0, nv, real && nv > 0, lane, tr);
   };
 
-  HeadState st;
+  HeadState<DD> st;
   auto reset = [&]() {
     st.m = -INFINITY;
     st.l = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) st.o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < SH::VW; ++jj) st.o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
   auto flush = [&](int item) {
     const size_t slot = (size_t)item + w;
@@ -531,13 +544,15 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
     lt += shfl_xor_f(lt, 16);
     lt += shfl_xor_f(lt, 32);
     if (m < G) {
-      float* po = ws.part_o + (slot * G + m) * D + 32 * g4;
+      // this lane's rows d = VW (4 g4 + r) + jj: VW consecutive d per r
+      float* po = ws.part_o + (slot * G + m) * D + 4 * SH::VW * g4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float4 lo4 = {st.o[0][r], st.o[1][r], st.o[2][r], st.o[3][r]};
-        float4 hi4 = {st.o[4][r], st.o[5][r], st.o[6][r], st.o[7][r]};
-        *reinterpret_cast<float4*>(po + 8 * r) = lo4;
-        *reinterpret_cast<float4*>(po + 8 * r + 4) = hi4;
+#pragma unroll
+        for (int q4 = 0; q4 < SH::VW / 4; ++q4) {
+          const float4 o4 = {st.o[4 * q4][r], st.o[4 * q4 + 1][r], st.o[4 * q4 + 2][r], st.o[4 * q4 + 3][r]};
+          *reinterpret_cast<float4*>(po + SH::VW * r + 4 * q4) = o4;
+        }
       }
       if (g4 == 0) {
         ws.part_ml[(slot * G + m) * 2 + 0] = st.m;
@@ -548,7 +563,7 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
 
   // Two register buffers: tile t + 1 (or a placeholder after the last tile)
   // is requested before the math of tile t.
-  TileRegs A, Bt;
+  TileRegs<DD> A, Bt;
   int itA, tokA, nvA, itB = 0, tokB = 0, nvB = 0;
   desc(t0, itA, tokA, nvA);
   set_q(itA);
@@ -913,8 +928,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int n_items = a.B * a.Hkv;
   const int workers = decode_workers();
   const int blocks = workers / kWPB;
-  if (a.io_bf16) {
-    decode_bf16_kernel<kOcc><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+  if (a.io_bf16 && a.d == 64) {
+    decode_bf16_kernel<kOcc, 64><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
+  } else if (a.io_bf16) {
+    decode_bf16_kernel<kOcc, 128><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
   } else if (a.d == 64) {
     decode_f32_kernel<64><<<blocks, kThreads, 0, s>>>(a, n_items, workers);
   } else {

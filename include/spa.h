@@ -318,10 +318,8 @@ spa_status spa_score_select_decode(const int8_t* qI, const int8_t* kI, const int
  * out [B, Hq, d] (out_dtype SPA_F32 or SPA_BF16); lse [B, Hq] fp32 natural-log
  * log-sum-exp of the scaled logits (may be NULL).  A head with no token gets
  * out = 0 and lse = -inf.
- * Supported: bf16 needs d == 128, f32 needs d in {64, 128}; Hq % Hkv == 0,
- * Hq/Hkv <= 16; blk in {16, 32, 64, 128}; B*Hkv <= 4096.  Head dimension 64
- * is therefore an fp32-only shape here: bf16 with d == 64 returns
- * SPA_ERR_UNSUPPORTED (the bf16 kernel's MFMA tiling fixes d at 128).
+ * Supported: d in {64, 128} (bf16 or f32); Hq % Hkv == 0, Hq/Hkv <= 16;
+ * blk in {16, 32, 64, 128}; B*Hkv <= 4096.
  * Workspace: spa_sparse_decode_attn_workspace_size bytes (depends on the
  * current device's compute-unit count).
  */

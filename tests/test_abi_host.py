@@ -104,7 +104,7 @@ def test_decode_attn_rejections(name):
         a = dict(args, **kw)
         return f(*a.values())
 
-    assert call(d=64) == S.SPA_ERR_UNSUPPORTED                 # bf16 needs d = 128
+    assert call(d=96) == S.SPA_ERR_UNSUPPORTED                 # d in {64, 128}
     assert call(Hq=30) == S.SPA_ERR_INVALID_ARG                # not a multiple of Hkv
     assert call(Hq=8 * 17) == S.SPA_ERR_UNSUPPORTED             # G > 16
     assert call(blk=48) == S.SPA_ERR_UNSUPPORTED

@@ -381,6 +381,8 @@ DECODE_EDGE = [
     ("f32_d128", dict(dtype="f32", d=128, Hq=8, Hkv=2)),
     ("blk32", dict(blk=32, k=20)),
     ("blk128", dict(blk=128, k=6, n_plant=(3, 3))),
+    ("bf16_d64", dict(d=64)),
+    ("bf16_d64_blk16_G8", dict(d=64, blk=16, k=40, Hq=16, Hkv=2)),
 ]
 
 
@@ -397,6 +399,29 @@ def test_decode_edge_shapes(name, over):
     gsel = sel_lists(step.idx, step.count)
     assert gsel == ref["sel"]
     attn_close(step.out.cpu().numpy(), ref["o"])
+
+
+@pytest.mark.parametrize("base", [gen.SMALL_DECODE_TOPP, gen.SMALL_DECODE_HEADSPLIT], ids=["topp", "headsplit"])
+def test_decode_bf16_d64(base):
+    """bf16 decode at head dimension 64: top-p lists, and local-window heads beside retrieval heads."""
+    cfg = dataclasses.replace(base, name=base.name + "_d64", d=64)
+    print(f"[decode d64] {cfg.name}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert np.array_equal(step.scores.cpu().numpy().astype(np.int64), ref["scores"])
+    gsel = sel_lists(step.idx, step.count)
+    if cfg.select == "topk":
+        assert gsel == ref["sel"]
+    else:
+        for b in range(cfg.B):
+            check_topp_row(gsel[b], ref["info"][b], cfg.k_min, cfg.k_max, cfg.p)
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], gsel, cfg.blk,
+                                        inp["head_mode"], cfg.local_sink_tok, cfg.local_window_tok)
+    attn_close(step.out.cpu().numpy(), o_ref)
+    assert np.allclose(step.lse.cpu().numpy(), lse_ref, atol=1e-4, rtol=1e-5)
 
 
 def test_decode_at_maximum_items():
