@@ -489,18 +489,6 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
       qr[j] = qv;
     }
   };
-  // Q of the wave's first kQCache items goes to LDS once, so an item switch
-  // inside the tile loop reads LDS instead of waiting on a global load
-  // (global loads complete in order, so that wait would drain the prefetch)
-  {
-    const int it_last = find_item(item_start, n_items, t1 - 1);
-    for (int c = 0; c < kQCache && it_first + c <= it_last; ++c) {
-      uint4 qr[SH::KS];
-      load_q(it_first + c, qr);
-#pragma unroll
-      for (int j = 0; j < SH::KS; ++j) qcache[wv][c][j][lane] = qr[j];
-    }
-  }
   bf16x8 qcur[SH::KS];
   auto set_q = [&](int it) {
     const int c = it - it_first;
@@ -566,8 +554,22 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   TileRegs<DD> A, Bt;
   int itA, tokA, nvA, itB = 0, tokB = 0, nvB = 0;
   desc(t0, itA, tokA, nvA);
-  set_q(itA);
+  // the first tile's K and V are requested before Q: the loads overlap, and
+  // the wait for Q (loads complete in order) then covers the tile as well
   load_kv(itA, tokA, nvA, true, A);
+  // Q of the wave's first kQCache items goes to LDS once, so an item switch
+  // inside the tile loop reads LDS instead of waiting on a global load
+  // (global loads complete in order, so that wait would drain the prefetch)
+  {
+    const int it_last = find_item(item_start, n_items, t1 - 1);
+    for (int c = 0; c < kQCache && it_first + c <= it_last; ++c) {
+      uint4 qr[SH::KS];
+      load_q(it_first + c, qr);
+#pragma unroll
+      for (int j = 0; j < SH::KS; ++j) qcache[wv][c][j][lane] = qr[j];
+    }
+  }
+  set_q(itA);
   int cur = itA;
   reset();
   int t = t0;
