@@ -9,19 +9,22 @@
 // Work decomposition (MI355X: 256 CUs, HBM-bound gather):
 //   * an "item" is one (sequence b, KV head g); its tokens are cut into 32-token
 //     tiles (a selected 64-token block is two tiles);
-//   * all items' tiles are laid end to end and split evenly over a persistent
-//     grid of waves (at least 2 tiles per wave for bf16), so load balance does not
-//     depend on how budgets vary per sequence (dual top-p gives 21..185
-//     blocks per sequence);
+//   * all items' tiles are laid end to end and split over a persistent grid
+//     of waves in contiguous ranges (at least 2 tiles per wave for bf16; the
+//     waves of each compute unit's second workgroup take 80 % of a first-slot
+//     wave's share, see make_split), so load balance does not depend on how
+//     budgets vary per sequence (dual top-p gives 21..185 blocks per
+//     sequence);
 //   * a wave writes one partial (unnormalised o, running max m, running sum l)
 //     per item it touched, into slot item + wave; a second kernel merges the
-//     partials of item i (slots i + w for w = first_tile(i)/share ..
-//     last_tile(i)/share) by log-sum-exp.  (Merging inside the main kernel
+//     partials of item i (slots i + w for the waves w whose ranges hold its
+//     first to last tile) by log-sum-exp.  (Merging inside the main kernel
 //     would need a device-scope release per wave, which on this chip writes
 //     back and invalidates the whole L2 of the XCD: far slower than a launch.)
 //
-// bf16 tile (d = 128, up to 16 query heads per KV head, GQA sharing: K/V are
-// read once per KV head for all its query heads):
+// bf16 tile (d = 128 shown; d = 64 halves the d-steps and the V^T rows; up to
+// 16 query heads per KV head, GQA sharing: K/V are read once per KV head for
+// all its query heads):
 //   S^T[32 tok, 16 heads] = K[32, 128] . Q^T     (2 x 4 MFMA 16x16x32 bf16)
 //   O^T[128, 16 heads]   += V^T[128, 32] . P^T   (8 MFMA 16x16x32 bf16)
 //   - K feeds the A operand straight from HBM: lane (row m, group g4) loads 16
@@ -64,9 +67,13 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 constexpr size_t kHeader = 256;
 constexpr int kQCache = 2;  // items whose Q a wave keeps in LDS
 constexpr int kOcc = 2;     // bf16 workgroups (4 waves each) resident per CU
+#ifndef SPA_SLOW_PCT
+#define SPA_SLOW_PCT 80
+#endif
+constexpr int kSlowPct = SPA_SLOW_PCT;  // tiles of a second-slot wave per 100 of a first-slot wave
 
 struct WsLayout {
-  int* hdr;         // [0] total tiles, [1] share, [2] workers
+  int* hdr;         // [0] total tiles, [1] workers, [2..5] the wave split (s1, s2, t1, half)
   int* item_start;  // [n_items + 1] first tile of each item (copy of the plan)
   float* part_ml;  // [slots][G][2]
   float* part_o;   // [slots][G][d]
@@ -93,11 +100,55 @@ __host__ __device__ inline size_t ws_total(int n_items, int workers, int G, int 
          align256(slots * G * d * sizeof(float));
 }
 
-// Tiles per wave: an even split over the persistent waves, but at least
-// min_share tiles, so that small steps (few sequences) do not scatter into
-// one-tile partials whose merge costs more than the attention itself.
-__device__ __forceinline__ int split_share(int total, int workers, int min_share) {
-  return total > 0 ? max((total + workers - 1) / workers, min_share) : 0;
+// The persistent waves' tile ranges, in wave order: waves w < half take s1
+// tiles each from tile 0, the others s2 each from tile t1 = half * s1 (the
+// last ranges may be short or empty).  Every wave takes at least min_share
+// tiles, so that small steps (few sequences) do not scatter into one-tile
+// partials whose merge costs more than the attention itself.  slow_pct sets
+// s2 relative to s1: the second half of the waves sit in each compute unit's
+// second workgroup slot, and while both slots stream, the older workgroup's
+// waves win the SIMDs' issue arbitration; measured per-wave timestamps put
+// the second slot's tile rate at about two thirds of the first's, so an even
+// split leaves the first slot idle for the last third of the kernel.  While
+// both slots stream, HBM is the bound, so the gain is the tail only (1-2 %
+// of the 128K decode attention at 80 %).
+struct Split {
+  int s1, s2, t1, half;
+};
+
+__host__ __device__ inline Split make_split(int total, int workers, int min_share, int slow_pct) {
+  Split sp{0, 0, 0, workers / 2};
+  if (total <= 0) return sp;
+  const int rest = workers - sp.half;
+  const long den = (long)sp.half * 100 + (long)rest * slow_pct;
+  sp.s1 = max(min_share, (int)(((long)total * 100 + den - 1) / den));
+  sp.s2 = max(min_share, sp.s1 * slow_pct / 100);
+  while ((long)sp.half * sp.s1 + (long)rest * sp.s2 < total) {
+    ++sp.s1;
+    sp.s2 = max(min_share, sp.s1 * slow_pct / 100);
+  }
+  sp.t1 = sp.half * sp.s1;
+  return sp;
+}
+__device__ __forceinline__ int split_begin(const Split& sp, int w) {
+  return w < sp.half ? w * sp.s1 : sp.t1 + (w - sp.half) * sp.s2;
+}
+__device__ __forceinline__ int split_len(const Split& sp, int w) { return w < sp.half ? sp.s1 : sp.s2; }
+// the wave whose range holds tile t
+__device__ __forceinline__ int split_wave(const Split& sp, int t) {
+  return t < sp.t1 ? t / sp.s1 : sp.half + (t - sp.t1) / sp.s2;
+}
+// the split travels from the main kernel to the merge in the workspace header
+__device__ __forceinline__ void store_split(const WsLayout& ws, int total, int workers, const Split& sp) {
+  ws.hdr[0] = total;
+  ws.hdr[1] = workers;
+  ws.hdr[2] = sp.s1;
+  ws.hdr[3] = sp.s2;
+  ws.hdr[4] = sp.t1;
+  ws.hdr[5] = sp.half;
+}
+__device__ __forceinline__ Split load_split(const WsLayout& ws) {
+  return Split{ws.hdr[2], ws.hdr[3], ws.hdr[4], ws.hdr[5]};
 }
 
 __device__ __forceinline__ void wave_sync() {
@@ -433,23 +484,19 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   __shared__ uint4 qcache[kWPB][kQCache][4][kWave];  // Q operands of a wave's first items
   __shared__ int4 tdesc[kWPB][kWave];                 // descriptors of 64 consecutive tiles
   const int total = build_plan(a, n_items, item_start, scratch);
-  const int share = split_share(total, workers, 2);
+  const Split sp = make_split(total, workers, 2, kSlowPct);
   const int G = a.Hq / a.Hkv;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, D);
   if (blockIdx.x == 0) {
     for (int t = threadIdx.x; t <= n_items; t += kThreads) ws.item_start[t] = item_start[t];
-    if (threadIdx.x == 0) {
-      ws.hdr[0] = total;
-      ws.hdr[1] = share;
-      ws.hdr[2] = workers;
-    }
+    if (threadIdx.x == 0) store_split(ws, total, workers, sp);
     write_empty_items(a, item_start, n_items, G, D, &scratch[0]);
   }
-  if (share == 0) return;
+  if (sp.s1 == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int w = blockIdx.x * kWPB + threadIdx.x / kWave;
-  const int t0 = w * share;
-  const int t1 = min(total, t0 + share);
+  const int t0 = split_begin(sp, w);
+  const int t1 = min(total, t0 + split_len(sp, w));
   if (t0 >= t1) return;
 
   const int tpb = (a.blk + kTile - 1) / kTile;
@@ -618,24 +665,20 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
   __shared__ float p_s[kWPB][16][kTile];
   __shared__ float mnew_s[kWPB][16];
   const int total = build_plan(a, n_items, item_start, scratch);
-  const int share = split_share(total, workers, 1);
+  const Split sp = make_split(total, workers, 1, 100);  // an even split
   const int G = a.Hq / a.Hkv;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, DD);
   if (blockIdx.x == 0) {
     for (int t = threadIdx.x; t <= n_items; t += kThreads) ws.item_start[t] = item_start[t];
-    if (threadIdx.x == 0) {
-      ws.hdr[0] = total;
-      ws.hdr[1] = share;
-      ws.hdr[2] = workers;
-    }
+    if (threadIdx.x == 0) store_split(ws, total, workers, sp);
     write_empty_items(a, item_start, n_items, G, DD, &scratch[0]);
   }
-  if (share == 0) return;
+  if (sp.s1 == 0) return;
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
   const int w = blockIdx.x * kWPB + wv;
-  int t = w * share;
-  const int t_end = min(total, t + share);
+  int t = split_begin(sp, w);
+  const int t_end = min(total, t + split_len(sp, w));
   if (t >= t_end) return;
   const int tpb = (a.blk + kTile - 1) / kTile;
   const float scale_log2 = a.scale * kLog2e;
@@ -766,11 +809,11 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int item = blockIdx.x / hgroups;
   const int hg = blockIdx.x - item * hgroups;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
-  const int share = ws.hdr[1];
+  const Split sp = load_split(ws);
   const int s0 = ws.item_start[item], s1 = ws.item_start[item + 1];
-  if (s1 <= s0 || share <= 0) return;
-  const int w0 = s0 / share;
-  const int nparts = (s1 - 1) / share - w0 + 1;
+  if (s1 <= s0 || sp.s1 <= 0) return;
+  const int w0 = split_wave(sp, s0);
+  const int nparts = split_wave(sp, s1 - 1) - w0 + 1;
   const int per_head = d / 4;
   const int pairs = kMergeGH * per_head;  // <= 256 (kMergeGH * d <= 1024)
   const int nsub = kMergeThreads / pairs;
