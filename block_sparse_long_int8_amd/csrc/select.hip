@@ -41,17 +41,41 @@ __device__ __forceinline__ int key_score(unsigned long long k) {
 }
 __device__ __forceinline__ int key_index(unsigned long long k) { return (int)(~(unsigned)k); }
 
+// Wave-wide inclusive prefix sum in registers: row shifts by 1, 2, 4 and 8
+// lanes scan each 16-lane row, then the last lane of row 0 is added to row 1
+// and of row 2 to row 3 (row broadcast 15), and the last lane of row 1 to
+// rows 2 and 3 (row broadcast 31).  Lanes with no source get the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ float wave_incl_scan_float(float x) {
+#define SPA_FSTEP(C, R) x += __builtin_bit_cast(float, dpp_or_zero<C, R>(__builtin_bit_cast(int, x)))
+  SPA_FSTEP(0x111, 0xf);
+  SPA_FSTEP(0x112, 0xf);
+  SPA_FSTEP(0x114, 0xf);
+  SPA_FSTEP(0x118, 0xf);
+  SPA_FSTEP(0x142, 0xa);
+  SPA_FSTEP(0x143, 0xc);
+#undef SPA_FSTEP
+  return x;
+}
+
 // Exclusive prefix sum of one int per thread across the workgroup; returns
 // the exclusive value and writes the total to *total.
 __device__ int block_excl_scan_int(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan_int(v);
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -69,12 +93,7 @@ __device__ int block_excl_scan_int(int v, int* scratch, int* total) {
 __device__ float block_excl_scan_float(float v, float* scratch, float* total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
-  float x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    float y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const float x = wave_incl_scan_float(v);
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
   float off = 0.f, tot = 0.f;
@@ -90,11 +109,18 @@ __device__ float block_excl_scan_float(float v, float* scratch, float* total) {
 }
 
 // Block-wide maximum of a and of b (one exchange through LDS).
+template <int M>
+__device__ __forceinline__ void max2_step(int& a, int& b) {
+  a = max(a, (int)lane_xor<M>((unsigned)a));
+  b = max(b, (int)lane_xor<M>((unsigned)b));
+}
 __device__ __forceinline__ void block_max2_int(int& a, int& b, int* scratch) {
-  for (int o = 1; o < kWave; o <<= 1) {
-    a = max(a, __shfl_xor(a, o, kWave));
-    b = max(b, __shfl_xor(b, o, kWave));
-  }
+  max2_step<1>(a, b);
+  max2_step<2>(a, b);
+  max2_step<4>(a, b);
+  max2_step<8>(a, b);
+  max2_step<16>(a, b);
+  max2_step<32>(a, b);
   const int wid = threadIdx.x / kWave;
   if ((threadIdx.x & (kWave - 1)) == 0) {
     scratch[2 * wid] = a;
@@ -307,13 +333,8 @@ __global__ void __launch_bounds__(kSortThreads) select_kernel(SelectArgs a) {
     if (tid >= kWave) return;
     const unsigned m = tid < nwords ? mask[tid] : 0u;
     const int c = __popc(m);
-    int incl = c;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (tid >= o) incl += y;
-    }
-    const int written = __shfl(incl, kWave - 1, kWave);
+    const int incl = wave_incl_scan_int(c);
+    const int written = __builtin_amdgcn_readlane(incl, kWave - 1);
     int pos = incl - c;
     unsigned mm = m;
     while (mm) {
