@@ -19,28 +19,6 @@ __device__ inline unsigned long long shfl_xor_u64(unsigned long long v, int m) {
   return ((unsigned long long)hi << 32) | lo;
 }
 
-// Value of lane (l ^ M) for a compile-time M: DPP lane moves for M <= 8
-// (quad permutes and row / half-row mirrors), a swizzle for 16, a permute for 32.
-template <int M>
-__device__ __forceinline__ unsigned lane_xor(unsigned v) {
-  const int x = (int)v;
-  if constexpr (M == 1) {
-    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
-  } else if constexpr (M == 2) {
-    return (unsigned)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-  } else if constexpr (M == 4) {
-    const int h = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);     // half-row mirror: l ^ 7
-    return (unsigned)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xF, 0xF, true);   // quad_perm [3,2,1,0]: ^ 3
-  } else if constexpr (M == 8) {
-    const int r = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);     // row mirror: l ^ 15
-    return (unsigned)__builtin_amdgcn_mov_dpp(r, 0x141, 0xF, 0xF, true);  // half-row mirror: ^ 7
-  } else if constexpr (M == 16) {
-    return (unsigned)__builtin_amdgcn_ds_swizzle(x, 0x401F);              // bitmask mode, xor 16
-  } else {
-    return (unsigned)__shfl_xor(x, M, kWave);
-  }
-}
-
 // One compare-exchange stage (k, j) of a descending bitonic sort on 32-bit
 // keys, EPT keys per thread (thread t owns elements t*EPT .. t*EPT+EPT-1).
 template <int EPT, int K, int J>

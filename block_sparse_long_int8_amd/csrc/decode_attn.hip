@@ -163,15 +163,17 @@ __device__ __forceinline__ int list_row(const DecodeArgs& a, int b, int g) {
   return a.per_group ? b * a.Hkv + g : b;
 }
 
-// Number of 32-token tiles of item (b, g).
+// Number of 32-token tiles of item (b, g).  The head mode, the sequence
+// length and the list count are loaded unconditionally (every row of count
+// exists), so the three loads share one round trip.
 __device__ __forceinline__ int item_tiles(const DecodeArgs& a, int b, int g, int tpb) {
+  const int local = a.head_mode ? (int)a.head_mode[g] : 0;
   const int L = a.seq_len[b];
-  if (a.head_mode && a.head_mode[g]) {
-    const int ns = min(a.sink_tok, L);
-    const int wstart = max(ns, L - a.window_tok);
-    return (ns + kTile - 1) / kTile + (L - wstart + kTile - 1) / kTile;
-  }
-  return a.count[list_row(a, b, g)] * tpb;
+  const int cnt = a.count[list_row(a, b, g)];
+  const int ns = min(a.sink_tok, L);
+  const int wstart = max(ns, L - a.window_tok);
+  const int local_tiles = (ns + kTile - 1) / kTile + (L - wstart + kTile - 1) / kTile;
+  return local ? local_tiles : cnt * tpb;
 }
 
 // Block indices of a retrieval item, 64 at a time in the lanes of a wave, so
@@ -447,9 +449,15 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item
     const int it = find_item(item_start, n_items, tt);
     const int u = tt - item_start[it];
     const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
+    // the list entry is loaded before the head mode is known (a local head's
+    // tile reads a clamped, in-bounds entry and ignores it): one round trip
+    const int slot = u / tpb;
+    const int sub = u - slot * tpb;
+    const int local = a.head_mode ? (int)a.head_mode[g] : 0;
     const int L = a.seq_len[b];
+    const int j = a.idx[(size_t)list_row(a, b, g) * a.cap + min(slot, a.cap - 1)];
     win.item = it;
-    if (a.head_mode && a.head_mode[g]) {
+    if (local) {
       const int ns = min(a.sink_tok, L);
       const int wstart = max(ns, L - a.window_tok);
       const int nst = (ns + kTile - 1) / kTile;
@@ -461,9 +469,6 @@ __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item
         win.nvalid = min(kTile, L - win.tok0);
       }
     } else {
-      const int slot = u / tpb;
-      const int sub = u - slot * tpb;
-      const int j = a.idx[(size_t)list_row(a, b, g) * a.cap + slot];
       win.tok0 = j * a.blk + sub * kTile;
       win.nvalid = min(min(kTile, a.blk - sub * kTile), L - win.tok0);
     }

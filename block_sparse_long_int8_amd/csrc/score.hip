@@ -6,7 +6,7 @@
 // §2) and every product is accumulated exactly in int32.
 //
 //  * decode: one lane per (key block, head) for r = 16 (a 16-byte load, four
-//    v_dot4 of 4 MACs each, then a shuffle sum over the block's heads); a
+//    v_dot4 of 4 MACs each, then a lane-move sum over the block's heads); a
 //    thread-per-block loop handles other r.  With per-group selection (SparDA
 //    page, §2 "Indexador de Pronóstico Compacto") the heads split into
 //    consecutive equal groups and each group's sum is a score row of its own.
@@ -99,10 +99,22 @@ __global__ void __launch_bounds__(256) score_decode_kernel(const int8_t* __restr
   }
 }
 
+// Sum over each aligned run of 2^log2hpg lanes (log2hpg <= 6), by register
+// lane moves; every lane of the wave must call it.
+__device__ __forceinline__ int group_sum(int v, int log2hpg) {
+  if (log2hpg >= 1) v += (int)lane_xor<1>((unsigned)v);
+  if (log2hpg >= 2) v += (int)lane_xor<2>((unsigned)v);
+  if (log2hpg >= 3) v += (int)lane_xor<4>((unsigned)v);
+  if (log2hpg >= 4) v += (int)lane_xor<8>((unsigned)v);
+  if (log2hpg >= 5) v += (int)lane_xor<16>((unsigned)v);
+  if (log2hpg >= 6) v += (int)lane_xor<32>((unsigned)v);
+  return v;
+}
+
 // Fast decode path for r == 16 and a power-of-two H <= 64: one lane per
 // (block, head) loads that head's 16 bytes (the wave reads 1 KB contiguous),
 // four v_dot4 give the head dot, ReLU * w, and each group's 2^log2hpg
-// neighbouring lanes sum their heads with xor shuffles.
+// neighbouring lanes sum their heads with register lane moves.
 // grid: ceil(B*nKb*H / 256); block 256.
 __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __restrict__ qI,
                                                                const int8_t* __restrict__ kI,
@@ -133,7 +145,7 @@ __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __r
     dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
     v = valid ? wt * max(dot, 0) : 0;
   }
-  for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
+  v = group_sum(v, log2hpg);
   if (in && (h & ((1 << log2hpg) - 1)) == 0) {
     const int groups = H >> log2hpg;
     scores[((size_t)b * groups + (h >> log2hpg)) * nKb + j] = valid ? v : INT32_MIN_V;
@@ -216,7 +228,7 @@ __global__ void __launch_bounds__(256) score_decode_q4_kernel(const int8_t* __re
       v = valid ? wt * max((dot >> 4) << (e & 7), 0) : 0;
     }
   }
-  for (int o = 1; o < (1 << log2hpg); o <<= 1) v += __shfl_xor(v, o, kWave);
+  v = group_sum(v, log2hpg);
   if (in && (h & ((1 << log2hpg) - 1)) == 0) {
     const int groups = H >> log2hpg;
     scores[((size_t)b * groups + (h >> log2hpg)) * nKb + j] = valid ? v : INT32_MIN_V;
