@@ -121,7 +121,9 @@ __host__ __device__ inline Split make_split(int total, int workers, int min_shar
   if (total <= 0) return sp;
   const int rest = workers - sp.half;
   const long den = (long)sp.half * 100 + (long)rest * slow_pct;
-  sp.s1 = max(min_share, (int)(((long)total * 100 + den - 1) / den));
+  const long num = (long)total * 100 + den - 1;
+  // a 32-bit division when it fits (the 64-bit one is a long instruction sequence)
+  sp.s1 = max(min_share, num <= 0x7FFFFFFF ? (int)num / (int)den : (int)(num / den));
   sp.s2 = max(min_share, sp.s1 * slow_pct / 100);
   while ((long)sp.half * sp.s1 + (long)rest * sp.s2 < total) {
     ++sp.s1;
@@ -229,12 +231,7 @@ __device__ int build_plan(const DecodeArgs& a, int n_items, int* item_start, int
   }
   // exclusive scan of per-thread totals
   const int lane = tid & (kWave - 1), wid = tid / kWave;
-  int x = local;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan_int(local);
   if (lane == kWave - 1) scratch[wid] = x;
   __syncthreads();
   int off = 0, tot = 0;
@@ -258,6 +255,21 @@ __device__ __forceinline__ int find_item(const int* item_start, int n_items, int
     if (item_start[mid] <= t) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// The same for a wave-uniform t (item_start[0] == 0 <= t), searched by the
+// whole wave in two steps instead of a chain of dependent LDS reads: lane l
+// compares the first item of segment l (segments of ceil(n_items / 64)
+// items), then the items of the last segment that starts at or below t.
+// Every lane of the wave must call it; n_items <= 4096.
+__device__ __forceinline__ int find_item_wave(const int* item_start, int n_items, int t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int seg = (n_items + kWave - 1) / kWave;
+  const int i1 = lane * seg;
+  const int c1 = __popcll(__ballot(i1 < n_items && item_start[i1] <= t));  // >= 1: item_start[0] = 0
+  const int i2 = (c1 - 1) * seg + lane;
+  const int c2 = __popcll(__ballot(lane < seg && i2 < n_items && item_start[i2] <= t));
+  return (c1 - 1) * seg + c2 - 1;
 }
 
 // ------------------------------------------------------------- merging ----
@@ -438,15 +450,26 @@ struct TileWindow {
   int item, tok0, nvalid;
 };
 
+// it_lo is an item at or before the one holding tile base.  Lane l holds the
+// next item boundary item_start[it_lo + 1 + l]: the item of tile base + l is
+// it_lo plus the number of boundaries at or below it, counted over the
+// boundaries inside the window (usually a few).  When all 64 boundaries lie
+// inside the window (items of one tile or none), each lane searches.
+// Every lane of the wave must call it.
 __device__ __forceinline__ void fill_window(const DecodeArgs& a, const int* item_start, int n_items,
-                                            int total, int tpb, int base, TileWindow& win) {
-  const int tt = base + (threadIdx.x & (kWave - 1));
+                                            int total, int tpb, int base, int it_lo, TileWindow& win) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int tt = base + lane;
   win.base = base;
   win.item = 0;
   win.tok0 = 0;
   win.nvalid = 0;
+  const int bnd = item_start[min(it_lo + 1 + lane, n_items)];  // item_start[n_items] = total
+  const int nb = __popcll(__ballot(bnd <= base + kWave - 1));
+  int it_scan = it_lo;
+  for (int k = 0; k < nb && nb < kWave; ++k) it_scan += __builtin_amdgcn_readlane(bnd, k) <= tt ? 1 : 0;
   if (tt < total) {
-    const int it = find_item(item_start, n_items, tt);
+    const int it = nb < kWave ? it_scan : find_item(item_start, n_items, tt);
     const int u = tt - item_start[it];
     const int b = it / a.Hkv, g = it - (it / a.Hkv) * a.Hkv;
     // the list entry is loaded before the head mode is known (a local head's
@@ -512,21 +535,26 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   const uint16_t* vc = (const uint16_t*)a.v;
 
   const int wv = threadIdx.x / kWave;
-  const int it_first = find_item(item_start, n_items, t0);
+  const int it_first = find_item_wave(item_start, n_items, t0);
   // Tile descriptors sit in LDS: reading one is an LDS access, so it never
   // waits behind the K/V loads in flight (global loads complete in order).
   int win_base = t0;
-  auto refill = [&](int base) {
+  auto refill = [&](int base, int it_lo) {
     TileWindow win;
-    fill_window(a, item_start, n_items, total, tpb, base, win);
+    fill_window(a, item_start, n_items, total, tpb, base, it_lo, win);
     wave_sync();
     tdesc[wv][lane] = int4{win.item, win.tok0, win.nvalid, 0};
     wave_sync();
     win_base = base;
   };
-  refill(t0);
+  refill(t0, it_first);
+  // the wave's last item, from the window when the range fits in it
+  const int it_last = t1 - t0 <= kWave ? __builtin_amdgcn_readfirstlane(tdesc[wv][t1 - 1 - t0].x)
+                                       : find_item(item_start, n_items, t1 - 1);
   auto desc = [&](int t, int& it, int& tok0, int& nv) {
-    if (t - win_base >= kWave) refill(t);
+    // a later window starts at t: the item of tile t - 1 (the old window's
+    // last lane) is a lower bound of t's
+    if (t - win_base >= kWave) refill(t, __builtin_amdgcn_readfirstlane(tdesc[wv][kWave - 1].x));
     const int4 dd = tdesc[wv][t - win_base];
     it = __builtin_amdgcn_readfirstlane(dd.x);
     tok0 = __builtin_amdgcn_readfirstlane(dd.y);
@@ -613,7 +641,6 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   // inside the tile loop reads LDS instead of waiting on a global load
   // (global loads complete in order, so that wait would drain the prefetch)
   {
-    const int it_last = find_item(item_start, n_items, t1 - 1);
     for (int c = 0; c < kQCache && it_first + c <= it_last; ++c) {
       uint4 qr[SH::KS];
       load_q(it_first + c, qr);

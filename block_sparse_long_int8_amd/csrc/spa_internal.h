@@ -58,6 +58,35 @@ __device__ __forceinline__ unsigned lane_xor(unsigned v) {
   }
 }
 
+// Wave-wide inclusive prefix sum in registers: row shifts by 1, 2, 4 and 8
+// lanes scan each 16-lane row, then the last lane of row 0 is added to row 1
+// and of row 2 to row 3 (row broadcast 15), and the last lane of row 1 to
+// rows 2 and 3 (row broadcast 31).  Lanes with no source get the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_or_zero(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ float wave_incl_scan_float(float x) {
+#define SPA_FSTEP(C, R) x += __builtin_bit_cast(float, dpp_or_zero<C, R>(__builtin_bit_cast(int, x)))
+  SPA_FSTEP(0x111, 0xf);
+  SPA_FSTEP(0x112, 0xf);
+  SPA_FSTEP(0x114, 0xf);
+  SPA_FSTEP(0x118, 0xf);
+  SPA_FSTEP(0x142, 0xa);
+  SPA_FSTEP(0x143, 0xc);
+#undef SPA_FSTEP
+  return x;
+}
+
 // ---- launch plumbing --------------------------------------------------------
 struct LaunchStatus {
   int code;  // 0 ok, else hipError_t value
