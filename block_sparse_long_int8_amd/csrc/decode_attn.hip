@@ -399,8 +399,8 @@ __device__ __forceinline__ void tile_math(const TileRegs<DD>& t, const bf16x8* q
       x[mt * 4 + r] = v;
       tmax = fmaxf(tmax, v);
     }
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-  tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+  tmax = fmaxf(tmax, lane_swap_f<16>(tmax));
+  tmax = fmaxf(tmax, lane_swap_f<32>(tmax));
   // lazy reference: the running sums keep their reference maximum until a
   // tile's maximum exceeds it by more than 2^8 (exp2 domain), so O is
   // rescaled only on the rare tiles that raise it that much
@@ -609,8 +609,8 @@ __global__ void __launch_bounds__(kThreads, OCC) decode_bf16_kernel(DecodeArgs a
   auto flush = [&](int item) {
     const size_t slot = (size_t)item + w;
     float lt = st.l;
-    lt += shfl_xor_f(lt, 16);
-    lt += shfl_xor_f(lt, 32);
+    lt += lane_swap_f<16>(lt);
+    lt += lane_swap_f<32>(lt);
     if (m < G) {
       // this lane's rows d = VW (4 g4 + r) + jj: VW consecutive d per r
       float* po = ws.part_o + (slot * G + m) * D + 4 * SH::VW * g4;

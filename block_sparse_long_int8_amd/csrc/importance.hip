@@ -310,7 +310,7 @@ __global__ void __launch_bounds__(64 * W) importance_pass_kernel(ImpArgs a) {
             psum += t <= qpos ? e : 0.f;
           }
       }
-      psum += shfl_xor_f(psum, 32);
+      psum += lane_swap_f<32>(psum);
       if (hi == 0) red[i & 1][wv][l32] = psum;
       // the previous tile's per-head sums are complete (barrier below it):
       // add them in head order and write once for the workgroup
@@ -336,8 +336,8 @@ __global__ void __launch_bounds__(64 * W) importance_pass_kernel(ImpArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // the partner lane (lane ^ 32) covered the other keys of the same query
-      const float m2 = shfl_xor_f(m[half], 32);
-      const float l2 = shfl_xor_f(l[half], 32);
+      const float m2 = lane_swap_f<32>(m[half]);
+      const float l2 = lane_swap_f<32>(l[half]);
       const float M = fmaxf(m[half], m2);
       const float S = M == -INFINITY ? 0.f
                                      : l[half] * __builtin_amdgcn_exp2f(m[half] - M) +

@@ -306,7 +306,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int e = 0; e < 16; ++e) tm = fmaxf(tm, s[mt][e]);
-    tm = fmaxf(tm, shfl_xor_f(tm, 32));
+    tm = fmaxf(tm, lane_swap_f<32>(tm));
     const float tmc = tm * c2;
     const bool resc = tmc > mrun + kLazy;
     if (__any((int)resc)) {

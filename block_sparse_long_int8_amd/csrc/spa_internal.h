@@ -87,6 +87,27 @@ __device__ __forceinline__ float wave_incl_scan_float(float x) {
   return x;
 }
 
+// Value of lane (l ^ M), M = 16 or 32, through the gfx950 lane swaps (VALU
+// only, no LDS round trip; for a single dependent reduction step, where the
+// swizzle or permute latency would show).  v_permlane16_swap exchanges 16-lane
+// rows 1 and 3 of its first operand with rows 0 and 2 of its second, and
+// v_permlane32_swap the upper half of the first with the lower half of the
+// second; with both operands v, lane l finds lane l ^ M's value in the first
+// result when bit M of l is set, else in the second.  All lanes of the wave
+// must be active.
+template <int M>
+__device__ __forceinline__ float lane_swap_f(float v) {
+  static_assert(M == 16 || M == 32, "lane_swap_f: lane distance 16 or 32");
+  const unsigned u = __float_as_uint(v);
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float((__lane_id() & 32) ? r[0] : r[1]);
+  }
+}
+
 // ---- launch plumbing --------------------------------------------------------
 struct LaunchStatus {
   int code;  // 0 ok, else hipError_t value
