@@ -437,6 +437,50 @@ def test_decode_at_maximum_items():
     attn_close(step.out.cpu().numpy(), ref["o"])
 
 
+@pytest.mark.parametrize("seq", [16, 1], ids=["one_block", "one_token"])
+def test_decode_one_tile_items(seq):
+    # 4096 items of exactly one tile: every 64-tile window of a wave holds 64
+    # item boundaries, so each lane searches the plan for its tile's item
+    cfg = dataclasses.replace(gen.TINY_DECODE, name=f"edge_one_tile_{seq}", B=512, Hq=8, Hkv=8, T=128, blk=16, k=2,
+                              n_plant=(1, 1), seq_lens=tuple([seq] * 512))
+    print(f"[decode one-tile items] seq_len {seq}", flush=True)
+    inp, t = _decode_inputs(cfg)
+    step = S.DecodeStep(_spec(cfg))
+    step(t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], t["seq_len"], t["head_mode"])
+    torch.cuda.synchronize()
+    ref = O.decode_step(inp)
+    assert sel_lists(step.idx, step.count) == ref["sel"]
+    attn_close(step.out.cpu().numpy(), ref["o"])
+
+
+def test_decode_mostly_empty_items():
+    # 4096 items, most with no selected block: runs of empty items put more
+    # than 64 item boundaries inside a wave's 64-tile window, so each lane
+    # searches the plan for its tile's item; empty items get zeros and -inf
+    cfg = dataclasses.replace(gen.TINY_DECODE, name="edge_sparse_items", B=512, Hq=8, Hkv=8, d=128, T=64, blk=16,
+                              k=2, n_plant=(1, 1), dtype="bf16", seq_lens=tuple([64] * 512))
+    print("[decode mostly-empty items]", flush=True)
+    inp, t = _decode_inputs(cfg)
+    rng = np.random.default_rng(23)
+    sel = []
+    for b in range(cfg.B):
+        n = int(rng.integers(1, 3)) if rng.random() < 0.125 else 0
+        sel.append(sorted(int(x) for x in rng.choice(4, size=n, replace=False)))
+    idx_h = np.full((cfg.B, 2), -1, dtype=np.int32)
+    for b, blocks in enumerate(sel):
+        idx_h[b, :len(blocks)] = blocks
+    idx = torch.from_numpy(idx_h).cuda()
+    cnt = torch.tensor([len(x) for x in sel], dtype=torch.int32, device="cuda")
+    out, lse = S.spa_sparse_decode_attn(t["q"], t["k"], t["v"], t["seq_len"], idx, cnt, cfg.blk)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.decode_attention(inp["q"], inp["k"], inp["v"], cfg.dtype, inp["seq_len"], sel, cfg.blk)
+    attn_close(out.float().cpu().numpy(), o_ref)
+    lse_h = lse.cpu().numpy()
+    fin = np.isfinite(lse_ref)
+    assert (np.isfinite(lse_h) == fin).all()
+    assert np.allclose(lse_h[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
+
+
 def test_prefill_long_block_lists():
     # lists of more than 64 blocks: the kernel reloads its register copy of the list
     rng = np.random.default_rng(9)
