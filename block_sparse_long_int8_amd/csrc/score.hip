@@ -114,39 +114,35 @@ __device__ __forceinline__ int group_sum(int v, int log2hpg) {
 // Fast decode path for r == 16 and a power-of-two H <= 64: one lane per
 // (block, head) loads that head's 16 bytes (the wave reads 1 KB contiguous),
 // four v_dot4 give the head dot, ReLU * w, and each group's 2^log2hpg
-// neighbouring lanes sum their heads with register lane moves.
-// grid: ceil(B*nKb*H / 256); block 256.
+// neighbouring lanes sum their heads with register lane moves.  The sequence
+// is the grid's y index, so no lane divides by nKb.  (Two or four lanes per
+// thread, with their loads issued together, were slower: fewer waves hide
+// less of the load latency.)
+// grid: (ceil(nKb*H / 256), B); block 256.
 __global__ void __launch_bounds__(256) score_decode_r16_kernel(const int8_t* __restrict__ qI,
                                                                const int8_t* __restrict__ kI,
                                                                const int8_t* __restrict__ w, int H,
-                                                               int log2H, int log2hpg, int nKb, int B,
+                                                               int log2H, int log2hpg, int nKb,
                                                                const int32_t* __restrict__ seq_len,
                                                                int blk, int32_t* __restrict__ scores) {
-  const long t = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long total = (long)B * nKb * H;
-  const bool in = t < total;
-  const long bj = in ? (t >> log2H) : 0;
-  const int h = (int)(t & (H - 1));
-  const int b = (int)(bj / nKb);
-  const int j = (int)(bj - (long)b * nKb);
-  int v = 0;
-  bool valid = false;
-  if (in) {
-    // every (block, head) below nKb is addressable: the loads go out together
-    // with seq_len's, and the sequence end only masks the result
-    const int4 kv = *reinterpret_cast<const int4*>(kI + (size_t)t * 16);
-    const int4 qv = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
-    const int wt = w[(size_t)b * H + h];
-    const int L = seq_len[b];
-    valid = j < min(nKb, (L + blk - 1) / blk);
-    int dot = __builtin_amdgcn_sdot4(qv.x, kv.x, 0, false);
-    dot = __builtin_amdgcn_sdot4(qv.y, kv.y, dot, false);
-    dot = __builtin_amdgcn_sdot4(qv.z, kv.z, dot, false);
-    dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
-    v = valid ? wt * max(dot, 0) : 0;
-  }
-  v = group_sum(v, log2hpg);
-  if (in && (h & ((1 << log2hpg) - 1)) == 0) {
+  const int b = blockIdx.y;
+  const int n = nKb * H;  // (block, head) lanes of this sequence
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int h = t & (H - 1);
+  const int j = t >> log2H;
+  // every (block, head) below nKb is addressable: the loads go out together
+  // with seq_len's, and the sequence end only masks the result
+  const int4 kv = t < n ? *reinterpret_cast<const int4*>(kI + ((size_t)b * n + t) * 16) : int4{0, 0, 0, 0};
+  const int4 qv = *reinterpret_cast<const int4*>(qI + ((size_t)b * H + h) * 16);
+  const int wt = w[(size_t)b * H + h];
+  const int L = seq_len[b];
+  const bool valid = t < n && j < min(nKb, (L + blk - 1) / blk);
+  int dot = __builtin_amdgcn_sdot4(qv.x, kv.x, 0, false);
+  dot = __builtin_amdgcn_sdot4(qv.y, kv.y, dot, false);
+  dot = __builtin_amdgcn_sdot4(qv.z, kv.z, dot, false);
+  dot = __builtin_amdgcn_sdot4(qv.w, kv.w, dot, false);
+  const int v = group_sum(valid ? wt * max(dot, 0) : 0, log2hpg);
+  if (t < n && (h & ((1 << log2hpg) - 1)) == 0) {
     const int groups = H >> log2hpg;
     scores[((size_t)b * groups + (h >> log2hpg)) * nKb + j] = valid ? v : INT32_MIN_V;
   }
@@ -362,14 +358,13 @@ __global__ void __launch_bounds__(64) score_prefill_kernel(const int8_t* __restr
 hipError_t launch_score_decode(const int8_t* qI, const int8_t* kI, const int8_t* w, int B, int H,
                                int r, int groups, int nKb, const int32_t* seq_len, int blk,
                                int32_t* scores, hipStream_t s) {
-  if (r == 16 && H <= kWave && (H & (H - 1)) == 0) {
+  if (r == 16 && H <= kWave && (H & (H - 1)) == 0 && B <= 65535 && (long)nKb * H <= 0x7FFFFF00L) {
     // groups divides a power of two, so the heads per group are one too
     int log2H = 0, log2hpg = 0;
     while ((1 << log2H) < H) ++log2H;
     while ((1 << log2hpg) < H / groups) ++log2hpg;
-    const long total = (long)B * nKb * H;
-    score_decode_r16_kernel<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(qI, kI, w, H, log2H, log2hpg, nKb,
-                                                                             B, seq_len, blk, scores);
+    const dim3 grid((unsigned)(((long)nKb * H + 255) / 256), (unsigned)B);
+    score_decode_r16_kernel<<<grid, 256, 0, s>>>(qI, kI, w, H, log2H, log2hpg, nKb, seq_len, blk, scores);
     return hipGetLastError();
   }
   dim3 grid((nKb + 255) / 256, B);
