@@ -41,6 +41,7 @@
 //     descriptors (item, first token, valid count) are computed 64 at a time,
 //     one per lane, so no tile waits on a dependent index load.
 // fp32 tile (d in {64, 128}): plain VALU version of the same online softmax.
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -827,17 +828,20 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 // nsub-th partial; it loads its partials eight at a time before combining
 // them, so those loads are in flight together, and the nsub sums are added by
 // log-sum-exp in LDS.  Items with no tile were written by workgroup 0 of the
-// main kernel.
-constexpr int kMergeGH = 2;  // query heads per workgroup
+// main kernel.  When the pair grid would leave most compute units idle and
+// items have many partials (one sequence at 32K: 16 workgroups, up to 69
+// partials each), one query head per workgroup with sixteen loads in flight
+// spreads the same reads over twice the compute units.
 constexpr int kMergeThreads = 256;
 
+template <int GH, int BATCH>  // query heads per workgroup, partial loads of a thread in flight together
 __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs a, int n_items, int workers) {
   __shared__ float Ms_all[kMergeThreads];
   __shared__ float red[kMergeThreads];
   __shared__ float4 acc_s[kMergeThreads];
   const int G = a.Hq / a.Hkv;
   const int d = a.d;
-  const int hgroups = (G + kMergeGH - 1) / kMergeGH;
+  const int hgroups = (G + GH - 1) / GH;
   const int item = blockIdx.x / hgroups;
   const int hg = blockIdx.x - item * hgroups;
   WsLayout ws = ws_layout(a.ws, n_items, workers, G, d);
@@ -847,23 +851,23 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
   const int w0 = split_wave(sp, s0);
   const int nparts = split_wave(sp, s1 - 1) - w0 + 1;
   const int per_head = d / 4;
-  const int pairs = kMergeGH * per_head;  // <= 256 (kMergeGH * d <= 1024)
+  const int pairs = GH * per_head;  // <= 256 (GH * d <= 1024)
   const int nsub = kMergeThreads / pairs;
   const int tid = threadIdx.x;
   const int sub = tid / pairs;
   const int pair = tid - sub * pairs;
   const int hl = pair / per_head;
-  const int h = hg * kMergeGH + hl;
+  const int h = hg * GH + hl;
   const int c4 = pair - hl * per_head;
   const bool active = sub < nsub && h < G;
   float M = -INFINITY, L = 0.f;
   float4 acc = {0.f, 0.f, 0.f, 0.f};
   if (active) {
-    for (int p0 = sub; p0 < nparts; p0 += 8 * nsub) {
-      float2 ml[8];
-      float4 ow[8];
+    for (int p0 = sub; p0 < nparts; p0 += BATCH * nsub) {
+      float2 ml[BATCH];
+      float4 ow[BATCH];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < BATCH; ++e) {
         const int p = p0 + e * nsub;
         if (p < nparts) {
           const size_t slot = (size_t)item + w0 + p;
@@ -876,7 +880,7 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
       }
       float Mc = M;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Mc = fmaxf(Mc, ml[e].x);
+      for (int e = 0; e < BATCH; ++e) Mc = fmaxf(Mc, ml[e].x);
       if (Mc != -INFINITY) {
         const float sc = exp2f(M - Mc);  // 0 while M is -inf
         L *= sc;
@@ -885,7 +889,7 @@ __global__ void __launch_bounds__(kMergeThreads) decode_merge_kernel(DecodeArgs 
         acc.z *= sc;
         acc.w *= sc;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < BATCH; ++e) {
           if (ml[e].x == -INFINITY) continue;
           const float f = exp2f(ml[e].x - Mc);
           L += f * ml[e].y;
@@ -1017,7 +1021,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = a.Hq / a.Hkv;
-  decode_merge_kernel<<<n_items * ((G + kMergeGH - 1) / kMergeGH), kMergeThreads, 0, s>>>(a, n_items, workers);
+  // most partials an item can have: its most tiles (a full list, or the sink
+  // and window of a local head) over the smallest wave share
+  const int tpb = (a.blk + kTile - 1) / kTile;
+  const int local_tiles = a.head_mode ? (a.sink_tok + a.window_tok) / kTile + 2 : 0;
+  const int max_parts = std::max(a.cap * tpb, local_tiles) / (a.io_bf16 ? 2 : 1) + 1;
+  if ((long)n_items * ((G + 1) / 2) < 64 && max_parts > 16) {
+    decode_merge_kernel<1, 16><<<n_items * G, kMergeThreads, 0, s>>>(a, n_items, workers);
+  } else {
+    decode_merge_kernel<2, 8><<<n_items * ((G + 1) / 2), kMergeThreads, 0, s>>>(a, n_items, workers);
+  }
   return hipGetLastError();
 }
 
