@@ -48,6 +48,8 @@
 // masks are skipped for tiles whose key positions all lie below the block's
 // smallest query position (every block of an earlier segment), which one
 // wave vote decides.
+#include <type_traits>
+
 #include "spa_internal.h"
 
 namespace spa {
@@ -286,8 +288,10 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    // ---- mask: this lane holds keys 32mt + 8a + 4hi + r
-    if (need_mask) {
+    // ---- mask: this lane holds keys 32mt + 8a + 4hi + r; only the block
+    // that crosses T needs the t < T test besides the positions
+    auto mask = [&](auto tail_tag) __attribute__((always_inline)) {
+      constexpr bool TAIL = decltype(tail_tag)::value;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -297,8 +301,14 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
           const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (!(tok0 + key0 + r < a.T && kpv[r] <= qp)) s[mt][4 * aa + r] = -INFINITY;
+            if (!((!TAIL || tok0 + key0 + r < a.T) && kpv[r] <= qp)) s[mt][4 * aa + r] = -INFINITY;
         }
+    };
+    if (need_mask) {
+      if (tok0 + BLK > a.T)
+        mask(std::true_type{});
+      else
+        mask(std::false_type{});
     }
     // ---- online softmax (exp2 domain, lazy reference)
     float tm = -INFINITY;
