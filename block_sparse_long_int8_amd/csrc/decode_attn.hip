@@ -825,8 +825,8 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 // One workgroup of 256 threads per (item, pair of query heads), so the merge
 // spreads over all compute units (one workgroup per item, 1024 threads, took
 // 60 % longer).  Thread (sub, pair) owns one float4 of one head and every
-// nsub-th partial; it loads its partials eight at a time before combining
-// them, so those loads are in flight together, and the nsub sums are added by
+// nsub-th partial; it loads its partials BATCH (eight) at a time before
+// combining them, so those loads are in flight together, and the nsub sums are added by
 // log-sum-exp in LDS.  Items with no tile were written by workgroup 0 of the
 // main kernel.  When the pair grid would leave most compute units idle and
 // items have many partials (one sequence at 32K: 16 workgroups, up to 69
