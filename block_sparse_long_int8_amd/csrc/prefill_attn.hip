@@ -48,8 +48,6 @@
 // masks are skipped for tiles whose key positions all lie below the block's
 // smallest query position (every block of an earlier segment), which one
 // wave vote decides.
-#include <type_traits>
-
 #include "spa_internal.h"
 
 namespace spa {
@@ -128,7 +126,7 @@ __device__ __forceinline__ void stage(const uint16_t* __restrict__ kb, const uin
     if (kpos)
       __builtin_amdgcn_global_load_lds(kpos + min(tok0 + lane, T - 1), (lds_void_t*)Slot<S>::pos(), 4, 0, 0);
     else
-      Slot<S>::pos()[lane] = tok0 + lane;
+      Slot<S>::pos()[lane] = tok0 + lane < T ? tok0 + lane : 0x7FFFFFFF;  // past T: masked by position
   }
 }
 
@@ -246,6 +244,13 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     const int tok0 = tk0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile u have landed
     __syncthreads();
+    // keys at or past T (the tail of the last block) take position INT_MAX so
+    // that the position test alone masks them; loaded positions are patched
+    // once they have landed, behind one more barrier (at most one tile per list)
+    if (kpos && tok0 + BLK > a.T) {
+      if (w == 0 && tok0 + lane >= a.T) Slot<S>::pos()[lane] = 0x7FFFFFFF;
+      __syncthreads();
+    }
     // tile u+2's entry and rows first: a wait they may need then comes before
     // the next tile's loads are issued
     int tk2 = 0;
@@ -259,8 +264,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
     tk1 = tk2;
     src1[0] = src2[0];
     src1[1] = src2[1];
-    const bool need_mask =
-        force_mask || tok0 + BLK > a.T || __any((int)(tok0 + lane < a.T && Slot<S>::pos()[lane] > qmin));
+    const bool need_mask = force_mask || __any((int)(Slot<S>::pos()[lane] > qmin));
     if (!active) return;
 
     // ---- S^T = K . Q^T
@@ -288,10 +292,9 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-    // ---- mask: this lane holds keys 32mt + 8a + 4hi + r; only the block
-    // that crosses T needs the t < T test besides the positions
-    auto mask = [&](auto tail_tag) __attribute__((always_inline)) {
-      constexpr bool TAIL = decltype(tail_tag)::value;
+    // ---- mask: this lane holds keys 32mt + 8a + 4hi + r (keys past T carry
+    // position INT_MAX, so the position test covers them)
+    if (need_mask) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -301,14 +304,8 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
           const int kpv[4] = {kp4.x, kp4.y, kp4.z, kp4.w};
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (!((!TAIL || tok0 + key0 + r < a.T) && kpv[r] <= qp)) s[mt][4 * aa + r] = -INFINITY;
+            if (!(kpv[r] <= qp)) s[mt][4 * aa + r] = -INFINITY;
         }
-    };
-    if (need_mask) {
-      if (tok0 + BLK > a.T)
-        mask(std::true_type{});
-      else
-        mask(std::false_type{});
     }
     // ---- online softmax (exp2 domain, lazy reference)
     float tm = -INFINITY;
