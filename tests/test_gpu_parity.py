@@ -818,3 +818,44 @@ def test_prefill_all_blocks_equals_dense_causal():
                                  [[list(range(i + 1)) for i in range(nb)]], cfg.blk, blocks=blocks)
     rows = np.concatenate([np.arange(i * 64, (i + 1) * 64) for i in blocks])
     attn_close(out.cpu().numpy()[:, :, rows], ref[:, :, rows])
+
+
+@pytest.mark.parametrize("positions", ["identity", "permuted"])
+def test_prefill_ragged_T(positions):
+    # T = 1000: the last key block holds 40 tokens.  Its tail must be masked
+    # through the positions (written past T at staging for identity positions,
+    # patched after the load for given ones); the block is selected by many rows.
+    B, Hq, Hkv, T, blk, seg = 2, 8, 2, 1000, 64, 256
+    nb = -(-T // blk)
+    print(f"[prefill ragged T] {positions}", flush=True)
+    rng = np.random.default_rng(31 if positions == "identity" else 32)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, T, 128), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128), dtype=np.float32))
+    if positions == "identity":
+        pos = np.arange(T, dtype=np.int32)
+    else:
+        pos = np.concatenate([s + rng.permutation(min(seg, T - s)) for s in range(0, T, seg)]).astype(np.int32)
+    sel = []
+    idx = np.full((B, nb, 6), -1, dtype=np.int32)
+    cnt = np.zeros((B, nb), dtype=np.int32)
+    for b in range(B):
+        rows = []
+        for i in range(nb):
+            blocks = {0, i, nb - 1} | set(int(x) for x in rng.choice(nb, size=3, replace=False))
+            blocks = sorted(blocks)
+            rows.append(blocks)
+            idx[b, i, :len(blocks)] = blocks
+            cnt[b, i] = len(blocks)
+        sel.append(rows)
+    pos2 = np.tile(pos, (B, 1))
+    kw = {} if positions == "identity" else dict(q_pos=dev(pos2), k_pos=dev(pos2))
+    out, lse = S.spa_block_sparse_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(idx), dev(cnt), blk, **kw)
+    torch.cuda.synchronize()
+    for b in range(B):
+        o_ref, lse_ref = O.prefill_attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], "bf16", pos, pos, [sel[b]], blk)
+        attn_close(out[b:b + 1].cpu().numpy(), o_ref)
+        lse_h = lse[b:b + 1].cpu().numpy()
+        fin = np.isfinite(lse_ref)
+        assert (np.isfinite(lse_h) == fin).all()
+        assert np.allclose(lse_h[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
