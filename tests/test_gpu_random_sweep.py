@@ -55,7 +55,7 @@ def _draw(seed: int):
     """One decode configuration and selection path, from a seeded generator."""
     g = np.random.default_rng(1000 + seed)
     f32 = g.random() < 0.25
-    d = int(g.choice([64, 128])) if f32 else 128
+    d = int(g.choice([64, 128]))  # bf16 and fp32 both take d 64 and 128
     blk = int(g.choice([16, 32, 64, 128]))
     Hkv = int(g.choice([1, 2, 4]))
     G = int(g.choice([1, 2, 3, 4, 8, 16] if Hkv == 1 else [1, 2, 3, 4, 8]))
