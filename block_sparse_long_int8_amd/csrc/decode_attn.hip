@@ -727,9 +727,34 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
     const int seg_end = min(t_end, item_start[item + 1]);
     const int b = item / a.Hkv, g = item - (item / a.Hkv) * a.Hkv;
     const size_t kv_off = ((size_t)b * a.Hkv + g) * (size_t)a.Tcap * DD;
+    // the sequence length, head mode, list count and first list window are
+    // requested with Q: one round trip (window entries are clamped in bounds;
+    // those past the count, and a local head's, go unused)
+    const int row = list_row(a, b, g);
+    const int L = a.seq_len[b];
+    // (without head modes the byte is read from seq_len[b] and ignored, so the
+    // load needs no branch that would wait for it at once)
+    const uint8_t* hmp = a.head_mode ? a.head_mode + g : reinterpret_cast<const uint8_t*>(a.seq_len + b);
+    const int hm_raw = *hmp;
+    const int cnt_all = a.count[row];
+    IdxWindow win;
+    win.base = (t - item_start[item]) / tpb;
+    win.val = a.idx[(size_t)row * a.cap + min(win.base + lane, a.cap - 1)];
+    // Q of the item's G heads (contiguous, G * DD floats), every float4 of a
+    // lane loaded before any is stored.  Indices past the end are clamped to
+    // the last float4, so those lanes load and store it again (same value).
+    constexpr int kQ4 = 16 * DD / 4 / kWave;  // float4 per lane for 16 heads
+    const int nq4 = G * DD / 4;
+    const f32x4* q4 = reinterpret_cast<const f32x4*>(q + ((size_t)b * a.Hq + g * G) * DD);
+    f32x4 qv[kQ4];
+#pragma unroll
+    for (int j = 0; j < kQ4; ++j) qv[j] = q4[min(lane + kWave * j, nq4 - 1)];
     wave_sync();
-    for (int e = lane; e < G * DD; e += kWave) q_s[wv][e] = q[((size_t)b * a.Hq + g * G) * DD + e];
+#pragma unroll
+    for (int j = 0; j < kQ4; ++j) reinterpret_cast<f32x4*>(q_s[wv])[min(lane + kWave * j, nq4 - 1)] = qv[j];
     wave_sync();
+    const bool local = a.head_mode && hm_raw != 0;
+    const int cnt = local ? 0 : cnt_all;
     float mrun[16], lrun[16], acc[16][NDL];
 #pragma unroll
     for (int h = 0; h < 16; ++h) {
@@ -738,15 +763,19 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
 #pragma unroll
       for (int c = 0; c < NDL; ++c) acc[h][c] = 0.f;
     }
-    const int L = a.seq_len[b];
-    const bool local = a.head_mode && a.head_mode[g];
-    const int cnt = local ? 0 : a.count[list_row(a, b, g)];
-    IdxWindow win;
-    if (!local) load_window(a, list_row(a, b, g), (t - item_start[item]) / tpb, cnt, win);
     for (int u = t - item_start[item]; u < seg_end - item_start[item]; ++u) {
       int tok0, nvalid;
       tile_info(a, b, g, u, tpb, L, local, cnt, win, tok0, nvalid);
       if (nvalid <= 0) continue;
+      // the V values of every token of the tile are requested with the K rows,
+      // before the scores: one round trip per tile.  Tokens past nvalid re-read
+      // the last valid row; their probabilities are 0.
+      const float* vbase = vc + kv_off + (size_t)tok0 * DD + lane;
+      float vv[kTile][NDL];
+#pragma unroll
+      for (int tt = 0; tt < kTile; ++tt)
+#pragma unroll
+        for (int c = 0; c < NDL; ++c) vv[tt][c] = vbase[(size_t)min(tt, nvalid - 1) * DD + kWave * c];
       const float* krow = kc + kv_off + (size_t)(tok0 + min(tau, nvalid - 1)) * DD;
       float sc[8];
 #pragma unroll
@@ -766,9 +795,12 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
       for (int hh = 0; hh < 8; ++hh) {
         const int h = 2 * hh + half;
         const float x = tau < nvalid ? sc[hh] * scale_log2 : -INFINITY;
-        float mx = x;
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, shfl_xor_f(mx, o));
+        float mx = x;  // maximum over the 32 tokens of this half, by register lane moves
+        mx = fmaxf(mx, __uint_as_float(lane_xor<1>(__float_as_uint(mx))));
+        mx = fmaxf(mx, __uint_as_float(lane_xor<2>(__float_as_uint(mx))));
+        mx = fmaxf(mx, __uint_as_float(lane_xor<4>(__float_as_uint(mx))));
+        mx = fmaxf(mx, __uint_as_float(lane_xor<8>(__float_as_uint(mx))));
+        mx = fmaxf(mx, __uint_as_float(lane_xor<16>(__float_as_uint(mx))));
         if (h < G) {
           const float m_new = fmaxf(mrun[h], mx);
           const float base = m_new == -INFINITY ? 0.f : m_new;
@@ -784,25 +816,20 @@ __global__ void __launch_bounds__(kThreads) decode_f32_kernel(DecodeArgs a, int 
           const float base = m_new == -INFINITY ? 0.f : m_new;
           const float corr = exp2f(mrun[h] - base);
           mrun[h] = m_new;
-          float ps = 0.f;
-          for (int tt = 0; tt < nvalid; ++tt) ps += p_s[wv][h][tt];
-          lrun[h] = lrun[h] * corr + ps;
 #pragma unroll
           for (int c = 0; c < NDL; ++c) acc[h][c] *= corr;
-        }
-      }
-      for (int tt = 0; tt < nvalid; ++tt) {
-        const float* vrow = vc + kv_off + (size_t)(tok0 + tt) * DD;
-        float vv[NDL];
+          // every token of the tile in order (probability 0 past nvalid, which
+          // leaves both sums unchanged)
+          float ps = 0.f;
 #pragma unroll
-        for (int c = 0; c < NDL; ++c) vv[c] = vrow[lane + kWave * c];
-#pragma unroll
-        for (int h = 0; h < 16; ++h)
-          if (h < G) {
+          for (int tt = 0; tt < kTile; ++tt) {
             const float pv = p_s[wv][h][tt];
+            ps += pv;
 #pragma unroll
-            for (int c = 0; c < NDL; ++c) acc[h][c] += pv * vv[c];
+            for (int c = 0; c < NDL; ++c) acc[h][c] += pv * vv[tt][c];
           }
+          lrun[h] = lrun[h] * corr + ps;
+        }
       }
       wave_sync();
     }
