@@ -24,7 +24,10 @@ Prints one JSON line.  roofline: the dominant launch (decode: the sparse
 attention entry point, main kernel + merge, against 8 TB/s of HBM; prefill:
 the block-sparse attention kernel against the bf16 dense MFMA peak), timed
 with HIP events on the stream it runs on.  cpu_baseline: the CPU oracle on a
-bounded sample of the same inputs.
+bounded sample of the same inputs.  achievable: what the library's two rate
+probes (include/spa_probe.h) reach on the same GPU, a plain streaming HBM read
+and a loop of independent bf16 MFMAs; the roofline also states its fraction of
+that achievable rate beside the fraction of the vendor peak.
 """
 from __future__ import annotations
 
@@ -42,6 +45,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 INT8_MFMA_PEAK_TOPS = 5000.0
+PROBE_READ_BYTES = 2 << 30      # the read probe's buffer: well beyond the 256 MB Infinity Cache
+PROBE_MFMA_ITERS = 4096         # rounds of the MFMA probe (about half a millisecond per call)
 ROTATE_BYTES = 1 << 30          # bytes one rotation over the copies must touch
 COPY_MEM_LIMIT = 64 << 30       # device bytes all copies together may take
 
@@ -69,6 +74,7 @@ def parse():
                     help="decode: replay each step as a HIP graph (one per input set) or launch it call by call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the achievable-rate probes")
     ap.add_argument("--traffic-json", default=None,
                     help="counter-measured HBM traffic of the dominant launch (default profiles/<workload>_traffic.json)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -641,6 +647,44 @@ def bench_prefill(args, cfg):
     return res
 
 
+def achievable_rates():
+    """The achievable HBM read rate and bf16 MFMA rate of this GPU: the best of five event-timed calls of
+    each rate probe, after one warm-up, on the stream they run on."""
+    import torch
+
+    import block_sparse_long_int8_amd as S
+    n_cu = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    buf = torch.empty(PROBE_READ_BYTES, dtype=torch.uint8, device="cuda")
+    sink_i = torch.zeros(1, dtype=torch.int32, device="cuda")
+    sink_f = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def best(fn, n=5):
+        fn()
+        ts = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    read_wg, mfma_wg = 8 * n_cu, 2 * n_cu
+    t_read = best(lambda: S.spa_probe_read(buf, read_wg, sink_i))
+    flops = mfma_wg * 4 * PROBE_MFMA_ITERS * S.PROBE_MFMA_FLOPS_PER_WAVE_ROUND
+    t_mfma = best(lambda: S.spa_probe_mfma_bf16(mfma_wg, PROBE_MFMA_ITERS, sink_f))
+    del buf
+    torch.cuda.synchronize()
+    log("[bench] rate probes done")
+    return {"hbm_read_gbs": PROBE_READ_BYTES / t_read / 1e9, "mfma_bf16_tflops": flops / t_mfma / 1e12,
+            "read_probe": f"spa_probe_read: {PROBE_READ_BYTES} bytes, 16-byte non-temporal loads, {read_wg} "
+                          f"workgroups of 256 threads",
+            "mfma_probe": f"spa_probe_mfma_bf16: {mfma_wg} workgroups of four waves, {PROBE_MFMA_ITERS} rounds of "
+                          f"four independent 32x32x16 bf16 products",
+            "timing": "best of five event-timed calls after one warm-up"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -649,6 +693,12 @@ def main():
         sys.exit(2)
     cfg = config_of(args.workload)
     res = bench_prefill(args, cfg) if args.workload.startswith("prefill") else bench_decode(args, cfg)
+    if not args.no_probes:
+        rates = achievable_rates()
+        res["achievable"] = rates
+        r = res["roofline"]
+        r["achievable_peak"] = rates["hbm_read_gbs"] if r["bound"] == "hbm" else rates["mfma_bf16_tflops"]
+        r["frac_of_achievable"] = r["achieved"] / r["achievable_peak"]
     print(json.dumps(res), flush=True)
 
 

@@ -2,7 +2,8 @@
 
 The library (libspa.so, HIP kernels behind a C ABI declared in include/spa.h)
 does all the work; this package is its thin ctypes binding plus the two hot
-paths wired as sequences of calls.
+paths wired as sequences of calls.  The same library carries two rate probes
+of the device (include/spa_probe.h) that the measurements compare against.
 """
 from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORTED, SPA_ERR_WORKSPACE, SPA_F32,
                    SPA_OK, SPA_SCORE_DECODE, SPA_SCORE_PREFILL_POOLED, SPA_SCORE_PREFILL_TOKENS, SPA_SCORE_DECODE_GROUPED,
@@ -17,7 +18,7 @@ from ._lib import (SPA_BF16, SPA_ERR_HIP, SPA_ERR_INVALID_ARG, SPA_ERR_UNSUPPORT
                    spa_sparse_decode_attn, spa_sparse_decode_attn_grouped, spa_sparse_decode_attn_workspace_size,
                    spa_sparse_decode_attn_noalloc,
                    spa_importance_permutation, spa_importance_permutation_workspace_size, spa_quantize_selector_keys,
-                   spa_index_score_q4)
+                   spa_index_score_q4, spa_probe_read, spa_probe_mfma_bf16, PROBE_MFMA_FLOPS_PER_WAVE_ROUND)
 from .pipeline import DecodeSpec, DecodeStep, PrefillSpec, PrefillStep
 
 __all__ = [n for n in dir() if not n.startswith("_")]

@@ -20,7 +20,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspa.so")
-HEADER = os.path.join(os.path.dirname(_PKG), "include", "spa.h")
+INCLUDE = os.path.join(os.path.dirname(_PKG), "include")
+HEADER = os.path.join(INCLUDE, "spa.h")
 
 SPA_OK = 0
 SPA_ERR_INVALID_ARG = -1
@@ -84,6 +85,8 @@ _SIGS = {
     "spa_index_score_q4": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _i, _vp, _vp]),
     "spa_importance_permutation": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _i, _f, _i, _vp, _vp, _vp, _sz, _vp]),
     "spa_importance_permutation_workspace_size": (_sz, [_i, _i, _i]),
+    "spa_probe_read": (_i, [_vp, _sz, _i, _vp, _vp]),
+    "spa_probe_mfma_bf16": (_i, [_i, _i, _vp, _vp]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -112,9 +115,12 @@ def lib() -> ctypes.CDLL:
 
 
 def declared_symbols():
-    """Function names declared in include/spa.h."""
-    with open(HEADER) as f:
-        text = f.read()
+    """Function names declared in the headers under include/ (spa.h, spa_probe.h)."""
+    text = ""
+    for name in sorted(os.listdir(INCLUDE)):
+        if name.endswith(".h"):
+            with open(os.path.join(INCLUDE, name)) as f:
+                text += f.read()
     return sorted(set(re.findall(r"^\s*(?:spa_status|size_t|const char\*|int|void)\s+(spa_\w+)\s*\(", text, re.M)))
 
 
@@ -583,3 +589,25 @@ def spa_importance_permutation(q, k, seg, proxy=64, seq_len=None, scale=None, im
                                           _ptr(imp), _ptr(perm), _ptr(ws), ws.numel(), _stream())
     _check("spa_importance_permutation", st)
     return imp, perm
+
+
+# ---- rate probes of the device (include/spa_probe.h) -------------------------
+
+PROBE_MFMA_FLOPS_PER_WAVE_ROUND = 131072  # four 32x32x16 bf16 products
+
+
+def spa_probe_read(buf: torch.Tensor, workgroups: int, sink: torch.Tensor) -> None:
+    """Read all of buf (a contiguous device tensor, a multiple of 16 bytes) once; asynchronous."""
+    _want(buf, "buf")
+    _want(sink, "sink", (1,), torch.int32)
+    _on_device(buf=buf, sink=sink)
+    nbytes = buf.numel() * buf.element_size()
+    _check("spa_probe_read", lib().spa_probe_read(_ptr(buf), nbytes, int(workgroups), _ptr(sink), _stream()))
+
+
+def spa_probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor) -> int:
+    """Run the bf16 MFMA loop; asynchronous.  Returns the flops the call performs."""
+    _want(sink, "sink", (1,), torch.float32)
+    _on_device(sink=sink)
+    _check("spa_probe_mfma_bf16", lib().spa_probe_mfma_bf16(int(workgroups), int(iters), _ptr(sink), _stream()))
+    return int(workgroups) * 4 * int(iters) * PROBE_MFMA_FLOPS_PER_WAVE_ROUND

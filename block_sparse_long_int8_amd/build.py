@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libspa.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.cpp", "score.hip", "select.hip", "select_hist.hip", "decode_attn.hip", "prefill_attn.hip", "permute.hip",
-           "importance.hip", "debug_checks.hip"]
+           "importance.hip", "debug_checks.hip", "probes.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are kept out of the generated code on purpose
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",

@@ -15,6 +15,7 @@
 #include <string>
 
 #include "../../include/spa.h"
+#include "../../include/spa_probe.h"
 #include "spa_internal.h"
 
 namespace {
@@ -582,6 +583,23 @@ spa_status spa_segment_permute(const void* src, void* dst, int64_t outer, int T,
   REQUIRE(s0 + n <= d0 || d0 + n <= s0, SPA_ERR_INVALID_ARG, "src and dst overlap");
   DEVICE_CHECKS(CHECK_STEP(spa::dbg_perm(perm, T, seg, s_)));
   return from_hip(spa::launch_permute(src, dst, outer, T, row_bytes, perm, inverse, (hipStream_t)stream), fn);
+}
+
+spa_status spa_probe_read(const void* buf, size_t bytes, int workgroups, uint32_t* sink, void* stream) {
+  const char* fn = "spa_probe_read";
+  REQUIRE(buf && sink, SPA_ERR_INVALID_ARG, "null pointer");
+  REQUIRE(aligned16(buf), SPA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  REQUIRE(bytes > 0 && bytes % 16 == 0, SPA_ERR_INVALID_ARG, "bytes must be a positive multiple of 16 (got %zu)", bytes);
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), SPA_ERR_INVALID_ARG, "workgroups %d outside 1..2^20", workgroups);
+  return from_hip(spa::launch_probe_read(buf, bytes, workgroups, sink, (hipStream_t)stream), fn);
+}
+
+spa_status spa_probe_mfma_bf16(int workgroups, int iters, float* sink, void* stream) {
+  const char* fn = "spa_probe_mfma_bf16";
+  REQUIRE(sink, SPA_ERR_INVALID_ARG, "null pointer");
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), SPA_ERR_INVALID_ARG, "workgroups %d outside 1..2^20", workgroups);
+  REQUIRE(iters >= 1 && iters <= (1 << 24), SPA_ERR_INVALID_ARG, "iters %d outside 1..2^24", iters);
+  return from_hip(spa::launch_probe_mfma_bf16(workgroups, iters, sink, (hipStream_t)stream), fn);
 }
 
 }  // extern "C"

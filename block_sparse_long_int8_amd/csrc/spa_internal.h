@@ -246,6 +246,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int T, size_t row_bytes,
                           const int32_t* perm, int inverse, hipStream_t s);
 
+// rate probes of the device (probes.hip)
+hipError_t launch_probe_read(const void* buf, size_t bytes, int workgroups, unsigned* sink, hipStream_t s);
+hipError_t launch_probe_mfma_bf16(int workgroups, int iters, float* sink, hipStream_t s);
+
 
 // ---- optional device-side checks (debug_checks.hip) ------------------------
 // Each launches a check kernel on s that records violations in one device word;

@@ -231,6 +231,27 @@ def test_debug_check_switch_and_codes():
         assert getattr(S, name) == int(val), name
 
 
+def test_probe_rejections():
+    bad = ctypes.c_void_p(0x1001)  # misaligned
+    # spa_probe_read(buf, bytes, workgroups, sink, stream)
+    r = L.spa_probe_read
+    assert r(N, 16, 1, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert r(_fake(), 16, 1, N, N) == S.SPA_ERR_INVALID_ARG
+    assert r(bad, 16, 1, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert r(_fake(), 0, 1, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert r(_fake(), 24, 1, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert r(_fake(), 16, 0, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert r(_fake(), 16, (1 << 20) + 1, _fake(2), N) == S.SPA_ERR_INVALID_ARG
+    assert b"workgroups" in L.spa_last_error()
+    # spa_probe_mfma_bf16(workgroups, iters, sink, stream)
+    m = L.spa_probe_mfma_bf16
+    assert m(1, 1, N, N) == S.SPA_ERR_INVALID_ARG
+    assert m(0, 1, _fake(), N) == S.SPA_ERR_INVALID_ARG
+    assert m(1, 0, _fake(), N) == S.SPA_ERR_INVALID_ARG
+    assert m(1, (1 << 24) + 1, _fake(), N) == S.SPA_ERR_INVALID_ARG
+    assert b"iters" in L.spa_last_error()
+
+
 def test_host_rejections_precede_device_checks():
     # with the device-side checks on, every host-side rejection still returns first, before any
     # device work (these calls pass fake host addresses and no GPU is needed)
