@@ -11,8 +11,11 @@ softmax(s/8) with K_min 16 / K_max 512 plus 1 sink and 4 local blocks
 
 ``--workload`` selects another of the named workloads: the other decode
 shapes (tokens/s, same definition) or the 64K permuted block-sparse prefill
-(prompt tokens/s; a step is permute Q/K/V and the per-token indexer vectors,
-pool + score, select, sparse attention, inverse permute of O).
+(prompt tokens/s; a step is pool + score of the per-token indexer vectors
+gathered through the permutation, select, and the sparse attention reading
+Q, K, V and writing O in the original token order; with the importance
+permutation, computing it first; in chunks of query tokens with ``--chunk``;
+replayed as one HIP graph per step).
 
 All inputs are resident in HBM before the timed region.  Every per-step input
 is replicated in ``--copies`` buffer sets that consecutive steps rotate
@@ -71,7 +74,8 @@ def parse():
     ap.add_argument("--select-algo", choices=("sort", "hist"), default="sort",
                     help="selection kernel: bitonic sort of the candidates, or the sort-free radix threshold search")
     ap.add_argument("--launch", choices=("graph", "eager"), default="graph",
-                    help="decode: replay each step as a HIP graph (one per input set) or launch it call by call")
+                    help="replay the timed steps as HIP graphs (decode: one per input set; prefill: one whole "
+                         "step, every chunk) or launch them call by call")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the achievable-rate probes")
@@ -559,8 +563,18 @@ def bench_prefill(args, cfg):
         step.attend(x["q"], x["k"], x["v"])
         mark()
 
-    for _ in range(args.warmup):
+    # the timed steps: replays of one HIP graph holding a whole step (every chunk), or eager calls
+    use_graph = args.launch == "graph"
+    launch = run
+    if use_graph:
         run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        launch = graph.replay
+    for _ in range(args.warmup):
+        launch()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} steps done")
     if args.copy_calibration_mib:
@@ -569,7 +583,7 @@ def bench_prefill(args, cfg):
     torch.cuda.synchronize()
     evt[0].record()
     for i in range(args.steps):
-        run()
+        launch()
         evt[i + 1].record()
     torch.cuda.synchronize()
     total_ms = evt[0].elapsed_time(evt[-1])
@@ -581,18 +595,46 @@ def bench_prefill(args, cfg):
     for i in range(args.steps):
         run(evs[i])
     torch.cuda.synchronize()
-    st_ms = {n: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
+    st_ms = {n: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs])) for j, n in enumerate(stages)}
+    # with graphs, each stage alone: one graph holding the stage's calls (every chunk) for all the
+    # timed steps back to back, replayed once between one event pair, so the time per call carries no
+    # host or graph launch gap; the roofline uses the attention's
+    st_alone = None
+    if use_graph:
+        fns = {}
+        if importance:
+            fns["importance_perm"] = lambda: step.importance(x["q"], x["k"])
+        fns["pool_score"] = lambda: step.score(x["qI"], x["kI"], x["w"])
+        fns["select"] = step.select
+        fns["attention"] = lambda: step.attend(x["q"], x["k"], x["v"])
+        st_alone = {}
+        for name, fn in fns.items():
+            fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(args.steps):
+                    fn()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            st_alone[name] = e0.elapsed_time(e1) / args.steps
+    st_op = st_alone or st_ms
 
     idx, counts = step.idx[0].cpu().numpy(), step.count[0].cpu().numpy()
     chunks = len(step.chunks)
     used_perm = step.perm[0].cpu().numpy() if importance else inp["perm"]
     pairs = prefill_pairs(used_perm, idx, counts, cfg.blk)
     flop = 4.0 * cfg.d * cfg.Hq * pairs * cfg.B
-    attn_s = st_ms["attention"] * 1e-3
+    attn_s = st_op["attention"] * 1e-3
     achieved = flop / attn_s / 1e12
     nq = cfg.nb
     score_ops = 2.0 * cfg.r * cfg.H_idx * (nq * (nq - 1) // 2) * cfg.B
-    score_s = st_ms["pool_score"] * 1e-3
+    score_s = st_op["pool_score"] * 1e-3
     pool_bytes = cfg.B * cfg.T * (2 * cfg.H_idx * cfg.r)
     traffic = load_traffic(args.traffic_json, source_sha("prefill_attn.hip"))
     res = {
@@ -613,18 +655,24 @@ def bench_prefill(args, cfg):
                    "seg": cfg.seg, "causal": True, "seed": args.seed, "select_algo": args.select_algo,
                    "permutation": "importance-sorted (last query block as proxy)" if importance
                    else "uniform random per segment", "heavy_hitter_frac": cfg.hh_frac,
-                   "chunks": chunks, "chunk_tokens": args.chunk or cfg.T},
+                   "chunks": chunks, "chunk_tokens": args.chunk or cfg.T,
+                   "launch": "hip_graph, one step per graph" if use_graph else "eager"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic if chunks == 1 else None,
                      "traffic_source": TRAFFIC_NOTE.format(w=args.workload) + " (one-chunk runs only)",
                      "kernel": "spa_block_sparse_prefill (prefill attention kernel"
                                + (f", {chunks} launches per step" if chunks > 1 else "") + ")",
                      "algorithmic_flop_per_launch": flop / chunks, "attended_pairs_per_head": pairs,
-                     "avg_launch_ms": attn_s * 1e3 / chunks},
+                     "avg_launch_ms": attn_s * 1e3 / chunks,
+                     "launch_timing": ("one graph of the attention calls of every timed step back to back, one "
+                                       "event pair around its replay" if st_alone
+                                       else "events around the eager attention calls")},
         "step_ms_p10_p50_p90": [pct(per_step, 10), pct(per_step, 50), pct(per_step, 90)],
-        "step_timing": "events between the timed steps themselves",
+        "step_timing": "events between the timed steps themselves" + (" (graph replays)" if use_graph else ""),
         "stages_ms": st_ms,
-        "stage_timing": "a second pass of the same steps with events between stages",
+        "stages_alone_ms": st_alone,
+        "stage_timing": "stages_ms: median over a second pass of the same steps, launched call by call with "
+                        "events between stages; stages_alone_ms: each stage alone, its calls for every timed step in one graph",
         "scoring": {"int8_ops": score_ops, "tops": score_ops / score_s / 1e12,
                     "frac_of_int8_mfma_peak": score_ops / score_s / 1e12 / INT8_MFMA_PEAK_TOPS,
                     "pool_read_bytes": pool_bytes,
@@ -637,10 +685,10 @@ def bench_prefill(args, cfg):
         n_proxy = min(cfg.proxy, cfg.T)
         imp_flop = 2 * 2.0 * cfg.B * cfg.Hq * n_proxy * cfg.T * cfg.d
         imp_bytes = 2 * cfg.B * cfg.Hkv * cfg.T * cfg.d * 2
-        t_imp = st_ms["importance_perm"] * 1e-3
-        res["importance"] = {"ms": st_ms["importance_perm"], "flop": imp_flop, "tflops": imp_flop / t_imp / 1e12,
+        t_imp = st_op["importance_perm"] * 1e-3
+        res["importance"] = {"ms": st_op["importance_perm"], "flop": imp_flop, "tflops": imp_flop / t_imp / 1e12,
                              "k_bytes": imp_bytes, "k_gbs": imp_bytes / t_imp / 1e9,
-                             "share_of_step": st_ms["importance_perm"] / sum(st_ms.values())}
+                             "share_of_step": st_op["importance_perm"] / sum(st_op.values())}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         res["cpu_baseline"] = prefill_cpu_baseline(inp, cfg)

@@ -319,3 +319,18 @@ class PrefillStep:
             self.select(ci)
             self.attend(q, k, v, ci)
         return self.out
+
+    def capture(self, q, k, v, qI_tok, kI_tok, w, perm=None) -> "torch.cuda.CUDAGraph":
+        """Record one whole prefill step (every chunk) on these tensors as a HIP graph.
+
+        Replay with ``graph.replay()``: the launches of a chunked step then go
+        out without a host round trip per call.  The graph reads and writes the
+        tensors it was recorded with (a positions tensor that ``set_perm`` had
+        to expand is recorded too).
+        """
+        self(q, k, v, qI_tok, kI_tok, w, perm)  # settle lazy state outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self(q, k, v, qI_tok, kI_tok, w, perm)
+        return g

@@ -768,6 +768,49 @@ def test_importance_prefill_pipeline_parity():
     attn_close(out.cpu().numpy(), ref["o"])
 
 
+@pytest.mark.parametrize("chunk,kind", [(0, "given"), (512, "given"), (512, "importance")],
+                         ids=["one_shot", "chunked", "chunked_importance"])
+def test_prefill_graph_replay(chunk, kind):
+    """A prefill step recorded as a HIP graph gives the eager result bit for bit on every replay.
+
+    Between replays eager kernels overwrite every output (O and lse with NaN;
+    scores, lists and counts with 0, values that stay in bounds if a replay
+    failed to rewrite them) and the device synchronises; halfway new query
+    values go into the recorded input tensor, so later replays must follow them.
+    """
+    cfg = gen.SMALL_PREFILL
+    print(f"[prefill graph replay] chunk {chunk} {kind}", flush=True)
+    inp, t = _prefill_inputs(cfg)
+    spec = S.PrefillSpec(B=cfg.B, T=cfg.T, Hq=cfg.Hq, Hkv=cfg.Hkv, d=cfg.d, blk=cfg.blk, H_idx=cfg.H_idx, r=cfg.r,
+                         k=cfg.k, n_sink=cfg.n_sink, n_local=cfg.n_local, seg=cfg.seg, chunk=chunk, perm_kind=kind)
+    step = S.PrefillStep(spec)
+    args = (t["q"], t["k"], t["v"], t["qI"], t["kI"], t["w"], None if kind == "importance" else t["perm"])
+
+    def outputs():
+        return [step.out, step.lse] + step._scores + step._idx + step._count
+
+    step(*args)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in outputs()]
+    g = step.capture(*args)
+    q_new = dev(gen.make(cfg, seed=1)["q"], "bf16")
+    for rep in range(6):
+        if rep == 3:  # new query values in the recorded tensor: recompute the eager reference
+            t["q"].copy_(q_new)
+            step(*args)
+            torch.cuda.synchronize()
+            ref = [x.clone() for x in outputs()]
+        step.out.fill_(float("nan"))
+        step.lse.fill_(float("nan"))
+        for x in step._scores + step._idx + step._count:
+            x.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (got, want) in enumerate(zip(outputs(), ref)):
+            assert torch.equal(got, want), f"replay {rep}: output {j} differs from the eager step"
+
+
 def test_prefill_chunked_equals_one_shot_bitwise():
     # chunks of 512 query slots, with q / out / lse in original order (rows perm[slot]) or in slot order and
     # k / v in original order or permuted into slot order, give exactly the rows of the one-shot call
