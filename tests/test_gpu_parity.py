@@ -902,3 +902,53 @@ def test_prefill_ragged_T(positions):
         fin = np.isfinite(lse_ref)
         assert (np.isfinite(lse_h) == fin).all()
         assert np.allclose(lse_h[fin], lse_ref[fin], atol=1e-4, rtol=1e-5)
+
+
+@pytest.mark.parametrize("positions", ["identity", "permuted"])
+def test_prefill_empty_and_fully_masked_rows(positions):
+    # Rows whose list is empty (the kernel's early exit) and rows whose listed blocks all lie
+    # after every query of the row (each key masked by position) get O = 0 and lse = -inf, as the
+    # oracle's softmax over no keys does; the other rows match the oracle.  Calls with no
+    # sequences or no query rows launch nothing.
+    B, Hq, Hkv, T, blk = 2, 4, 1, 320, 64
+    nb = T // blk
+    print(f"[prefill empty rows] {positions}", flush=True)
+    rng = np.random.default_rng(41)
+    q = gen.f32_to_bf16_bits(rng.standard_normal((B, Hq, T, 128), dtype=np.float32))
+    k = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128), dtype=np.float32))
+    v = gen.f32_to_bf16_bits(rng.standard_normal((B, Hkv, T, 128), dtype=np.float32))
+    if positions == "identity":
+        pos = np.arange(T, dtype=np.int32)
+    else:  # segments of two blocks, the last one block long: block 4 (positions 256..319) is still after all others
+        pos = np.concatenate([s + rng.permutation(min(128, T - s)) for s in range(0, T, 128)]).astype(np.int32)
+    # per sequence and query block: [] is empty; [4] for query blocks 0..2 is fully masked
+    # (every position in block 4 exceeds every position in blocks 0..3)
+    sel = [[[], [0, 1], [4], [3], [0, 2, 4]],
+           [[4], [], [1, 2], [], [0]]]
+    idx = np.full((B, nb, 3), -1, dtype=np.int32)
+    cnt = np.zeros((B, nb), dtype=np.int32)
+    for b in range(B):
+        for i, blocks in enumerate(sel[b]):
+            idx[b, i, :len(blocks)] = blocks
+            cnt[b, i] = len(blocks)
+    pos2 = np.tile(pos, (B, 1))
+    kw = {} if positions == "identity" else dict(q_pos=dev(pos2), k_pos=dev(pos2))
+    out, lse = S.spa_block_sparse_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(idx), dev(cnt), blk, **kw)
+    torch.cuda.synchronize()
+    o_h, lse_h = out.cpu().numpy(), lse.cpu().numpy()
+    o_ref, lse_ref = O.prefill_attention(q, k, v, "bf16", pos, pos, sel, blk)
+    dead = ~np.isfinite(lse_ref)
+    assert dead[0, :, 0:64].all() and dead[0, :, 128:192].all() and dead[1, :, 0:64].all() and dead[1, :, 64:128].all()
+    assert (o_h[dead] == 0).all() and np.isneginf(lse_h[dead]).all()
+    attn_close(o_h, o_ref)
+    assert np.allclose(lse_h[~dead], lse_ref[~dead], atol=1e-4, rtol=1e-5)
+    # no sequences, then no query rows (a chunk of length 0 at the end of the sequence)
+    z = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    zi = lambda *shape: torch.empty(shape, dtype=torch.int32, device="cuda")
+    o0, l0 = S.spa_block_sparse_prefill(z(0, Hq, T, 128), z(0, Hkv, T, 128), z(0, Hkv, T, 128), zi(0, nb, 3),
+                                        zi(0, nb), blk)
+    assert o0.shape == (0, Hq, T, 128) and l0.shape == (0, Hq, T)
+    o1, l1 = S.spa_block_sparse_prefill(z(B, Hq, 0, 128), dev(k, "bf16"), dev(v, "bf16"), zi(B, 0, 3), zi(B, 0), blk,
+                                        q_blk0=nb)
+    torch.cuda.synchronize()
+    assert o1.shape == (B, Hq, 0, 128) and l1.shape == (B, Hq, 0)
