@@ -42,7 +42,15 @@
 // reference until a tile's maximum exceeds it by more than 2^8 in the exp2
 // domain, so the O rescale (64 multiplies per lane) runs only on the rare
 // tiles that raise the maximum that much.  The result is the same softmax;
-// only the reference point of the partial sums differs.
+// only the reference point of the partial sums differs.  The largest
+// probability is then 2^x rather than 1, and the bf16 P operand rounds it to
+// 8 significant bits, so O is normalised by the sum of the probabilities as
+// rounded (v_dot2 against ones, 16 instructions per tile): O is an exact
+// convex combination of V rows with the bf16 weights, and a row that a few
+// keys dominate stays within rounding of the exact output.  The log-sum-exp
+// keeps the exact fp32 sum.  (Normalised by the exact sum, that rounding
+// alone moved such rows by up to 0.4 % of |v|; rescaling at every new
+// maximum fixes it too, at 5 % of the kernel's time against 3 % here.)
 //
 // Keys are masked with k_pos <= q_pos (original positions) and t < T; the
 // masks are skipped for tiles whose key positions all lie below the block's
@@ -235,7 +243,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.f;
-  float mrun = -INFINITY, lsum = 0.f;
+  float mrun = -INFINITY, lsum = 0.f, lsum_r = 0.f;  // exact and as-rounded probability sums
   const int grp = lane >> 4, s16 = lane & 15;
 
   // one tile: compute tile u from buffer S while tile u+1 streams into the other
@@ -322,6 +330,7 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
       lsum *= corr;
+      lsum_r *= corr;
       mrun = mnew;
     }
     const float nb = mrun == -INFINITY ? 0.f : -mrun;
@@ -339,6 +348,19 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
                                 cvt_pk_bf16(p[6], p[7])});
     }
     lsum += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    {
+      const bf16x2_t one2 = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);  // (1, 1)
+      float pr = 0.f;
+#pragma unroll
+      for (int kb4 = 0; kb4 < 4; ++kb4) {
+        const uint4 pu = __builtin_bit_cast(uint4, pf[kb4]);
+        pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.x), one2, pr, false);
+        pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.y), one2, pr, false);
+        pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.z), one2, pr, false);
+        pr = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pu.w), one2, pr, false);
+      }
+      lsum_r += pr;
+    }
     // ---- O^T += V^T . P^T
     const uint8_t* vt = Slot<S>::v();
     bf16x8 vf[4][4];
@@ -376,8 +398,9 @@ __global__ void __launch_bounds__(kWaves * kWave, 1) prefill_kernel(PrefillArgs 
 
   // ---- epilogue: normalise and store; lane holds d = 32dt + 8a + 4hi + r of its query slot
   const float lt = lsum + shfl_xor_f(lsum, 32);
+  const float lr = lsum_r + shfl_xor_f(lsum_r, 32);  // >= 1 when lt > 0: the row maximum's weight is >= 1
   const bool empty = !(lt > 0.f);
-  const float inv = empty ? 0.f : 1.f / lt;
+  const float inv = empty ? 0.f : 1.f / lr;
   const size_t obase = qrow0 * D + 4 * hi;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)

@@ -69,7 +69,7 @@ def _draw(seed: int):
     if g.random() < 0.5:
         kw.update(select="topk", k=int(g.integers(0, nb + 1)))
     else:
-        k_min = int(g.integers(0, 9))
+        k_min = min(int(g.integers(0, 9)), nb)
         kw.update(select="topp", p=float(g.choice([0.5, 0.8, 0.95])), beta=float(g.choice([0.125, 0.5, 1.0])),
                   k_min=k_min, k_max=int(g.integers(max(k_min, 1), nb + 1)))
     seq_lens = tuple(int(x) for x in g.integers(1, T + 1, size=B))
