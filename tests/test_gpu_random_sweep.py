@@ -85,7 +85,7 @@ def _draw(seed: int):
     return cfg, PATHS[seed % len(PATHS)]
 
 
-@pytest.mark.parametrize("seed", range(96))
+@pytest.mark.parametrize("seed", range(200))
 def test_decode_random_sweep(seed):
     cfg, path = _draw(seed)
     print(f"[random decode] seed {seed} {path}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} d={cfg.d} T={cfg.T} blk={cfg.blk} "
@@ -138,7 +138,7 @@ def _draw_prefill(seed: int):
         n_sink=int(g.integers(0, 3)), n_local=int(g.integers(0, 3)), seg=seg)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(60))
 def test_prefill_random_sweep(seed):
     cfg = _draw_prefill(seed)
     print(f"[random prefill] seed {seed}: B={cfg.B} T={cfg.T} Hq={cfg.Hq} Hkv={cfg.Hkv} H_idx={cfg.H_idx} k={cfg.k} "
@@ -189,7 +189,7 @@ def _draw_variant(seed: int):
     return cfg, ("separate-hist" if seed % 2 else "separate")
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_decode_variant_random_sweep(seed):
     cfg, path = _draw_variant(seed)
     print(f"[random decode variant] seed {seed} {path}: per_group={cfg.per_group} q4={cfg.selector_q4} B={cfg.B} "
